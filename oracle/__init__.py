@@ -1,0 +1,34 @@
+"""fp64 CPU oracle for the VDN-H3 dual-branch hybrid attention layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+link anything in this package: only the test suite, the smoke check in
+``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` use it.
+It shares no code with the HIP library and imports nothing from
+``hybrid_softmax_linear_block_amd``.
+
+Source: the VDN-H3 open-source article (tahou.com, article 216474224916730885),
+section "技术核心设计 / 双分支混合注意力机制" (dual-branch hybrid attention) and
+section "自适应门控融合双分支输出" (adaptive gated fusion of the branch outputs).
+
+Every function is a plain definition evaluated in float64 with NumPy; no
+blocking, fusion or reordering beyond what the definition states.  Readings
+the article leaves open are listed in the module docstrings of ``layout``
+and ``hybrid`` and are the same as the ones the HIP library implements.
+
+Parity status per function (what pins it, in ``tests/test_oracle_*.py``):
+  layout.frame_sets / layout.tables   pinned: the article's worked example
+                                      (frame 7 of 0..14), closed form for the
+                                      per-frame window, partition invariant.
+  hybrid.softmax_branch               pinned: dense token-mask brute force,
+                                      torch SDPA special case, constant-V.
+  hybrid.linear_states / linear_branch pinned: exact integer text-once
+                                      invariant, quadratic masked brute force,
+                                      constant-V closed form, phi closed forms.
+  hybrid.epilogue                     pinned: zero/one-hot weight closed forms,
+                                      RMSNorm scope closed form.
+  Anchor frames as queries (they attend to every frame): parity unpinned --
+  the article says only that anchors interact with the other frames.
+"""
+from .layout import Layout, frame_sets, tables  # noqa: F401
+from .hybrid import (phi, softmax_branch, linear_states, linear_branch,  # noqa: F401
+                     epilogue, hybrid_forward)
