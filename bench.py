@@ -1,0 +1,197 @@
+"""Throughput of the hybrid attention layer on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
+
+One step = one full forward of the layer (softmax branch, state build, scan,
+readout, gate GEMM + epilogue, output GEMM + residual) over one batch of
+seeded synthetic inputs already resident in HBM.  Prints one JSON line.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from hybrid_softmax_linear_block_amd import api  # noqa: E402
+from hybrid_softmax_linear_block_amd.inputs import WORKLOADS, make_inputs, sample_tokens  # noqa: E402
+
+METRIC = "hybrid-attn layer Mtokens/s + softmax-branch TFLOP/s (768p-shaped, bf16)"
+PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense MFMA TFLOP/s, MI355X published
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = {"softmax": "attn_softmax.hip", "softmax_fp8": "fp8_softmax.hip"}
+
+
+def layout_of(w):
+    return api.Layout(w.batch, w.frames, w.tokens_per_frame, w.text_tokens, w.heads, w.head_dim,
+                      w.chunk_frames, w.chunk_radius, w.anchor_first, w.anchor_last)
+
+
+def softmax_pairs(w):
+    """Visible (query, key) pairs per (batch, head), from the library's tables."""
+    _, sc, _, _ = api.layout_tables(layout_of(w))
+    n = w.tokens_per_frame
+    return int(sum(n * (int(c) * n + w.text_tokens) for c in sc))
+
+
+def work_counts(w):
+    pairs = softmax_pairs(w)
+    B, H, D, N, T, L, hid = w.batch, w.heads, w.head_dim, w.n_video, w.frames, w.text_tokens, w.hidden
+    soft = 4.0 * D * pairs * B * H
+    states = 2.0 * (N + L) * D * (D + 1) * B * H
+    readout = 2.0 * N * D * (D + 1) * B * H
+    gemm = 2 * (2.0 * B * N * hid * 2 * hid)
+    return {"pairs_per_bh": pairs, "softmax_flop": soft, "linear_flop": states + readout, "gemm_flop": gemm,
+            "layer_flop": soft + states + readout + gemm}
+
+
+def describe(w):
+    return ("%s: batch %d, %d latent frames x %d tokens/frame, %d heads x dim %d (hidden %d), %d text tokens, "
+            "chunk %d frame(s) radius %d, anchors %s, %s%s" % (
+                w.name, w.batch, w.frames, w.tokens_per_frame, w.heads, w.head_dim, w.hidden, w.text_tokens,
+                w.chunk_frames, w.chunk_radius,
+                "/".join(str(a) for a, on in ((0, w.anchor_first), (w.frames - 1, w.anchor_last)) if on) or "none",
+                w.act, " (softmax fp8)" if w.soft == "fp8" else ""))
+
+
+def traffic_for(kernel_key, workload):
+    """HBM bytes per launch measured with rocprofv3 counters, if the summary
+    under profiles/ was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel_key, workload))
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "hybrid_softmax_linear_block_amd", "csrc", KERNEL_SOURCES[kernel_key])
+    if rec.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, budget_s=20.0):
+    """Time the fp64 oracle on the host on a bounded token sample and scale
+    to Mtokens/s: full-state build (all tokens) + per-token work measured on
+    the sample, extrapolated linearly in tokens."""
+    import oracle
+    from oracle.layout import Layout as OLayout
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    lay = OLayout(w.batch, w.frames, w.tokens_per_frame, w.text_tokens, w.heads, w.head_dim,
+                  w.chunk_frames, w.chunk_radius, w.anchor_first, w.anchor_last)
+    try:
+        t0 = time.perf_counter()
+        st = oracle.linear_states(inp["k"], inp["v"], inp["text_k"], inp["text_v"], lay)
+        t_states = time.perf_counter() - t0
+        per = 2
+        tok = sample_tokens(w, per_frame=per)
+        t0 = time.perf_counter()
+        o_s = oracle.softmax_branch(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], lay, tokens=tok)
+        o_l = oracle.linear_branch(inp["q"], st, lay, tokens=tok)
+        oracle.epilogue(inp["x"][:, tok], o_s, o_l, inp["w_gs"], inp["w_gl"], inp["w_os"], inp["w_ol"],
+                        inp["rms_w"])
+        t_rows = time.perf_counter() - t0
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    n_s = len(tok)
+    full = t_states + t_rows * (w.n_video / n_s)
+    return {"value": w.batch * w.n_video / full / 1e6, "unit": "Mtokens/s", "cores": cores, "kind": "oracle",
+            "sample": ("fp64 NumPy oracle: full per-frame state build over all %d tokens (%.1f s) + softmax, "
+                       "readout and epilogue for %d sampled query tokens (%.1f s), per-token part scaled "
+                       "linearly to all %d tokens" % (w.n_video, t_states, n_s, t_rows, w.n_video)),
+            "wall_s": round(t_states + t_rows, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the layer shards by heads; "
+              "see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = WORKLOADS[args.workload]
+    print("bench: generating %s" % w.name, file=sys.stderr, flush=True)
+    inp = make_inputs(w)
+    dt = torch.float32 if w.act == "f32" else torch.bfloat16
+    dev = {k: torch.from_numpy(v).to("cuda").to(dt) for k, v in inp.items()}
+    lay = layout_of(w)
+    soft = "fp8" if w.soft == "fp8" else None
+    ws = torch.empty(api.workspace_size(lay, "f32" if w.act == "f32" else "bf16", soft), dtype=torch.uint8,
+                     device="cuda")
+    y = torch.empty_like(dev["x"])
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(timer=None):
+        api.forward(lay, dev["x"], dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"], dev["w_gs"],
+                    dev["w_gl"], dev["w_os"], dev["w_ol"], dev["rms_w"], soft=soft, y=y, workspace=ws,
+                    stream=stream, debug={"stage_events": timer.address} if timer else None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers = [api.StageTimer() for _ in range(args.steps)]
+    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(timers[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = {k: [] for k in api.STAGES}
+    for t in timers:
+        for k, v in t.elapsed_ms().items():
+            stage[k].append(v)
+    for t in timers:
+        t.close()
+    stage_ms = {k: float(np.mean(v)) for k, v in stage.items()}
+    ms = wall * 1e3 / args.steps
+    wc = work_counts(w)
+    soft_key = "softmax_fp8" if soft else "softmax"
+    soft_ms = stage_ms["softmax"]
+    soft_tflops = wc["softmax_flop"] / (soft_ms * 1e-3) / 1e12
+    peak = PEAK["fp8" if soft else w.act]
+    value = w.batch * w.n_video / (ms * 1e-3) / 1e6
+    out = {
+        "metric": METRIC, "value": round(value, 4), "unit": "Mtokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.act, "data": "synthetic",
+        "config": {"workload": describe(w), "batch": w.batch, "video_tokens": w.n_video,
+                   "text_tokens": w.text_tokens, "heads": w.heads, "head_dim": w.head_dim,
+                   "parallelism": "none (1 GPU)"},
+        "softmax_tflops": round(soft_tflops, 2),
+        "layer_tflops": round(wc["layer_flop"] / (ms * 1e-3) / 1e12, 2),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "roofline": {"kernel": "k_attn_bf16 (softmax branch)" if not soft else "softmax branch fp8",
+                     "bound": "mfma", "achieved": round(soft_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(soft_tflops / peak, 4), "traffic": traffic_for(soft_key, w.name),
+                     "flop_per_launch": wc["softmax_flop"]},
+    }
+    if not args.no_cpu_baseline and w.act != "f32":
+        print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

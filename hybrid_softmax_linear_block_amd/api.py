@@ -1,0 +1,229 @@
+"""ctypes binding of libhybattn.so (C ABI in include/hyb_attn.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+PyTorch provides device memory and the current stream.  If the library is
+missing, ``load()`` raises -- there is no fallback.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhybattn.so")
+
+HYB_OK, HYB_ERR_INVALID_ARGUMENT, HYB_ERR_UNSUPPORTED, HYB_ERR_WORKSPACE_TOO_SMALL, HYB_ERR_HIP = range(5)
+DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
+
+
+class HybError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("hyb status %d: %s" % (status, msg))
+        self.status = status
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "frames", "tokens_per_frame", "text_tokens", "heads", "head_dim",
+        "chunk_frames", "chunk_radius", "anchor_first", "anchor_last")]
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_tok", ctypes.c_int64), ("stride_head", ctypes.c_int64)]
+
+
+class _Debug(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("o_soft", "o_lin", "delta_f32", "gates", "scales",
+                                                "stage_events")]
+
+
+STAGES = ("weights", "quant", "softmax", "states", "scan", "readout", "gate", "out")
+
+
+@dataclass(frozen=True)
+class Layout:
+    batch: int
+    frames: int
+    tokens_per_frame: int
+    text_tokens: int
+    heads: int
+    head_dim: int
+    chunk_frames: int = 1
+    chunk_radius: int = 1
+    anchor_first: bool = True
+    anchor_last: bool = True
+
+    def c(self):
+        return _Layout(self.batch, self.frames, self.tokens_per_frame, self.text_tokens, self.heads,
+                       self.head_dim, self.chunk_frames, self.chunk_radius, int(self.anchor_first),
+                       int(self.anchor_last))
+
+    @property
+    def n_video(self):
+        return self.frames * self.tokens_per_frame
+
+    @property
+    def hidden(self):
+        return self.heads * self.head_dim
+
+
+_lib = None
+
+
+def load(path=None):
+    """Load the HIP library (once).  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("libhybattn.so not found at %s; build it with "
+                           "python -m hybrid_softmax_linear_block_amd.build_lib" % p)
+    lib = ctypes.CDLL(p)
+    lib.hyb_layout_tables.restype = ctypes.c_int
+    lib.hyb_layout_tables.argtypes = [ctypes.POINTER(_Layout)] + [ctypes.POINTER(ctypes.c_int32)] * 4
+    lib.hyb_workspace_size.restype = ctypes.c_int
+    lib.hyb_workspace_size.argtypes = [ctypes.POINTER(_Layout), ctypes.c_int, ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_size_t)]
+    lib.hyb_attn_forward.restype = ctypes.c_int
+    lib.hyb_attn_forward.argtypes = (
+        [ctypes.POINTER(_Layout), ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        + [_Tensor] * 5 + [ctypes.c_void_p] * 5 + [ctypes.c_float, ctypes.c_float]
+        + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(_Debug)])
+    lib.hyb_status_string.restype = ctypes.c_char_p
+    lib.hyb_status_string.argtypes = [ctypes.c_int]
+    lib.hyb_last_error.restype = ctypes.c_char_p
+    lib.hyb_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(st):
+    if st != HYB_OK:
+        raise HybError(st, load().hyb_last_error().decode())
+
+
+def layout_tables(lay: Layout):
+    """Host-side frame tables: (soft_frames [T,T], soft_count [T], fwd [T,2], bwd [T,2])."""
+    lib = load()
+    T = lay.frames
+    sf = np.zeros(T * T, np.int32)
+    sc = np.zeros(T, np.int32)
+    fw = np.zeros(2 * T, np.int32)
+    bw = np.zeros(2 * T, np.int32)
+    P = ctypes.POINTER(ctypes.c_int32)
+    c = lay.c()
+    _check(lib.hyb_layout_tables(ctypes.byref(c), sf.ctypes.data_as(P), sc.ctypes.data_as(P),
+                                 fw.ctypes.data_as(P), bw.ctypes.data_as(P)))
+    return sf.reshape(T, T), sc, fw.reshape(T, 2), bw.reshape(T, 2)
+
+
+def workspace_size(lay: Layout, act="bf16", soft=None):
+    lib = load()
+    n = ctypes.c_size_t(0)
+    c = lay.c()
+    _check(lib.hyb_workspace_size(ctypes.byref(c), DTYPES[act], DTYPES[soft or act], ctypes.byref(n)))
+    return n.value
+
+
+def _tensor4(t):
+    if t is None:
+        return _Tensor(None, 0, 0, 0)
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B, tokens, H, D] tensor with contiguous D")
+    return _Tensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def forward(lay: Layout, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin,
+            rms_weight, soft=None, softmax_scale=0.0, eps=1e-6, y=None, workspace=None, debug=None,
+            stream=None):
+    """y = x + delta for the hybrid layer, computed by libhybattn on the GPU.
+
+    Tensors are torch device tensors in the activation dtype (float32 or
+    bfloat16): x [B, N, hid]; q, k, v [B, N, H, D]; text_k, text_v
+    [B, L, H, D]; weights [hid, hid] ([in][out]); rms_weight [hid].  ``soft``
+    is None (same as the activations) or "fp8".  ``debug`` may map any of
+    o_soft, o_lin, delta_f32, gates, scales to float32 device tensors, and
+    "stage_events" to the address of an array of 2 * len(STAGES) hipEvent_t
+    (see ``StageTimer``).
+    """
+    import torch
+    lib = load()
+    act = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(x.dtype)
+    if act is None:
+        raise ValueError("activations must be float32 or bfloat16")
+    for t in (x, q, k, v, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin, rms_weight):
+        if t.dtype != x.dtype or not t.is_cuda:
+            raise ValueError("all tensors must be device tensors of the activation dtype")
+    for t in (x, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin, rms_weight):
+        if not t.is_contiguous():
+            raise ValueError("x, weights and rms_weight must be contiguous")
+    if y is None:
+        y = torch.empty_like(x)
+    if workspace is None:
+        workspace = torch.empty(workspace_size(lay, act, soft), dtype=torch.uint8, device=x.device)
+    dbg = None
+    if debug:
+        dbg = _Debug(*([_ptr(debug.get(n)) for n in ("o_soft", "o_lin", "delta_f32", "gates", "scales")]
+                       + [debug.get("stage_events")]))
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    c = lay.c()
+    st = lib.hyb_attn_forward(
+        ctypes.byref(c), DTYPES[act], DTYPES[soft or act], x.data_ptr(),
+        _tensor4(q), _tensor4(k), _tensor4(v), _tensor4(text_k), _tensor4(text_v),
+        w_gate_soft.data_ptr(), w_gate_lin.data_ptr(), w_out_soft.data_ptr(), w_out_lin.data_ptr(),
+        rms_weight.data_ptr(), float(softmax_scale), float(eps), y.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), stream, ctypes.byref(dbg) if dbg is not None else None)
+    _check(st)
+    return y
+
+
+class StageTimer:
+    """2 HIP events per stage, recorded by the library around each stage on
+    the call's stream; ``elapsed_ms()`` returns per-stage milliseconds of the
+    last recorded call."""
+
+    def __init__(self):
+        import torch
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        n = 2 * len(STAGES)
+        self.events = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events[i] = ev
+        torch.cuda.synchronize()
+
+    @property
+    def address(self):
+        return ctypes.addressof(self.events)
+
+    def elapsed_ms(self):
+        out = {}
+        for i, name in enumerate(STAGES):
+            a, b = self.events[2 * i], self.events[2 * i + 1]
+            self._hip.hipEventSynchronize(b)
+            ms = ctypes.c_float(0)
+            if self._hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out[name] = ms.value
+        return out
+
+    def close(self):
+        for ev in self.events:
+            if ev:
+                self._hip.hipEventDestroy(ev)
+        self.events = None

@@ -1,0 +1,338 @@
+// C ABI of the hybrid attention library: argument validation, workspace
+// planning, host-side frame tables and dispatch to the kernel sequences.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/hyb_attn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hyb_status fail(hyb_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+hyb_status check_layout(const hyb_layout* L, bool tables_only) {
+  if (!L) return fail(HYB_ERR_INVALID_ARGUMENT, "layout is NULL");
+  if (L->frames < 1) return fail(HYB_ERR_INVALID_ARGUMENT, "frames must be >= 1 (got %d)", L->frames);
+  if (L->chunk_frames < 1) return fail(HYB_ERR_INVALID_ARGUMENT, "chunk_frames must be >= 1");
+  if (L->chunk_radius < 0) return fail(HYB_ERR_INVALID_ARGUMENT, "chunk_radius must be >= 0");
+  if ((L->anchor_first != 0 && L->anchor_first != 1) || (L->anchor_last != 0 && L->anchor_last != 1))
+    return fail(HYB_ERR_INVALID_ARGUMENT, "anchor flags must be 0 or 1");
+  if (tables_only) return HYB_OK;
+  if (L->batch < 1 || L->tokens_per_frame < 1 || L->heads < 1)
+    return fail(HYB_ERR_INVALID_ARGUMENT, "batch, tokens_per_frame and heads must be >= 1");
+  if (L->text_tokens < 0) return fail(HYB_ERR_INVALID_ARGUMENT, "text_tokens must be >= 0");
+  if (L->head_dim != 32 && L->head_dim != 64 && L->head_dim != 128)
+    return fail(HYB_ERR_UNSUPPORTED, "head_dim %d not supported (32, 64, 128)", L->head_dim);
+  const long long N = (long long)L->frames * L->tokens_per_frame;
+  if (N > (1LL << 30) || (long long)L->batch * N * L->heads > (1LL << 31) || L->text_tokens > (1 << 30))
+    return fail(HYB_ERR_UNSUPPORTED, "problem too large for 32-bit work indexing");
+  if ((long long)L->heads * L->head_dim > 65536) return fail(HYB_ERR_UNSUPPORTED, "hidden size too large");
+  return HYB_OK;
+}
+
+hyb_status check_dtypes(const hyb_layout* L, hyb_dtype act, hyb_dtype soft) {
+  if (act != HYB_F32 && act != HYB_BF16) return fail(HYB_ERR_UNSUPPORTED, "activation dtype must be F32 or BF16");
+  if (soft != act && !(soft == HYB_FP8_E4M3 && act == HYB_BF16))
+    return fail(HYB_ERR_UNSUPPORTED, "softmax dtype must equal the activation dtype, or be FP8_E4M3 with BF16");
+  if (act == HYB_BF16 && L->head_dim == 32) return fail(HYB_ERR_UNSUPPORTED, "bf16 path needs head_dim 64 or 128");
+  return HYB_OK;
+}
+
+hyb::Dims make_dims(const hyb_layout* L) {
+  hyb::Dims d;
+  d.B = L->batch;
+  d.T = L->frames;
+  d.n = L->tokens_per_frame;
+  d.L = L->text_tokens;
+  d.H = L->heads;
+  d.D = L->head_dim;
+  d.N = (long long)d.T * d.n;
+  d.hid = d.H * d.D;
+  d.g.T = d.T;
+  d.g.C = L->chunk_frames;
+  d.g.R = L->chunk_radius;
+  d.g.af = L->anchor_first;
+  d.g.al = L->anchor_last;
+  return d;
+}
+
+// State-build split: enough workgroups to fill the chip, >= 256 tokens each.
+void state_split(const hyb::Dims& d, int* split, int* ts, int* tsplit) {
+  const long long tiles = (d.n + 63) / 64;
+  long long want = (1024 + (long long)d.B * d.H * d.T - 1) / ((long long)d.B * d.H * d.T);
+  long long cap = (d.n + 255) / 256;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  if (want > tiles) want = tiles;
+  *split = (int)want;
+  *ts = (int)(64 * ((tiles + want - 1) / want));
+  *tsplit = d.L > 0 ? (int)((d.L + *ts - 1) / *ts) : 0;
+}
+
+enum {
+  W_OS, W_OL, W_SS, W_PART, W_PRE, W_CHI, W_CLO, W_CZ, W_AP, W_WG, W_WO,
+  W_Q8, W_K8, W_V8, W_TK8, W_TV8, W_SC, W_AM, W_STATES, W_COMB, W_COUNT
+};
+
+struct Plan {
+  size_t off[W_COUNT];
+  size_t total;
+};
+
+Plan make_plan(const hyb::Dims& d, hyb_dtype act, hyb_dtype soft) {
+  Plan p;
+  size_t sz[W_COUNT] = {0};
+  const size_t BN = (size_t)d.B * d.N, hid = d.hid, D = d.D, BH = (size_t)d.B * d.H;
+  sz[W_OS] = BN * hid * 4;
+  sz[W_OL] = BN * hid * 4;
+  sz[W_SS] = BN * d.H * 4;
+  if (act == HYB_F32) {
+    sz[W_STATES] = BH * (d.T + 1) * D * (D + 1) * 4;
+    sz[W_COMB] = BH * d.T * D * (D + 1) * 4;
+    sz[W_AP] = BN * 2 * hid * 4;
+  } else {
+    int split, ts, tsplit;
+    state_split(d, &split, &ts, &tsplit);
+    const size_t slots = (size_t)d.T * split + tsplit;
+    sz[W_PART] = BH * slots * (D * D + D) * 4;
+    sz[W_PRE] = BH * d.T * (D * D + D) * 4;
+    sz[W_CHI] = BH * d.T * D * D * 2;
+    sz[W_CLO] = BH * d.T * D * D * 2;
+    sz[W_CZ] = BH * d.T * D * 4;
+    sz[W_AP] = BN * 2 * hid * 2;
+    sz[W_WG] = 2 * hid * hid * 2;
+    sz[W_WO] = 2 * hid * hid * 2;
+    if (soft == HYB_FP8_E4M3) {
+      const size_t vt = (size_t)d.T * ((d.n + 63) / 64) * 64;  // per (b,h) padded video keys
+      const size_t lt = (size_t)((d.L + 63) / 64) * 64;
+      sz[W_Q8] = BN * hid;
+      sz[W_K8] = BN * hid;
+      sz[W_V8] = BH * vt * D;
+      sz[W_TK8] = (size_t)d.B * d.L * hid;
+      sz[W_TV8] = BH * lt * D;
+      sz[W_SC] = 5 * BH * 4;
+      sz[W_AM] = 5 * BH * 4;
+    }
+  }
+  size_t o = 0;
+  for (int i = 0; i < W_COUNT; ++i) {
+    p.off[i] = o;
+    o = align_up(o + sz[i], 256);
+  }
+  p.total = o;
+  return p;
+}
+
+hyb_status check_tensor(const char* name, const hyb_tensor& t, size_t es, bool required) {
+  if (!t.ptr) return required ? fail(HYB_ERR_INVALID_ARGUMENT, "%s.ptr is NULL", name) : HYB_OK;
+  if (!aligned(t.ptr, 16)) return fail(HYB_ERR_INVALID_ARGUMENT, "%s.ptr is not 16-byte aligned", name);
+  const int64_t q = (int64_t)(16 / es);
+  if (t.stride_b < 0 || t.stride_tok < 0 || t.stride_head < 0)
+    return fail(HYB_ERR_INVALID_ARGUMENT, "%s has a negative stride", name);
+  if (t.stride_b % q || t.stride_tok % q || t.stride_head % q)
+    return fail(HYB_ERR_INVALID_ARGUMENT, "%s strides must be multiples of %lld elements", name, (long long)q);
+  return HYB_OK;
+}
+
+// Byte extent [lo, hi) of a strided tensor.
+void extent(const hyb_tensor& t, long long B, long long T, long long H, long long D, size_t es, uintptr_t* lo,
+            uintptr_t* hi) {
+  *lo = (uintptr_t)t.ptr;
+  *hi = *lo + (size_t)(((B - 1) * t.stride_b + (T - 1) * t.stride_tok + (H - 1) * t.stride_head + D) * es);
+}
+
+hyb::Tensor4 t4(const hyb_tensor& t) {
+  hyb::Tensor4 r;
+  r.p = t.ptr;
+  r.sb = t.stride_b;
+  r.st = t.stride_tok;
+  r.sh = t.stride_head;
+  return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hyb_status_string(hyb_status s) {
+  switch (s) {
+    case HYB_OK: return "ok";
+    case HYB_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case HYB_ERR_UNSUPPORTED: return "unsupported";
+    case HYB_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case HYB_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* hyb_last_error(void) { return g_err; }
+
+hyb_status hyb_layout_tables(const hyb_layout* layout, int32_t* soft_frames, int32_t* soft_count, int32_t* fwd,
+                             int32_t* bwd) {
+  g_err[0] = 0;
+  hyb_status st = check_layout(layout, true);
+  if (st != HYB_OK) return st;
+  if (!soft_frames || !soft_count || !fwd || !bwd) return fail(HYB_ERR_INVALID_ARGUMENT, "table pointer is NULL");
+  hyb::FrameGeom g{layout->frames, layout->chunk_frames, layout->chunk_radius, layout->anchor_first,
+                   layout->anchor_last};
+  const int T = g.T;
+  for (int f = 0; f < T; ++f) {
+    const hyb::SoftRanges sr = hyb::soft_ranges(g, f);
+    int c = 0;
+    for (int r = 0; r < sr.n; ++r)
+      for (int x = sr.lo[r]; x < sr.hi[r]; ++x) soft_frames[(size_t)f * T + c++] = x;
+    soft_count[f] = c;
+    for (int i = c; i < T; ++i) soft_frames[(size_t)f * T + i] = -1;
+    hyb::linear_ranges(g, f, &fwd[2 * f], &fwd[2 * f + 1], &bwd[2 * f], &bwd[2 * f + 1]);
+  }
+  return HYB_OK;
+}
+
+hyb_status hyb_workspace_size(const hyb_layout* layout, hyb_dtype act, hyb_dtype soft, size_t* bytes) {
+  g_err[0] = 0;
+  hyb_status st = check_layout(layout, false);
+  if (st != HYB_OK) return st;
+  st = check_dtypes(layout, act, soft);
+  if (st != HYB_OK) return st;
+  if (!bytes) return fail(HYB_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = make_plan(make_dims(layout), act, soft).total;
+  return HYB_OK;
+}
+
+hyb_status hyb_attn_forward(const hyb_layout* layout, hyb_dtype act, hyb_dtype soft, const void* x, hyb_tensor q,
+                            hyb_tensor k, hyb_tensor v, hyb_tensor text_k, hyb_tensor text_v,
+                            const void* w_gate_soft, const void* w_gate_lin, const void* w_out_soft,
+                            const void* w_out_lin, const void* rms_weight, float softmax_scale, float eps, void* y,
+                            void* workspace, size_t workspace_bytes, void* stream, const hyb_debug* dbg) {
+  g_err[0] = 0;
+  hyb_status st = check_layout(layout, false);
+  if (st != HYB_OK) return st;
+  st = check_dtypes(layout, act, soft);
+  if (st != HYB_OK) return st;
+  const size_t es = act == HYB_F32 ? 4 : 2;
+  const hyb::Dims d = make_dims(layout);
+  const bool has_text = d.L > 0;
+  if ((st = check_tensor("q", q, es, true)) != HYB_OK) return st;
+  if ((st = check_tensor("k", k, es, true)) != HYB_OK) return st;
+  if ((st = check_tensor("v", v, es, true)) != HYB_OK) return st;
+  if ((st = check_tensor("text_k", text_k, es, has_text)) != HYB_OK) return st;
+  if ((st = check_tensor("text_v", text_v, es, has_text)) != HYB_OK) return st;
+  const void* ptrs[] = {x, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin, rms_weight, y, workspace};
+  const char* names[] = {"x", "w_gate_soft", "w_gate_lin", "w_out_soft", "w_out_lin", "rms_weight", "y", "workspace"};
+  for (int i = 0; i < 8; ++i) {
+    if (!ptrs[i]) return fail(HYB_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (!aligned(ptrs[i], i == 7 ? 256 : 16))
+      return fail(HYB_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", names[i], i == 7 ? 256 : 16);
+  }
+  if (!(eps > 0.f) || !isfinite(eps)) return fail(HYB_ERR_INVALID_ARGUMENT, "eps must be finite and > 0");
+  if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale))
+    return fail(HYB_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  if (dbg) {
+    const void* dp[] = {dbg->o_soft, dbg->o_lin, dbg->delta_f32, dbg->gates, dbg->scales};
+    for (int i = 0; i < 5; ++i)
+      if (dp[i] && !aligned(dp[i], 16)) return fail(HYB_ERR_INVALID_ARGUMENT, "debug buffer %d not 16-byte aligned", i);
+  }
+  {  // y must not overlap q, k, v
+    const uintptr_t ylo = (uintptr_t)y, yhi = ylo + (size_t)d.B * d.N * d.hid * es;
+    const hyb_tensor* ts[] = {&q, &k, &v};
+    for (int i = 0; i < 3; ++i) {
+      uintptr_t lo, hi;
+      extent(*ts[i], d.B, d.N, d.H, d.D, es, &lo, &hi);
+      if (ylo < hi && lo < yhi) return fail(HYB_ERR_INVALID_ARGUMENT, "y overlaps q, k or v");
+    }
+  }
+  const Plan plan = make_plan(d, act, soft);
+  if (workspace_bytes < plan.total)
+    return fail(HYB_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, plan.total);
+
+  char* ws = (char*)workspace;
+  const float tau = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)d.D);
+  const float sl2 = tau * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t he;
+  if (act == HYB_F32) {
+    hyb::F32Args a;
+    a.q = t4(q); a.k = t4(k); a.v = t4(v);
+    a.tk = t4(text_k); a.tv = t4(text_v);
+    a.x = (const float*)x;
+    a.wgs = (const float*)w_gate_soft; a.wgl = (const float*)w_gate_lin;
+    a.wos = (const float*)w_out_soft; a.wol = (const float*)w_out_lin;
+    a.rmsw = (const float*)rms_weight;
+    a.scale_log2 = sl2;
+    a.eps = eps;
+    a.os = (float*)(ws + plan.off[W_OS]);
+    a.ol = (float*)(ws + plan.off[W_OL]);
+    a.ss = (float*)(ws + plan.off[W_SS]);
+    a.states = (float*)(ws + plan.off[W_STATES]);
+    a.comb = (float*)(ws + plan.off[W_COMB]);
+    a.ap = (float*)(ws + plan.off[W_AP]);
+    a.y = (float*)y;
+    a.gates_dbg = dbg ? (float*)dbg->gates : nullptr;
+    a.delta_dbg = dbg ? (float*)dbg->delta_f32 : nullptr;
+    he = hyb::run_f32(d, a, s);
+  } else {
+    hyb::Bf16Args a;
+    memset(&a, 0, sizeof(a));
+    a.q = t4(q); a.k = t4(k); a.v = t4(v);
+    a.tk = t4(text_k); a.tv = t4(text_v);
+    a.x = (const hyb::bf16_t*)x;
+    a.wgs = (const hyb::bf16_t*)w_gate_soft; a.wgl = (const hyb::bf16_t*)w_gate_lin;
+    a.wos = (const hyb::bf16_t*)w_out_soft; a.wol = (const hyb::bf16_t*)w_out_lin;
+    a.rmsw = (const hyb::bf16_t*)rms_weight;
+    a.scale_log2 = sl2;
+    a.eps = eps;
+    a.fp8 = soft == HYB_FP8_E4M3;
+    a.os = (float*)(ws + plan.off[W_OS]);
+    a.ol = (float*)(ws + plan.off[W_OL]);
+    a.ss = (float*)(ws + plan.off[W_SS]);
+    a.part = (float*)(ws + plan.off[W_PART]);
+    a.pre = (float*)(ws + plan.off[W_PRE]);
+    a.comb_hi = (hyb::bf16_t*)(ws + plan.off[W_CHI]);
+    a.comb_lo = (hyb::bf16_t*)(ws + plan.off[W_CLO]);
+    a.comb_z = (float*)(ws + plan.off[W_CZ]);
+    a.ap = (hyb::bf16_t*)(ws + plan.off[W_AP]);
+    a.wg_t = (hyb::bf16_t*)(ws + plan.off[W_WG]);
+    a.wo_t = (hyb::bf16_t*)(ws + plan.off[W_WO]);
+    a.q8 = (uint8_t*)(ws + plan.off[W_Q8]);
+    a.k8 = (uint8_t*)(ws + plan.off[W_K8]);
+    a.v8t = (uint8_t*)(ws + plan.off[W_V8]);
+    a.tk8 = (uint8_t*)(ws + plan.off[W_TK8]);
+    a.tv8t = (uint8_t*)(ws + plan.off[W_TV8]);
+    a.scales = (float*)(ws + plan.off[W_SC]);
+    a.absmax = (uint32_t*)(ws + plan.off[W_AM]);
+    a.y = (hyb::bf16_t*)y;
+    a.gates_dbg = dbg ? (float*)dbg->gates : nullptr;
+    a.delta_dbg = dbg ? (float*)dbg->delta_f32 : nullptr;
+    a.ev = dbg ? (hipEvent_t*)dbg->stage_events : nullptr;
+    int split, ts, tsplit;
+    state_split(d, &split, &ts, &tsplit);
+    a.state_split = split;
+    a.text_split = tsplit;
+    a.state_slots = d.T * split + tsplit;
+    he = hyb::run_bf16(d, a, s);
+    if (he == hipSuccess && dbg && dbg->scales && a.fp8)
+      he = hipMemcpyAsync(dbg->scales, a.scales, 5 * (size_t)d.B * d.H * 4, hipMemcpyDeviceToDevice, s);
+  }
+  if (he == hipSuccess && dbg && dbg->o_soft)
+    he = hipMemcpyAsync(dbg->o_soft, ws + plan.off[W_OS], (size_t)d.B * d.N * d.hid * 4, hipMemcpyDeviceToDevice, s);
+  if (he == hipSuccess && dbg && dbg->o_lin)
+    he = hipMemcpyAsync(dbg->o_lin, ws + plan.off[W_OL], (size_t)d.B * d.N * d.hid * 4, hipMemcpyDeviceToDevice, s);
+  if (he != hipSuccess) return fail(HYB_ERR_HIP, "HIP error: %s", hipGetErrorString(he));
+  return HYB_OK;
+}
+
+}  // extern "C"

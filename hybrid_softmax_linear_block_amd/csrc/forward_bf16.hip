@@ -1,0 +1,42 @@
+// Launch sequence of the bf16 (optionally fp8-softmax) forward pass.
+// Everything is enqueued on the caller's stream; nothing synchronises.
+#include "kernels_bf16.h"
+
+namespace hyb {
+
+#define HYB_TRY(x)                 \
+  do {                             \
+    hipError_t e_ = (x);           \
+    if (e_ != hipSuccess) return e_; \
+  } while (0)
+
+// Stage indices match HYB_STAGE_* of the public header.
+enum { ST_WEIGHTS, ST_QUANT, ST_SOFTMAX, ST_STATES, ST_SCAN, ST_READOUT, ST_GATE, ST_OUT };
+
+#define HYB_STAGE(st, call)                                        \
+  do {                                                             \
+    if (a.ev) HYB_TRY(hipEventRecord(a.ev[2 * (st)], s));          \
+    HYB_TRY(call);                                                 \
+    if (a.ev) HYB_TRY(hipEventRecord(a.ev[2 * (st) + 1], s));      \
+  } while (0)
+
+static hipError_t nothing() { return hipSuccess; }
+
+hipError_t run_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
+  HYB_STAGE(ST_WEIGHTS, launch_weights_bf16(d, a, s));
+  if (a.fp8) {
+    HYB_STAGE(ST_QUANT, launch_quant_fp8(d, a, s));
+    HYB_STAGE(ST_SOFTMAX, launch_softmax_fp8(d, a, s));
+  } else {
+    HYB_STAGE(ST_QUANT, nothing());
+    HYB_STAGE(ST_SOFTMAX, launch_softmax_bf16(d, a, s));
+  }
+  HYB_STAGE(ST_STATES, launch_states_bf16(d, a, s));
+  HYB_STAGE(ST_SCAN, launch_scan_bf16(d, a, s));
+  HYB_STAGE(ST_READOUT, launch_readout_bf16(d, a, s));
+  HYB_STAGE(ST_GATE, launch_gate_gemm_bf16(d, a, s));
+  HYB_STAGE(ST_OUT, launch_out_gemm_bf16(d, a, s));
+  return hipSuccess;
+}
+
+}  // namespace hyb

@@ -1,0 +1,244 @@
+// Gated fusion of the two branches into the residual stream, as two bf16 MFMA
+// GEMMs with fused epilogues.
+//
+// VDN-H3 article (tahou.com), section "自适应门控融合双分支输出": the two branch
+// outputs differ in scale, so each gets its own content-dependent sigmoid gate
+// and its own output projection, and the result is added to the residual
+// stream; the linear branch is RMS-normalised before its element-wise gate.
+//   gate GEMM:   G = sigmoid(x [W_gs | W_gl]);
+//                A' = [G_s * O_s | G_l * (O_l * w / sqrt(mean(O_l^2) + eps))]  (bf16)
+//   output GEMM: y = x + A' [W_os ; W_ol]
+// Both GEMMs compute C^T = W^T X^T so that a lane owns one token (the RMS
+// factor is a per-lane scalar) and four consecutive features (vector stores).
+#include "kernels_bf16.h"
+
+namespace hyb {
+
+enum { EPI_GATE = 0, EPI_OUT = 1 };
+
+struct GemmArgs {
+  const bf16_t* A;   // [M][K] token rows
+  const bf16_t* Bt;  // [N][K] feature rows (weights transposed)
+  long long M;
+  int N, K;
+  int hid, H;
+  float eps;
+  // gate epilogue
+  const float *os, *ol, *ss;
+  const bf16_t* rmsw;
+  bf16_t* ap;
+  float* gates_dbg;
+  // output epilogue
+  const bf16_t* x;
+  bf16_t* y;
+  float* delta_dbg;
+};
+
+template <int WTM, int WFN, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
+  constexpr int BM = 2 * WTM * 32, BN = 2 * WFN * 32;
+  constexpr int RA = BM / 32, RB = BN / 32;  // granules per thread per k-tile
+  using SW = Swz<64>;
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * 64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int ntn = g.N / BN;
+  const unsigned wid = xcd_remap(blockIdx.x, gridDim.x);
+  const long long m0 = (long long)(wid / ntn) * BM;
+  const int n0 = (int)(wid % ntn) * BN;
+
+  floatx16 acc[WFN][WTM];
+#pragma unroll
+  for (int i = 0; i < WFN; ++i)
+#pragma unroll
+    for (int j = 0; j < WTM; ++j) acc[i][j] = zero16();
+
+  uint4 ra[RA], rb[RB];
+  auto load = [&](int kt) {
+    const int k0 = kt * 64;
+#pragma unroll
+    for (int r = 0; r < RA; ++r) {
+      const int gi = tid + 256 * r, row = gi >> 3, col = (gi & 7) * 8;
+      const long long m = m0 + row;
+      ra[r] = m < g.M ? ldg16(g.A + m * g.K + k0 + col) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int gi = tid + 256 * r, row = gi >> 3, col = (gi & 7) * 8;
+      rb[r] = ldg16(g.Bt + (long long)(n0 + row) * g.K + k0 + col);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < RA; ++r) {
+      const int gi = tid + 256 * r, row = gi >> 3, col = (gi & 7) * 8;
+      *(uint4*)&As[buf][SW::off(row, col)] = ra[r];
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int gi = tid + 256 * r, row = gi >> 3, col = (gi & 7) * 8;
+      *(uint4*)&Bs[buf][SW::off(row, col)] = rb[r];
+    }
+  };
+
+  const int nk = g.K / 64;
+  load(0);
+  stash(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) load(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 bt[WTM];
+#pragma unroll
+      for (int tb = 0; tb < WTM; ++tb)
+        bt[tb] = *(const bf16x8*)&As[buf][SW::off(wm * WTM * 32 + tb * 32 + l32, 16 * ks + 8 * half)];
+#pragma unroll
+      for (int fb = 0; fb < WFN; ++fb) {
+        const bf16x8 a = *(const bf16x8*)&Bs[buf][SW::off(wn * WFN * 32 + fb * 32 + l32, 16 * ks + 8 * half)];
+#pragma unroll
+        for (int tb = 0; tb < WTM; ++tb) acc[fb][tb] = mfma32(a, bt[tb], acc[fb][tb]);
+      }
+    }
+    if (more) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane owns token m, features n0' + 8*jg + 4*half + 0..3
+#pragma unroll
+  for (int tb = 0; tb < WTM; ++tb) {
+    const long long m = m0 + wm * WTM * 32 + tb * 32 + l32;
+    if (m >= g.M) continue;
+    float rinv = 0.f;
+    if constexpr (EPI == EPI_GATE) {
+      float tot = 0.f;
+      for (int hh = 0; hh < g.H; ++hh) tot += g.ss[m * g.H + hh];
+      rinv = rsqrtf(tot / (float)g.hid + g.eps);
+    }
+#pragma unroll
+    for (int fb = 0; fb < WFN; ++fb)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int n = n0 + wn * WFN * 32 + fb * 32 + 8 * jg + 4 * half;
+        const float c0 = acc[fb][tb][4 * jg], c1 = acc[fb][tb][4 * jg + 1];
+        const float c2 = acc[fb][tb][4 * jg + 2], c3 = acc[fb][tb][4 * jg + 3];
+        if constexpr (EPI == EPI_GATE) {
+          const float g0 = sigmoid_f(c0), g1 = sigmoid_f(c1), g2 = sigmoid_f(c2), g3 = sigmoid_f(c3);
+          float4 val;
+          if (n < g.hid) {
+            val = *(const float4*)(g.os + m * g.hid + n);
+          } else {
+            const int c = n - g.hid;
+            const float4 o = *(const float4*)(g.ol + m * g.hid + c);
+            const uint2 wv = *(const uint2*)(g.rmsw + c);
+            val.x = o.x * __uint_as_float(wv.x << 16) * rinv;
+            val.y = o.y * __uint_as_float(wv.x & 0xffff0000u) * rinv;
+            val.z = o.z * __uint_as_float(wv.y << 16) * rinv;
+            val.w = o.w * __uint_as_float(wv.y & 0xffff0000u) * rinv;
+          }
+          uint2 st;
+          st.x = pack_bf16x2(g0 * val.x, g1 * val.y);
+          st.y = pack_bf16x2(g2 * val.z, g3 * val.w);
+          *(uint2*)(g.ap + m * (2LL * g.hid) + n) = st;
+          if (g.gates_dbg) *(float4*)(g.gates_dbg + m * (2LL * g.hid) + n) = make_float4(g0, g1, g2, g3);
+        } else {
+          const uint2 xv = *(const uint2*)(g.x + m * g.hid + n);
+          uint2 st;
+          st.x = pack_bf16x2(__uint_as_float(xv.x << 16) + c0, __uint_as_float(xv.x & 0xffff0000u) + c1);
+          st.y = pack_bf16x2(__uint_as_float(xv.y << 16) + c2, __uint_as_float(xv.y & 0xffff0000u) + c3);
+          *(uint2*)(g.y + m * g.hid + n) = st;
+          if (g.delta_dbg) *(float4*)(g.delta_dbg + m * g.hid + n) = make_float4(c0, c1, c2, c3);
+        }
+      }
+  }
+}
+
+// Weight transposes into the GEMMs' [N][K] operand layout.
+//   mode 0: out[2*hid][hid],  out[c][r] = c < hid ? W_gs[r][c] : W_gl[r][c - hid]
+//   mode 1: out[hid][2*hid],  out[c][r] = r < hid ? W_os[r][c] : W_ol[r - hid][c]
+__global__ __launch_bounds__(256) void k_weight_transpose(const bf16_t* __restrict__ s0,
+                                                          const bf16_t* __restrict__ s1, int hid, int mode,
+                                                          bf16_t* __restrict__ out) {
+  __shared__ bf16_t t[64][66];
+  const int R = mode == 0 ? hid : 2 * hid;  // source rows
+  const int C = mode == 0 ? 2 * hid : hid;  // source cols
+  const int tc = blockIdx.x % (C / 64), tr = blockIdx.x / (C / 64);
+  const int r0 = tr * 64, c0 = tc * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int rr = i / 64, cc = i % 64;
+    const int r = r0 + rr, c = c0 + cc;
+    bf16_t val;
+    if (mode == 0) val = c < hid ? s0[(long long)r * hid + c] : s1[(long long)r * hid + c - hid];
+    else val = r < hid ? s0[(long long)r * hid + c] : s1[(long long)(r - hid) * hid + c];
+    t[rr][cc] = val;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int cc = i / 64, rr = i % 64;
+    out[(long long)(c0 + cc) * R + r0 + rr] = t[rr][cc];
+  }
+}
+
+hipError_t launch_weights_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
+  const int hid = d.hid;
+  const unsigned grid = (unsigned)((hid / 64) * (2 * hid / 64));
+  hipLaunchKernelGGL(k_weight_transpose, dim3(grid), dim3(256), 0, s, a.wgs, a.wgl, hid, 0, a.wg_t);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_weight_transpose, dim3(grid), dim3(256), 0, s, a.wos, a.wol, hid, 1, a.wo_t);
+  return hipGetLastError();
+}
+
+template <int WTM, int WFN, int EPI>
+static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+  constexpr int BM = 2 * WTM * 32, BN = 2 * WFN * 32;
+  if (g.N % BN != 0 || g.K % 64 != 0) return hipErrorInvalidValue;
+  const long long grid = ((g.M + BM - 1) / BM) * (g.N / BN);
+  hipLaunchKernelGGL((k_gemm_bf16<WTM, WFN, EPI>), dim3((unsigned)grid), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+static GemmArgs base_args(const Dims& d, const Bf16Args& a) {
+  GemmArgs g = {};
+  g.M = (long long)d.B * d.N;
+  g.hid = d.hid;
+  g.H = d.H;
+  g.eps = a.eps;
+  return g;
+}
+
+hipError_t launch_gate_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
+  GemmArgs g = base_args(d, a);
+  g.A = a.x;
+  g.Bt = a.wg_t;
+  g.N = 2 * d.hid;
+  g.K = d.hid;
+  g.os = a.os;
+  g.ol = a.ol;
+  g.ss = a.ss;
+  g.rmsw = a.rmsw;
+  g.ap = a.ap;
+  g.gates_dbg = a.gates_dbg;
+  if (g.N % 128 == 0) return launch_gemm<2, 2, EPI_GATE>(g, s);
+  return launch_gemm<2, 1, EPI_GATE>(g, s);
+}
+
+hipError_t launch_out_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
+  GemmArgs g = base_args(d, a);
+  g.A = a.ap;
+  g.Bt = a.wo_t;
+  g.N = d.hid;
+  g.K = 2 * d.hid;
+  g.x = a.x;
+  g.y = a.y;
+  g.delta_dbg = a.delta_dbg;
+  if (g.N % 128 == 0) return launch_gemm<2, 2, EPI_OUT>(g, s);
+  return launch_gemm<2, 1, EPI_OUT>(g, s);
+}
+
+}  // namespace hyb

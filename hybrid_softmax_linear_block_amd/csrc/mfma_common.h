@@ -1,0 +1,68 @@
+// MFMA / LDS building blocks for gfx950 (CDNA4, wave64).
+//
+// Lane layouts used throughout (verified on gfx950):
+//   v_mfma_f32_32x32x16_bf16  A: lane l holds row (l % 32), k = 8*(l/32) + e, e = 0..7
+//                             B: lane l holds col (l % 32), k = 8*(l/32) + e
+//                             C: lane l, element r: row 8*(r/4) + 4*(l/32) + r%4, col l % 32
+//   ds_read_b64_tr_b16        within each group of 16 lanes, result lane j element r
+//                             is element (j % 4) of the 8-byte row addressed by lane
+//                             (j/4 + 4r) of the group.
+// Because the contraction index of an MFMA may be permuted freely as long as A
+// and B agree, the kernels pick the key/token order inside each 16-wide k-step
+// to match the register layout the previous MFMA produced.
+#pragma once
+#include "common.h"
+
+namespace hyb {
+
+__device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) short4_t lds_short4;
+
+// Two transposing 8-byte LDS reads -> one bf16x8 MFMA operand.
+__device__ __forceinline__ bf16x8 tr_pair(const bf16_t* p0, const bf16_t* p1) {
+  short4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p0));
+  short4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p1));
+  typedef __attribute__((ext_vector_type(8))) short short8_t;
+  short8_t c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// Row-major bf16 tile in LDS, COLS elements per row, with the 16-byte granule
+// index XOR-swizzled by row so that (a) 16 consecutive rows read at one
+// granule and (b) 4 consecutive rows read across 4 consecutive granules both
+// touch distinct banks.
+template <int COLS>
+struct Swz {
+  static constexpr int G = COLS / 8;
+  static_assert(G == 8 || G == 16, "tile width must be 64 or 128 bf16");
+  __device__ static __forceinline__ int key(int row) {
+    if constexpr (G == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  }
+  // element offset of (row, col); col may be any value, its granule is swizzled
+  __device__ static __forceinline__ int off(int row, int col) {
+    return row * COLS + ((((col >> 3) ^ key(row))) << 3) + (col & 7);
+  }
+};
+
+__device__ __forceinline__ floatx16 zero16() {
+  floatx16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *(const uint4*)p; }
+
+// XCD-aware remap: hardware dispatches workgroup i to XCD i % 8.  Return the
+// logical index so that each XCD runs a contiguous range of logical work.
+__device__ __forceinline__ unsigned xcd_remap(unsigned i, unsigned total) {
+  const unsigned xcd = i & 7u, local = i >> 3;
+  const unsigned q = total >> 3, r = total & 7u;
+  return xcd * q + (xcd < r ? xcd : r) + local;
+}
+
+}  // namespace hyb

@@ -1,0 +1,165 @@
+/*
+ * hyb_attn.h -- C ABI of the MI355X (gfx950) VDN-H3 dual-branch hybrid
+ * attention layer (forward pass).
+ *
+ * The layer is defined in the VDN-H3 open-source article (tahou.com, article
+ * 216474224916730885):
+ *   - section "双分支混合注意力机制" (dual-branch hybrid attention):
+ *       softmax branch: exact softmax attention of each video token over the
+ *       key frames of its local window (chunks of consecutive latent frames,
+ *       a chunk seeing itself and its neighbouring chunks), the first and last
+ *       frames as boundary anchors, and all text tokens;
+ *       linear branch: a forward state summing phi(K)^T V over the frames
+ *       before the window and a backward state over the frames after it, both
+ *       leaving out window and anchor frames, each holding half of the text;
+ *       the two reads are merged so that text counts once;
+ *       worked example: frame 7 of 0..14 keeps 6, 7, 8, 0, 14 in softmax,
+ *       forward state 1-5, backward state 9-13;
+ *   - section "自适应门控融合双分支输出" (adaptive gated fusion): one
+ *       content-dependent sigmoid gate per branch, RMSNorm before the linear
+ *       branch's element-wise gate, a separate output projection per branch,
+ *       summed into the residual stream.
+ *
+ * Readings fixed by this library where the article is silent:
+ *   tau = 1/sqrt(D) unless softmax_scale > 0;  phi(u) = elu(u) + 1;
+ *   O_l = phi(q)^T (S+ + S-) / (phi(q)^T (z+ + z-) + eps);
+ *   g_s = sigmoid(x W_gs), g_l = sigmoid(x W_gl), element-wise over hidden;
+ *   r = O_l * w / sqrt(mean_hidden(O_l^2) + eps)  (per token, full hidden);
+ *   y = x + (g_s * O_s) W_os + (g_l * r) W_ol,  weights [in][out] row-major;
+ *   an anchor frame used as a query attends to every frame and its linear
+ *   states hold text only; chunks are formed over the non-anchor frames in
+ *   order (the last one may be short).
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are device memory owned by the caller.  The library
+ *     never allocates or frees memory; scratch space is the caller's
+ *     workspace, sized with hyb_workspace_size().
+ *   - hyb_attn_forward() only enqueues work on `stream` and returns; it never
+ *     synchronises.  Device faults surface at the caller's next sync.
+ *   - Every argument is validated before the first launch; on failure nothing
+ *     is launched, the status is returned and hyb_last_error() (thread-local)
+ *     describes it.  A failed launch returns HYB_ERR_HIP.
+ *   - The library keeps no mutable global state besides the thread-local
+ *     error message; concurrent calls on different streams with distinct
+ *     workspaces are independent.
+ */
+#ifndef HYB_ATTN_H
+#define HYB_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HYB_OK = 0,
+  HYB_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, bad size, bad stride */
+  HYB_ERR_UNSUPPORTED = 2,        /* valid but not implemented (head_dim, dtype combination) */
+  HYB_ERR_WORKSPACE_TOO_SMALL = 3,
+  HYB_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} hyb_status;
+
+typedef enum { HYB_F32 = 0, HYB_BF16 = 1, HYB_FP8_E4M3 = 2 } hyb_dtype;
+
+/* Shape and window of one call.
+ *   video tokens N = frames * tokens_per_frame, token index = f * n + p
+ *   (frame major).  Supported: batch, frames, tokens_per_frame, heads >= 1;
+ *   text_tokens >= 0; head_dim in {32, 64, 128} (bf16 and fp8 softmax:
+ *   {64, 128}); chunk_frames >= 1 (1 = per-frame window; 5 = the article's
+ *   chunking); chunk_radius >= 0 (1 = self + adjacent chunks);
+ *   anchor_first / anchor_last are 0 or 1. */
+typedef struct {
+  int32_t batch, frames, tokens_per_frame, text_tokens, heads, head_dim;
+  int32_t chunk_frames;
+  int32_t chunk_radius;
+  int32_t anchor_first, anchor_last;
+} hyb_layout;
+
+/* A [B, tokens, H, D] activation in the activation dtype; strides in
+ * elements; the D dimension is contiguous.  ptr must be 16-byte aligned and
+ * every stride a multiple of 16 bytes' worth of elements. */
+typedef struct {
+  const void* ptr;
+  int64_t stride_b, stride_tok, stride_head;
+} hyb_tensor;
+
+/* Stages of one forward call, in launch order (see hyb_debug.stage_events). */
+enum {
+  HYB_STAGE_WEIGHTS = 0,   /* weight transposes into the GEMM operand layout */
+  HYB_STAGE_QUANT = 1,     /* fp8 absmax + quantisation (fp8 softmax only) */
+  HYB_STAGE_SOFTMAX = 2,   /* block-sparse softmax branch */
+  HYB_STAGE_STATES = 3,    /* per-frame linear states */
+  HYB_STAGE_SCAN = 4,      /* prefix/suffix scan across frames */
+  HYB_STAGE_READOUT = 5,   /* phi(Q) readout */
+  HYB_STAGE_GATE = 6,      /* gate GEMM + RMSNorm/gating epilogue */
+  HYB_STAGE_OUT = 7,       /* output GEMM + residual */
+  HYB_STAGE_COUNT = 8
+};
+
+/* Optional float32 copies of intermediate results (each pointer may be NULL):
+ *   o_soft    [B, N, H, D]   softmax-branch output
+ *   o_lin     [B, N, H, D]   linear-branch output (before RMSNorm)
+ *   delta_f32 [B, N, hid]    y - x before rounding to the activation dtype
+ *   gates     [B, N, 2*hid]  [g_s | g_l]
+ *   scales    [5, B, H]      fp8 dequantisation scales of q, k, v, text_k,
+ *                            text_v (only written when soft == HYB_FP8_E4M3)
+ *   stage_events  NULL or an array of 2*HYB_STAGE_COUNT hipEvent_t created by
+ *                 the caller; events 2s and 2s+1 are recorded on `stream`
+ *                 right before and after stage s (for timing; a stage that
+ *                 does not run records both back to back). */
+typedef struct {
+  void *o_soft, *o_lin, *delta_f32, *gates, *scales;
+  void* stage_events;
+} hyb_debug;
+
+/* Host-only: the integer frame tables of the layout (frames and window
+ * fields of *layout are used; the rest is ignored).  T = frames.
+ *   soft_frames [T*T]  row f: the softmax key frames of query frame f in
+ *                      ascending order, padded with -1
+ *   soft_count  [T]    number of softmax key frames of frame f
+ *   fwd, bwd    [T*2]  half-open frame ranges [lo, hi) summed into the
+ *                      forward / backward linear state; {0, 0} when empty
+ * All four are caller-owned host arrays. */
+hyb_status hyb_layout_tables(const hyb_layout* layout, int32_t* soft_frames, int32_t* soft_count,
+                             int32_t* fwd, int32_t* bwd);
+
+/* Bytes of device workspace hyb_attn_forward() needs for this layout and
+ * dtype combination (act: HYB_F32 or HYB_BF16; soft: act or HYB_FP8_E4M3
+ * with act == HYB_BF16). */
+hyb_status hyb_workspace_size(const hyb_layout* layout, hyb_dtype act, hyb_dtype soft, size_t* bytes);
+
+/* The hybrid attention layer, y = x + delta.
+ *   x, y          [B, N, hid] contiguous, activation dtype; y may alias x
+ *                 (in-place residual) but must not overlap q, k, v
+ *   q, k, v       [B, N, H, D]; text_k, text_v [B, L, H, D]
+ *   w_gate_soft, w_gate_lin, w_out_soft, w_out_lin  [hid][hid] row-major
+ *                 ([in][out], y = x W), activation dtype
+ *   rms_weight    [hid], activation dtype
+ *   softmax_scale 0 selects 1/sqrt(D); eps > 0 (1e-6 in the article's setup)
+ *   workspace     device memory of at least hyb_workspace_size() bytes,
+ *                 256-byte aligned; its contents on entry are ignored
+ *   dbg           NULL or a hyb_debug whose non-null members receive float32
+ *                 intermediates
+ * Enqueued on `stream` (a hipStream_t; NULL = default stream). */
+hyb_status hyb_attn_forward(const hyb_layout* layout, hyb_dtype act, hyb_dtype soft,
+                            const void* x, hyb_tensor q, hyb_tensor k, hyb_tensor v,
+                            hyb_tensor text_k, hyb_tensor text_v,
+                            const void* w_gate_soft, const void* w_gate_lin,
+                            const void* w_out_soft, const void* w_out_lin,
+                            const void* rms_weight, float softmax_scale, float eps,
+                            void* y, void* workspace, size_t workspace_bytes,
+                            void* stream, const hyb_debug* dbg);
+
+/* Static description of a status code. */
+const char* hyb_status_string(hyb_status status);
+
+/* Thread-local message of the last failed call on this thread ("" if none). */
+const char* hyb_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYB_ATTN_H */

@@ -1,0 +1,126 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, fills the frame tables exactly as the oracle does, and
+rejects bad arguments before launching anything."""
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from hybrid_softmax_linear_block_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hyb_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(api.LIB_PATH), reason="libhybattn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hyb_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = api.load()
+    names = declared_functions()
+    assert names == sorted(["hyb_attn_forward", "hyb_last_error", "hyb_layout_tables",
+                            "hyb_status_string", "hyb_workspace_size"])
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_layout_tables_bit_exact_against_oracle():
+    for T, C, R, af, al in itertools.product(range(1, 36), (1, 2, 3, 5), (0, 1, 2), (0, 1), (0, 1)):
+        lay = api.Layout(1, T, 1, 0, 1, 64, C, R, bool(af), bool(al))
+        sf, sc, fw, bw = api.layout_tables(lay)
+        osf, osc, ofw, obw = oracle.tables(T, C, R, af, al)
+        assert np.array_equal(sf, np.array(osf, np.int32)), (T, C, R, af, al)
+        assert np.array_equal(sc, np.array(osc, np.int32))
+        assert np.array_equal(fw, np.array(ofw, np.int32)), (T, C, R, af, al, fw, ofw)
+        assert np.array_equal(bw, np.array(obw, np.int32))
+
+
+def test_worked_example_tables():
+    sf, sc, fw, bw = api.layout_tables(api.Layout(1, 15, 4032, 512, 24, 128))
+    assert list(sf[7][:sc[7]]) == [0, 6, 7, 8, 14]
+    assert list(fw[7]) == [1, 6] and list(bw[7]) == [9, 14]
+
+
+def test_table_validation():
+    with pytest.raises(api.HybError) as e:
+        api.layout_tables(api.Layout(1, 0, 1, 0, 1, 64))
+    assert e.value.status == api.HYB_ERR_INVALID_ARGUMENT
+    with pytest.raises(api.HybError):
+        api.layout_tables(api.Layout(1, 5, 1, 0, 1, 64, chunk_frames=0))
+    with pytest.raises(api.HybError):
+        api.layout_tables(api.Layout(1, 5, 1, 0, 1, 64, chunk_radius=-1))
+
+
+def test_workspace_size_and_dtype_rules():
+    lay = api.Layout(1, 15, 4032, 512, 24, 128)
+    n = api.workspace_size(lay, "bf16")
+    # fp32 branch outputs (2 x 743 MB) + bf16 A' (743 MB) dominate
+    assert 2.2e9 < n < 3.0e9
+    assert api.workspace_size(lay, "bf16", "fp8") > n
+    with pytest.raises(api.HybError) as e:
+        api.workspace_size(lay, "f32", "fp8")
+    assert e.value.status == api.HYB_ERR_UNSUPPORTED
+    with pytest.raises(api.HybError) as e:
+        api.workspace_size(api.Layout(1, 15, 64, 16, 2, 32), "bf16")
+    assert e.value.status == api.HYB_ERR_UNSUPPORTED
+    assert api.workspace_size(api.Layout(1, 15, 64, 16, 2, 32), "f32") > 0
+    with pytest.raises(api.HybError) as e:
+        api.workspace_size(api.Layout(1, 15, 64, 16, 2, 48), "f32")
+    assert e.value.status == api.HYB_ERR_UNSUPPORTED
+
+
+def _call(lay, **over):
+    """Call hyb_attn_forward with fake but aligned addresses; every case here
+    must fail validation before any HIP call is made."""
+    lib = api.load()
+    c = lay.c()
+    base = 1 << 40
+    T4 = api._Tensor
+    H, D = lay.heads, lay.head_dim
+    st = (lay.n_video * H * D, H * D, D)
+    args = dict(act=1, soft=1, x=base, q=T4(base + (1 << 34), *st), k=T4(base + (2 << 34), *st),
+                v=T4(base + (3 << 34), *st), tk=T4(base + (4 << 34), *st), tv=T4(base + (5 << 34), *st),
+                wgs=base + (6 << 34), wgl=base + (7 << 34), wos=base + (8 << 34), wol=base + (9 << 34),
+                rms=base + (10 << 34), scale=0.0, eps=1e-6, y=base + (11 << 34), ws=base + (12 << 34),
+                wsb=1 << 40, stream=None)
+    args.update(over)
+    r = lib.hyb_attn_forward(ctypes.byref(c), args["act"], args["soft"], args["x"], args["q"], args["k"],
+                             args["v"], args["tk"], args["tv"], args["wgs"], args["wgl"], args["wos"],
+                             args["wol"], args["rms"], args["scale"], args["eps"], args["y"], args["ws"],
+                             args["wsb"], args["stream"], None)
+    return r, lib.hyb_last_error().decode()
+
+
+def test_forward_validation_errors():
+    lay = api.Layout(1, 15, 1024, 128, 8, 64)
+    T4 = api._Tensor
+    assert _call(lay, x=None)[0] == api.HYB_ERR_INVALID_ARGUMENT
+    assert _call(lay, q=T4(None, 0, 0, 0))[0] == api.HYB_ERR_INVALID_ARGUMENT
+    assert _call(lay, wgs=(1 << 40) + 2)[0] == api.HYB_ERR_INVALID_ARGUMENT       # misaligned
+    assert _call(lay, ws=(1 << 40) + 16)[0] == api.HYB_ERR_INVALID_ARGUMENT       # workspace not 256-aligned
+    assert _call(lay, k=T4(1 << 41, 1024 * 512, 512 + 4, 64))[0] == api.HYB_ERR_INVALID_ARGUMENT  # stride
+    assert _call(lay, eps=0.0)[0] == api.HYB_ERR_INVALID_ARGUMENT
+    assert _call(lay, eps=float("nan"))[0] == api.HYB_ERR_INVALID_ARGUMENT
+    assert _call(lay, scale=-1.0)[0] == api.HYB_ERR_INVALID_ARGUMENT
+    assert _call(lay, act=0, soft=2)[0] == api.HYB_ERR_UNSUPPORTED
+    assert _call(lay, act=2, soft=2)[0] == api.HYB_ERR_UNSUPPORTED
+    r, msg = _call(lay, wsb=1000)
+    assert r == api.HYB_ERR_WORKSPACE_TOO_SMALL and "needs" in msg
+    # y overlapping q is rejected
+    r, msg = _call(lay, y=(1 << 40) + (1 << 34) + 4096)
+    assert r == api.HYB_ERR_INVALID_ARGUMENT and "overlaps" in msg
+    # text tensors may be NULL only without text
+    assert _call(lay, tk=T4(None, 0, 0, 0))[0] == api.HYB_ERR_INVALID_ARGUMENT
+    bad = api.Layout(1, 15, 1024, 128, 8, 64, chunk_frames=0)
+    assert _call(bad)[0] == api.HYB_ERR_INVALID_ARGUMENT
+    assert _call(api.Layout(0, 15, 1024, 128, 8, 64))[0] == api.HYB_ERR_INVALID_ARGUMENT
+    assert api.load().hyb_status_string(3) == b"workspace too small"
