@@ -91,7 +91,7 @@ def cpu_baseline(w, inp, budget_s=20.0):
         t0 = time.perf_counter()
         st = oracle.linear_states(inp["k"], inp["v"], inp["text_k"], inp["text_v"], lay)
         t_states = time.perf_counter() - t0
-        per = 2
+        per = 16
         tok = sample_tokens(w, per_frame=per)
         t0 = time.perf_counter()
         o_s = oracle.softmax_branch(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], lay, tokens=tok)
@@ -118,6 +118,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the layer shards by heads; "
@@ -128,6 +130,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
+        return
     w = WORKLOADS[args.workload]
     print("bench: generating %s" % w.name, file=sys.stderr, flush=True)
     inp = make_inputs(w)

@@ -129,7 +129,7 @@ def workspace_size(lay: Layout, act="bf16", soft=None):
 
 
 def _tensor4(t):
-    if t is None:
+    if t is None or t.numel() == 0:
         return _Tensor(None, 0, 0, 0)
     if t.dim() != 4 or t.stride(3) != 1:
         raise ValueError("expected a [B, tokens, H, D] tensor with contiguous D")

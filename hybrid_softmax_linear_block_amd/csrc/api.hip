@@ -304,9 +304,9 @@ hyb_status hyb_attn_forward(const hyb_layout* layout, hyb_dtype act, hyb_dtype s
     a.comb_hi = (hyb::bf16_t*)(ws + plan.off[W_CHI]);
     a.comb_lo = (hyb::bf16_t*)(ws + plan.off[W_CLO]);
     a.comb_z = (float*)(ws + plan.off[W_CZ]);
-    a.ap = (hyb::bf16_t*)(ws + plan.off[W_AP]);
+    a.ap = (uint16_t*)(ws + plan.off[W_AP]);
     a.wg_t = (hyb::bf16_t*)(ws + plan.off[W_WG]);
-    a.wo_t = (hyb::bf16_t*)(ws + plan.off[W_WO]);
+    a.wo_t = (uint16_t*)(ws + plan.off[W_WO]);
     a.q8 = (uint8_t*)(ws + plan.off[W_Q8]);
     a.k8 = (uint8_t*)(ws + plan.off[W_K8]);
     a.v8t = (uint8_t*)(ws + plan.off[W_V8]);

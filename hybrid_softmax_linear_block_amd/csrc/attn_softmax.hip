@@ -23,56 +23,62 @@
 
 namespace hyb {
 
+// Key sequence of one query frame: up to three contiguous video frame ranges
+// of S(f) and the text, as 64-key tiles.  Kept in scalars (wave-uniform).
 struct KeySeq {
-  int nseg;
-  int start[4], len[4], tiles[4];
-  bool text[4];
-  int total;
+  int st0, ln0, nt0, st1, ln1, nt1, st2, ln2, nt2, ntt, total;
 };
 
 __device__ __forceinline__ KeySeq key_sequence(const Dims& d, int f) {
-  KeySeq ks;
   const SoftRanges sr = soft_ranges(d.g, f);
-  ks.nseg = 0;
-  ks.total = 0;
-  for (int r = 0; r < sr.n; ++r) {
-    ks.start[ks.nseg] = sr.lo[r] * d.n;
-    ks.len[ks.nseg] = (sr.hi[r] - sr.lo[r]) * d.n;
-    ks.text[ks.nseg] = false;
-    ++ks.nseg;
-  }
-  if (d.L > 0) {
-    ks.start[ks.nseg] = 0;
-    ks.len[ks.nseg] = d.L;
-    ks.text[ks.nseg] = true;
-    ++ks.nseg;
-  }
-  for (int s = 0; s < ks.nseg; ++s) {
-    ks.tiles[s] = (ks.len[s] + 63) >> 6;
-    ks.total += ks.tiles[s];
-  }
+  KeySeq ks;
+  ks.st0 = sr.lo[0] * d.n;
+  ks.ln0 = (sr.hi[0] - sr.lo[0]) * d.n;
+  ks.st1 = sr.n > 1 ? sr.lo[1] * d.n : 0;
+  ks.ln1 = sr.n > 1 ? (sr.hi[1] - sr.lo[1]) * d.n : 0;
+  ks.st2 = sr.n > 2 ? sr.lo[2] * d.n : 0;
+  ks.ln2 = sr.n > 2 ? (sr.hi[2] - sr.lo[2]) * d.n : 0;
+  ks.nt0 = (ks.ln0 + 63) >> 6;
+  ks.nt1 = (ks.ln1 + 63) >> 6;
+  ks.nt2 = (ks.ln2 + 63) >> 6;
+  ks.ntt = (d.L + 63) >> 6;
+  ks.total = ks.nt0 + ks.nt1 + ks.nt2 + ks.ntt;
   return ks;
 }
 
-// frame visiting order: anchors first (they see every frame), then the rest
-__device__ __forceinline__ int frame_by_cost(const FrameGeom& g, int i) {
-  const bool a0 = g.af;
-  const bool a1 = g.al && !(g.af && g.T == 1);
-  if (a0) { if (i == 0) return 0; --i; }
-  if (a1) { if (i == 0) return g.T - 1; --i; }
-  return interior_begin(g) + i;
+// tile t -> first key, number of valid keys, text or video
+__device__ __forceinline__ void locate(const KeySeq& ks, int L, int t, int& key0, int& valid, bool& text) {
+  text = false;
+  if (t < ks.nt0) { key0 = ks.st0 + t * 64; valid = min(64, ks.ln0 - t * 64); return; }
+  t -= ks.nt0;
+  if (t < ks.nt1) { key0 = ks.st1 + t * 64; valid = min(64, ks.ln1 - t * 64); return; }
+  t -= ks.nt1;
+  if (t < ks.nt2) { key0 = ks.st2 + t * 64; valid = min(64, ks.ln2 - t * 64); return; }
+  t -= ks.nt2;
+  text = true;
+  key0 = t * 64;
+  valid = min(64, L - t * 64);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Lazy rescaling: the running maximum only moves when a row's tile maximum
+// exceeds it by more than 2^8 (log2 units); probabilities then stay <= 2^8,
+// exact enough in bf16 and fp32, and the O rescale is skipped on most tiles.
+constexpr float kRescaleSlack = 8.f;
+
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void k_attn_bf16(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk,
-                                                        Tensor4 tv, float sl2, float* __restrict__ os) {
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
+void k_attn_bf16(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv, float sl2,
+                 float* __restrict__ os) {
   constexpr int BM = 32 * NW;
-  constexpr int NT = 64 * NW;
   constexpr int G = D / 8;                 // 16-byte granules per row
-  constexpr int GPT = (64 * G) / NT;       // granules per thread per tile
+  constexpr int RPC = 64 / G;              // rows per 1 KB chunk (one wave-wide LDS-DMA load)
+  constexpr int CHUNKS = 64 / RPC;         // chunks per 64-key tile
+  constexpr int CPW = CHUNKS / NW;         // chunks per wave
   constexpr int KS = D / 16;               // k-steps of Q K^T
   constexpr int DB = D / 32;               // 32-wide d blocks of O^T
-  static_assert((64 * G) % NT == 0, "tile granules must split evenly");
+  static_assert(CHUNKS % NW == 0, "tile chunks must split evenly over waves");
   using SW = Swz<D>;
 
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][64 * D];
@@ -88,8 +94,35 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bf16(Dims d, Tensor4 q, Tensor
   const int h = w % d.H; w /= d.H;
   const int b = w % d.B; w /= d.B;
   const int f = frame_by_cost(d.g, (int)w);
-
   const KeySeq ks = key_sequence(d, f);
+
+  // ---- K and V tiles: wave-wide direct-to-LDS loads of 1 KB chunks; lane l
+  // of a chunk fills row (l / G), physical granule (l % G), which holds the
+  // logical granule (l % G) ^ swizzle(row).  Rows past the tile's valid keys
+  // repeat the last valid row (their scores are masked to -inf).
+  auto issue = [&](int t, int buf) -> int {
+    int key0, valid;
+    bool text;
+    locate(ks, d.L, t, key0, valid, text);
+    const Tensor4& kt = text ? tk : k;
+    const Tensor4& vt = text ? tv : v;
+    const bf16_t* kb = (const bf16_t*)kt.p + tok_off(kt, b, key0, h);
+    const bf16_t* vb = (const bf16_t*)vt.p + tok_off(vt, b, key0, h);
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int c = wave * CPW + i;
+      const int r = c * RPC + lane / G;
+      const int gl = (lane % G) ^ SW::key(r);
+      const int rs = min(r, valid - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(kb + (long long)rs * kt.st + gl * 8),
+                                       (lds_void*)&Ks[buf][c * RPC * D], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vb + (long long)rs * vt.st + gl * 8),
+                                       (lds_void*)&Vs[buf][c * RPC * D], 16, 0, 0);
+    }
+    return valid;
+  };
+
+  int cur_valid = issue(0, 0);
 
   // ---- Q^T fragments (B operand): lane holds row l32, d = 16*s + 8*half + 0..7
   const int prow = qt * BM + wave * 32 + l32;
@@ -99,10 +132,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bf16(Dims d, Tensor4 q, Tensor
   {
     const bf16_t* qp = (const bf16_t*)q.p + tok_off(q, b, qtok, h) + 8 * half;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      uint4 u = row_ok ? ldg16(qp + 16 * s) : make_uint4(0, 0, 0, 0);
-      qf[s] = __builtin_bit_cast(bf16x8, u);
-    }
+    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, ldg16(qp + 16 * s));
   }
 
   floatx16 oacc[DB];
@@ -111,49 +141,17 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bf16(Dims d, Tensor4 q, Tensor
   float m_run = -INFINITY;  // running max in log2 units (already scaled)
   float l_run = 0.f;        // this lane's partial row sum
 
-  uint4 kreg[GPT], vreg[GPT];
-  int cur_valid = 0, nxt_valid = 0;
-
-  auto fetch = [&](int t, int& valid) {
-    int s = 0, lt = t;
-    while (s < ks.nseg - 1 && lt >= ks.tiles[s]) { lt -= ks.tiles[s]; ++s; }
-    const int key0 = ks.start[s] + lt * 64;
-    valid = min(64, ks.len[s] - lt * 64);
-    const Tensor4& kt = ks.text[s] ? tk : k;
-    const Tensor4& vt = ks.text[s] ? tv : v;
-    const bf16_t* kb = (const bf16_t*)kt.p + tok_off(kt, b, key0, h);
-    const bf16_t* vb = (const bf16_t*)vt.p + tok_off(vt, b, key0, h);
-#pragma unroll
-    for (int r = 0; r < GPT; ++r) {
-      const int gi = tid + r * NT;
-      const int row = gi / G, col = (gi % G) * 8;
-      if (row < valid) {
-        kreg[r] = ldg16(kb + (long long)row * kt.st + col);
-        vreg[r] = ldg16(vb + (long long)row * vt.st + col);
-      } else {
-        kreg[r] = make_uint4(0, 0, 0, 0);
-        vreg[r] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < GPT; ++r) {
-      const int gi = tid + r * NT;
-      const int row = gi / G, col = (gi % G) * 8;
-      *(uint4*)&Ks[buf][SW::off(row, col)] = kreg[r];
-      *(uint4*)&Vs[buf][SW::off(row, col)] = vreg[r];
-    }
-  };
-
-  fetch(0, cur_valid);
-  stash(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 landed in LDS
   __syncthreads();
+
+  const int grp = lane >> 4, j16 = lane & 15;
+  const int dsub = (grp & 1) * 16 + 4 * (j16 & 3);
 
   for (int t = 0; t < ks.total; ++t) {
     const int buf = t & 1;
     const bool more = t + 1 < ks.total;
-    if (more) fetch(t + 1, nxt_valid);
+    int nxt_valid = 0;
+    if (more) nxt_valid = issue(t + 1, buf ^ 1);
 
     // ---- scores S^T for two 32-key blocks
     floatx16 sacc[2];
@@ -176,21 +174,22 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bf16(Dims d, Tensor4 q, Tensor
           if (key >= cur_valid) sacc[kb][j] = -INFINITY;
         }
     }
-    // ---- online softmax (per lane = per query row)
-    float mx = sacc[0][0];
+    // ---- online softmax (per lane = per query row), lazily rescaled
+    float mx = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, fmaxf(sacc[0][j], sacc[1][j]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    const bool grow = mx > m_run + kRescaleSlack;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * sl2);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+      for (int i = 0; i < DB; ++i)
 #pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) oacc[i][j] *= alpha;
+        for (int j = 0; j < 16; ++j) oacc[i][j] *= alpha;
+    }
 
     bf16x8 pf[4];
 #pragma unroll
@@ -200,7 +199,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bf16(Dims d, Tensor4 q, Tensor
         bf16x8 p;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pv = exp2f(fmaf(sacc[kb][8 * hb + e], sl2, -m_new));
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * hb + e], sl2, -m_run));
           l_run += pv;
           p[e] = static_cast<__bf16>(pv);
         }
@@ -208,8 +207,6 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bf16(Dims d, Tensor4 q, Tensor
       }
 
     // ---- O^T += V^T P^T; V^T operand via transposing LDS reads
-    const int grp = lane >> 4, j16 = lane & 15;
-    const int dsub = (grp & 1) * 16 + 4 * (j16 & 3);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int kb0 = (kk >> 1) * 32 + (kk & 1) * 16 + 4 * half + (j16 >> 2);
@@ -221,8 +218,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bf16(Dims d, Tensor4 q, Tensor
       }
     }
 
-    if (more) stash(buf ^ 1);
     cur_valid = nxt_valid;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile landed
     __syncthreads();
   }
 

@@ -1,9 +1,447 @@
-// fp8 (OCP e4m3) softmax branch: placeholder until the e4m3 kernels land.
+// fp8 (OCP e4m3) softmax branch.
+//
+// The VDN-H3 article's performance section measures an "FP8 version" of the
+// model without saying which operations run in fp8; here the softmax
+// branch's Q, K, V (video and text) are quantised per (tensor, batch, head)
+// with scale = absmax / 448 and both Q K^T and P V run on the gfx950
+// 32x32x64 f8f6f4 MFMA with fp32 accumulation.  P is pre-scaled by 2^8 before
+// its e4m3 rounding (so probabilities down to 2^-17 survive) and the scale is
+// removed in fp32.  The linear branch and the epilogue stay in bf16/fp32.
+//
+// Layouts written by the quantiser (all per call, in the workspace):
+//   q8, k8, tk8   [B][tokens][H][D] e4m3 bytes
+//   v8t, tv8t     [B][H][frame][tile][D][64] e4m3 bytes: each 64-key tile of
+//                 a frame (or of the text) transposed, keys in the order the
+//                 P operand holds them (see slot_of_key)
+//   scales        [5][B][H] fp32 (q, k, v, text_k, text_v)
 #include "kernels_bf16.h"
 
 namespace hyb {
 
-hipError_t launch_quant_fp8(const Dims&, const Bf16Args&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_softmax_fp8(const Dims&, const Bf16Args&, hipStream_t) { return hipErrorNotSupported; }
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+// Key order inside a 64-key tile as the P operand of the P V MFMA holds it.
+// Lane half h, element e (0..31) of the operand is key
+//   (e/16)*32 + 8*((e%16)/4) + 4*h + e%4,
+// i.e. the two 32-key score blocks in their C-register order.  Inverse:
+__device__ __forceinline__ int slot_of_key(int key) {
+  const int kb = key >> 5, r = key & 31;
+  const int jg = r >> 3, half = (r >> 2) & 1, e4 = r & 3;
+  return 32 * half + 16 * kb + 4 * jg + e4;
+}
+
+__device__ __forceinline__ uint32_t f32_bits_abs(float x) { return __float_as_uint(x) & 0x7fffffffu; }
+
+// Two floats -> two e4m3 bytes in the low (sel=0) or high (sel=1) half of `old`.
+template <bool SEL>
+__device__ __forceinline__ int cvt_e4m3x2(float a, float b, int old) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, SEL);
+}
+
+__global__ void k_zero_u32(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// ---- absmax per (tensor, b, h): one workgroup per (tensor, b, h, 256-token chunk)
+struct QuantSrc {
+  Tensor4 t[5];
+  int tokens[5];
+};
+
+__device__ __forceinline__ void decode_chunk(const QuantSrc& src, const Dims& d, int chunk_tok, unsigned w, int& t,
+                                             int& b, int& h, int& c) {
+  for (t = 0; t < 5; ++t) {
+    const int nc = (src.tokens[t] + chunk_tok - 1) / chunk_tok;
+    const unsigned cnt = (unsigned)(nc * d.B * d.H);
+    if (w < cnt) break;
+    w -= cnt;
+  }
+  const int nc = (src.tokens[t] + chunk_tok - 1) / chunk_tok;
+  c = w % nc;
+  w /= nc;
+  h = w % d.H;
+  b = w / d.H;
+}
+
+__global__ __launch_bounds__(256) void k_absmax(Dims d, QuantSrc src, uint32_t* __restrict__ absmax) {
+  int t, b, h, c;
+  decode_chunk(src, d, 256, blockIdx.x, t, b, h, c);
+  const Tensor4& x = src.t[t];
+  const int G = d.D / 8;
+  const int tok0 = c * 256, tok1 = min(src.tokens[t], tok0 + 256);
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < (tok1 - tok0) * G; i += 256) {
+    const int tok = tok0 + i / G, col = (i % G) * 8;
+    const uint4 u = ldg16((const bf16_t*)x.p + tok_off(x, b, tok, h) + col);
+    const uint32_t* uu = (const uint32_t*)&u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m = max(m, f32_bits_abs(__uint_as_float(uu[j] << 16)));
+      m = max(m, f32_bits_abs(__uint_as_float(uu[j] & 0xffff0000u)));
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  __shared__ uint32_t red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t r = max(max(red[0], red[1]), max(red[2], red[3]));
+    atomicMax(absmax + (t * d.B + b) * d.H + h, r);
+  }
+}
+
+__device__ __forceinline__ float scale_of(uint32_t amax_bits) {
+  const float a = __uint_as_float(amax_bits);
+  return a > 0.f ? a / 448.f : 1.f;
+}
+
+// scales[i] = absmax[i] / 448 (1 for an all-zero or empty tensor)
+__global__ void k_scales(const uint32_t* __restrict__ absmax, float* __restrict__ scales, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) scales[i] = scale_of(absmax[i]);
+}
+
+// ---- row quantiser for q, k, text_k -> [B][tokens][H][D] bytes
+__global__ __launch_bounds__(256) void k_quant_rows(Dims d, QuantSrc src, const uint32_t* __restrict__ absmax,
+                                                    uint8_t* q8, uint8_t* k8, uint8_t* tk8) {
+  int t, b, h, c;
+  decode_chunk(src, d, 256, blockIdx.x, t, b, h, c);
+  // tensors 0 (q), 1 (k), 3 (text_k) quantise row-wise; v and text_v elsewhere
+  if (t == 2 || t == 4) return;
+  const int idx = (t * d.B + b) * d.H + h;
+  const float s = scale_of(absmax[idx]);
+  uint8_t* out = t == 0 ? q8 : (t == 1 ? k8 : tk8);
+  const float inv = 1.f / s;
+  const Tensor4& x = src.t[t];
+  const int G = d.D / 8;
+  const int tok0 = c * 256, tok1 = min(src.tokens[t], tok0 + 256);
+  for (int i = threadIdx.x; i < (tok1 - tok0) * G; i += 256) {
+    const int tok = tok0 + i / G, col = (i % G) * 8;
+    const uint4 u = ldg16((const bf16_t*)x.p + tok_off(x, b, tok, h) + col);
+    const uint32_t* uu = (const uint32_t*)&u;
+    int w0 = 0, w1 = 0;
+    w0 = cvt_e4m3x2<false>(__uint_as_float(uu[0] << 16) * inv, __uint_as_float(uu[0] & 0xffff0000u) * inv, w0);
+    w0 = cvt_e4m3x2<true>(__uint_as_float(uu[1] << 16) * inv, __uint_as_float(uu[1] & 0xffff0000u) * inv, w0);
+    w1 = cvt_e4m3x2<false>(__uint_as_float(uu[2] << 16) * inv, __uint_as_float(uu[2] & 0xffff0000u) * inv, w1);
+    w1 = cvt_e4m3x2<true>(__uint_as_float(uu[3] << 16) * inv, __uint_as_float(uu[3] & 0xffff0000u) * inv, w1);
+    const long long o = (((long long)b * src.tokens[t] + tok) * d.H + h) * d.D + col;
+    *(uint2*)(out + o) = make_uint2((uint32_t)w0, (uint32_t)w1);
+  }
+}
+
+// ---- V quantiser: one workgroup per (b, h, frame-or-text, 64-key tile);
+// output tile [D][64] with keys in slot order.
+template <int D>
+__global__ __launch_bounds__(256) void k_quant_vt(Dims d, QuantSrc src, const uint32_t* __restrict__ absmax,
+                                                  uint8_t* __restrict__ v8t, uint8_t* __restrict__ tv8t) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[D * 64];
+  const int ntv = (d.n + 63) / 64, ntt = (d.L + 63) / 64;
+  const int per_bh = d.T * ntv + ntt;
+  int w = blockIdx.x;
+  const int slot = w % per_bh; w /= per_bh;
+  const int h = w % d.H;
+  const int b = w / d.H;
+  const bool text = slot >= d.T * ntv;
+  int key0, valid;
+  if (!text) {
+    const int f = slot / ntv, tt = slot % ntv;
+    key0 = f * d.n + tt * 64;
+    valid = min(64, d.n - tt * 64);
+  } else {
+    const int tt = slot - d.T * ntv;
+    key0 = tt * 64;
+    valid = min(64, d.L - tt * 64);
+  }
+  const int tsel = text ? 4 : 2;
+  const Tensor4& x = src.t[tsel];
+  const float inv = 1.f / scale_of(absmax[(tsel * d.B + b) * d.H + h]);
+  constexpr int G = D / 8;
+  for (int i = threadIdx.x; i < 64 * G; i += 256) {
+    const int key = i / G, col = (i % G) * 8;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (key < valid) u = ldg16((const bf16_t*)x.p + tok_off(x, b, key0 + key, h) + col);
+    const uint32_t* uu = (const uint32_t*)&u;
+    const int sl = slot_of_key(key);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int w2 = cvt_e4m3x2<false>(__uint_as_float(uu[j] << 16) * inv,
+                                       __uint_as_float(uu[j] & 0xffff0000u) * inv, 0);
+      tile[(col + 2 * j) * 64 + sl] = (uint8_t)(w2 & 0xff);
+      tile[(col + 2 * j + 1) * 64 + sl] = (uint8_t)((w2 >> 8) & 0xff);
+    }
+  }
+  __syncthreads();
+  uint8_t* out = text ? tv8t + ((long long)(b * d.H + h) * ntt + (slot - d.T * ntv)) * (D * 64)
+                      : v8t + ((long long)(b * d.H + h) * d.T * ntv + slot) * (D * 64);
+  for (int i = threadIdx.x; i < D * 64 / 16; i += 256) *(uint4*)(out + i * 16) = *(const uint4*)(tile + i * 16);
+}
+
+// ---- fp8 flash kernel.  Same decomposition as the bf16 kernel; tiles never
+// straddle frames (per-frame 64-key tiles) so that they line up with the
+// transposed V tiles.
+__device__ __forceinline__ floatx16 mfma_f8(const i32x8& a, const i32x8& b, const floatx16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// byte-row tile swizzle on 16-byte granules (64- or 128-byte rows)
+template <int ROWB>
+__device__ __forceinline__ int swz8(int row, int byte) {
+  const int g = byte >> 4;
+  const int k = ROWB == 64 ? ((row >> 2) & 3) : ((row >> 1) & 7);
+  return row * ROWB + (((g ^ k)) << 4) + (byte & 15);
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void k_attn_fp8(Dims d, const uint8_t* __restrict__ q8,
+                                                       const uint8_t* __restrict__ k8,
+                                                       const uint8_t* __restrict__ v8t,
+                                                       const uint8_t* __restrict__ tk8,
+                                                       const uint8_t* __restrict__ tv8t,
+                                                       const float* __restrict__ scales, float sl2,
+                                                       float* __restrict__ os) {
+  constexpr int BM = 32 * NW, NT = 64 * NW;
+  constexpr int KSTEP = D / 64;      // 64-deep k-steps of Q K^T
+  constexpr int DB = D / 32;         // d blocks of O^T
+  constexpr int KG = 64 * D / 16;    // 16-byte granules of a K tile (== of a V tile)
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[2][64 * D];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs[2][D * 64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int qtiles = (d.n + BM - 1) / BM;
+  unsigned w = blockIdx.x;
+  const int qt = w % qtiles; w /= qtiles;
+  const int h = w % d.H; w /= d.H;
+  const int b = w % d.B; w /= d.B;
+  const int f = frame_by_cost(d.g, (int)w);
+  const float sq = scales[(0 * d.B + b) * d.H + h], sk = scales[(1 * d.B + b) * d.H + h];
+  const float sv = scales[(2 * d.B + b) * d.H + h];
+  const float stk = scales[(3 * d.B + b) * d.H + h], stv = scales[(4 * d.B + b) * d.H + h];
+
+  // key sequence: every frame of S(f) as its own run of tiles, then the text
+  const SoftRanges sr = soft_ranges(d.g, f);
+  const int ntv = (d.n + 63) / 64, ntt = (d.L + 63) / 64;
+  int nframes = 0;
+  for (int r = 0; r < sr.n; ++r) nframes += sr.hi[r] - sr.lo[r];
+  const int total = nframes * ntv + ntt;
+
+  const int prow = qt * BM + wave * 32 + l32;
+  const bool row_ok = prow < d.n;
+  const long long qtok = (long long)f * d.n + (row_ok ? prow : 0);
+  i32x8 qf[KSTEP];
+  {
+    const uint8_t* qp = q8 + (((long long)b * d.N + qtok) * d.H + h) * D + 32 * half;
+#pragma unroll
+    for (int s = 0; s < KSTEP; ++s) {
+      const uint4 u0 = row_ok ? *(const uint4*)(qp + 64 * s) : make_uint4(0, 0, 0, 0);
+      const uint4 u1 = row_ok ? *(const uint4*)(qp + 64 * s + 16) : make_uint4(0, 0, 0, 0);
+      qf[s] = i32x8{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+    }
+  }
+
+  floatx16 oacc_v[DB], oacc_t[DB];  // video and text parts (different V scales)
+#pragma unroll
+  for (int i = 0; i < DB; ++i) { oacc_v[i] = zero16(); oacc_t[i] = zero16(); }
+  float m_run = -INFINITY, l_run = 0.f;
+
+  uint4 kreg[(KG + NT - 1) / NT], vreg[(KG + NT - 1) / NT];
+  constexpr int GPT = (KG + NT - 1) / NT;
+  int cur_valid = 0, nxt_valid = 0;
+  bool cur_text = false, nxt_text = false;
+
+  auto fetch = [&](int t, int& valid, bool& is_text) {
+    const uint8_t* kb;
+    const uint8_t* vb;
+    long long kstride = (long long)d.H * D;
+    if (t < nframes * ntv) {
+      int fi = t / ntv, tt = t % ntv;
+      int g = 0;
+      for (int r = 0; r < sr.n; ++r) {
+        const int len = sr.hi[r] - sr.lo[r];
+        if (fi < len) { g = sr.lo[r] + fi; break; }
+        fi -= len;
+      }
+      valid = min(64, d.n - tt * 64);
+      is_text = false;
+      kb = k8 + (((long long)b * d.N + (long long)g * d.n + tt * 64) * d.H + h) * D;
+      vb = v8t + ((long long)(b * d.H + h) * d.T * ntv + (long long)g * ntv + tt) * (D * 64);
+    } else {
+      const int tt = t - nframes * ntv;
+      valid = min(64, d.L - tt * 64);
+      is_text = true;
+      kb = tk8 + (((long long)b * d.L + tt * 64) * d.H + h) * D;
+      vb = tv8t + ((long long)(b * d.H + h) * ntt + tt) * (D * 64);
+    }
+#pragma unroll
+    for (int r = 0; r < GPT; ++r) {
+      const int gi = tid + r * NT;
+      kreg[r] = make_uint4(0, 0, 0, 0);
+      vreg[r] = make_uint4(0, 0, 0, 0);
+      if (gi < KG) {
+        const int row = gi / (D / 16), col = (gi % (D / 16)) * 16;
+        if (row < valid) kreg[r] = *(const uint4*)(kb + (long long)row * kstride + col);
+        vreg[r] = *(const uint4*)(vb + gi * 16);
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < GPT; ++r) {
+      const int gi = tid + r * NT;
+      if (gi < KG) {
+        const int row = gi / (D / 16), col = (gi % (D / 16)) * 16;
+        *(uint4*)&Ks[buf][swz8<D>(row, col)] = kreg[r];
+        const int vrow = gi / 4, vcol = (gi % 4) * 16;
+        *(uint4*)&Vs[buf][swz8<64>(vrow, vcol)] = vreg[r];
+      }
+    }
+  };
+
+  fetch(0, cur_valid, cur_text);
+  stash(0);
+  __syncthreads();
+  const float pscale = 256.f;
+  for (int t = 0; t < total; ++t) {
+    const int buf = t & 1;
+    const bool more = t + 1 < total;
+    if (more) fetch(t + 1, nxt_valid, nxt_text);
+
+    floatx16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = zero16();
+      const int row = kb * 32 + l32;
+#pragma unroll
+      for (int s = 0; s < KSTEP; ++s) {
+        const uint4 a0 = *(const uint4*)&Ks[buf][swz8<D>(row, 64 * s + 32 * half)];
+        const uint4 a1 = *(const uint4*)&Ks[buf][swz8<D>(row, 64 * s + 32 * half + 16)];
+        const i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        sacc[kb] = mfma_f8(a, qf[s], sacc[kb]);
+      }
+    }
+    const float dq = sq * (cur_text ? stk : sk) * sl2;  // logit scale in log2 units
+    if (cur_valid < 64) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+          if (key >= cur_valid) sacc[kb][j] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * dq);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        oacc_v[i][j] *= alpha;
+        oacc_t[i][j] *= alpha;
+      }
+    // P (x 2^8) to e4m3, packed in operand order e = 16*kb + j
+    int pw[8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; j += 4) {
+        const float p0 = exp2f(fmaf(sacc[kb][j], dq, -m_new));
+        const float p1 = exp2f(fmaf(sacc[kb][j + 1], dq, -m_new));
+        const float p2 = exp2f(fmaf(sacc[kb][j + 2], dq, -m_new));
+        const float p3 = exp2f(fmaf(sacc[kb][j + 3], dq, -m_new));
+        l_run += (p0 + p1) + (p2 + p3);
+        int wv = cvt_e4m3x2<false>(p0 * pscale, p1 * pscale, 0);
+        wv = cvt_e4m3x2<true>(p2 * pscale, p3 * pscale, wv);
+        pw[(16 * kb + j) / 4] = wv;
+      }
+    const i32x8 pf = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+#pragma unroll
+    for (int i = 0; i < DB; ++i) {
+      const int row = i * 32 + l32;
+      const uint4 a0 = *(const uint4*)&Vs[buf][swz8<64>(row, 32 * half)];
+      const uint4 a1 = *(const uint4*)&Vs[buf][swz8<64>(row, 32 * half + 16)];
+      const i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      if (cur_text) oacc_t[i] = mfma_f8(a, pf, oacc_t[i]);
+      else oacc_v[i] = mfma_f8(a, pf, oacc_v[i]);
+    }
+    if (more) stash(buf ^ 1);
+    cur_valid = nxt_valid;
+    cur_text = nxt_text;
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float cv = sv / (pscale * l_tot), ct = stv / (pscale * l_tot);
+  if (row_ok) {
+    float* op = os + (((long long)b * d.N + qtok) * d.H + h) * D;
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d0 = i * 32 + 8 * jg + 4 * half;
+        float4 o4;
+        o4.x = oacc_v[i][4 * jg] * cv + oacc_t[i][4 * jg] * ct;
+        o4.y = oacc_v[i][4 * jg + 1] * cv + oacc_t[i][4 * jg + 1] * ct;
+        o4.z = oacc_v[i][4 * jg + 2] * cv + oacc_t[i][4 * jg + 2] * ct;
+        o4.w = oacc_v[i][4 * jg + 3] * cv + oacc_t[i][4 * jg + 3] * ct;
+        *(float4*)(op + d0) = o4;
+      }
+  }
+}
+
+static QuantSrc quant_src(const Dims& d, const Bf16Args& a) {
+  QuantSrc s;
+  s.t[0] = a.q; s.t[1] = a.k; s.t[2] = a.v; s.t[3] = a.tk; s.t[4] = a.tv;
+  s.tokens[0] = s.tokens[1] = s.tokens[2] = (int)d.N;
+  s.tokens[3] = s.tokens[4] = d.L;
+  return s;
+}
+
+hipError_t launch_quant_fp8(const Dims& d, const Bf16Args& a, hipStream_t s) {
+  const QuantSrc src = quant_src(d, a);
+  const int n = 5 * d.B * d.H;
+  hipLaunchKernelGGL(k_zero_u32, dim3((n + 255) / 256), dim3(256), 0, s, a.absmax, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  long long chunks = 0;
+  for (int t = 0; t < 5; ++t) chunks += (long long)((src.tokens[t] + 255) / 256) * d.B * d.H;
+  hipLaunchKernelGGL(k_absmax, dim3((unsigned)chunks), dim3(256), 0, s, d, src, a.absmax);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_scales, dim3((n + 255) / 256), dim3(256), 0, s, a.absmax, a.scales, n);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_quant_rows, dim3((unsigned)chunks), dim3(256), 0, s, d, src, a.absmax, a.q8, a.k8, a.tk8);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const long long vt = (long long)d.B * d.H * (d.T * ((d.n + 63) / 64) + (d.L + 63) / 64);
+  if (d.D == 128)
+    hipLaunchKernelGGL(k_quant_vt<128>, dim3((unsigned)vt), dim3(256), 0, s, d, src, a.absmax, a.v8t, a.tv8t);
+  else
+    hipLaunchKernelGGL(k_quant_vt<64>, dim3((unsigned)vt), dim3(256), 0, s, d, src, a.absmax, a.v8t, a.tv8t);
+  return hipGetLastError();
+}
+
+template <int D, int NW>
+static hipError_t launch_attn8(const Dims& d, const Bf16Args& a, hipStream_t s) {
+  constexpr int BM = 32 * NW;
+  const long long grid = (long long)((d.n + BM - 1) / BM) * d.H * d.B * d.T;
+  hipLaunchKernelGGL((k_attn_fp8<D, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, d, a.q8, a.k8, a.v8t, a.tk8,
+                     a.tv8t, a.scales, a.scale_log2, a.os);
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_fp8(const Dims& d, const Bf16Args& a, hipStream_t s) {
+  if (d.D == 128) return launch_attn8<128, 4>(d, a, s);
+  if (d.D == 64) return launch_attn8<64, 4>(d, a, s);
+  return hipErrorInvalidValue;
+}
 
 }  // namespace hyb

@@ -5,9 +5,12 @@
 // outputs differ in scale, so each gets its own content-dependent sigmoid gate
 // and its own output projection, and the result is added to the residual
 // stream; the linear branch is RMS-normalised before its element-wise gate.
-//   gate GEMM:   G = sigmoid(x [W_gs | W_gl]);
-//                A' = [G_s * O_s | G_l * (O_l * w / sqrt(mean(O_l^2) + eps))]  (bf16)
-//   output GEMM: y = x + A' [W_os ; W_ol]
+//   gate GEMM:   G = sigmoid(x [W_gs | W_gl])             (bf16 operands, exact inputs)
+//                A' = [G_s * O_s | G_l * (O_l * w / sqrt(mean(O_l^2) + eps))]
+//   output GEMM: y = x + A' [W_os ; W_ol]                 (fp16 operands)
+// A' is a computed intermediate, so it is rounded once, to fp16 (11-bit
+// significand, 8x finer than bf16); W_os / W_ol convert to fp16 exactly
+// within its range.  Values beyond +-65504 saturate.
 // Both GEMMs compute C^T = W^T X^T so that a lane owns one token (the RMS
 // factor is a per-lane scalar) and four consecutive features (vector stores).
 #include "kernels_bf16.h"
@@ -17,8 +20,8 @@ namespace hyb {
 enum { EPI_GATE = 0, EPI_OUT = 1 };
 
 struct GemmArgs {
-  const bf16_t* A;   // [M][K] token rows
-  const bf16_t* Bt;  // [N][K] feature rows (weights transposed)
+  const uint16_t* A;   // [M][K] token rows (bf16 or fp16 bits)
+  const uint16_t* Bt;  // [N][K] feature rows (weights transposed, same type)
   long long M;
   int N, K;
   int hid, H;
@@ -26,7 +29,7 @@ struct GemmArgs {
   // gate epilogue
   const float *os, *ol, *ss;
   const bf16_t* rmsw;
-  bf16_t* ap;
+  uint16_t* ap;
   float* gates_dbg;
   // output epilogue
   const bf16_t* x;
@@ -39,8 +42,8 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
   constexpr int BM = 2 * WTM * 32, BN = 2 * WFN * 32;
   constexpr int RA = BM / 32, RB = BN / 32;  // granules per thread per k-tile
   using SW = Swz<64>;
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
@@ -94,15 +97,20 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
     if (more) load(kt + 1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 bt[WTM];
+      uint4 bt[WTM];
 #pragma unroll
       for (int tb = 0; tb < WTM; ++tb)
-        bt[tb] = *(const bf16x8*)&As[buf][SW::off(wm * WTM * 32 + tb * 32 + l32, 16 * ks + 8 * half)];
+        bt[tb] = *(const uint4*)&As[buf][SW::off(wm * WTM * 32 + tb * 32 + l32, 16 * ks + 8 * half)];
 #pragma unroll
       for (int fb = 0; fb < WFN; ++fb) {
-        const bf16x8 a = *(const bf16x8*)&Bs[buf][SW::off(wn * WFN * 32 + fb * 32 + l32, 16 * ks + 8 * half)];
+        const uint4 a = *(const uint4*)&Bs[buf][SW::off(wn * WFN * 32 + fb * 32 + l32, 16 * ks + 8 * half)];
 #pragma unroll
-        for (int tb = 0; tb < WTM; ++tb) acc[fb][tb] = mfma32(a, bt[tb], acc[fb][tb]);
+        for (int tb = 0; tb < WTM; ++tb) {
+          if constexpr (EPI == EPI_GATE)
+            acc[fb][tb] = mfma32(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bt[tb]), acc[fb][tb]);
+          else
+            acc[fb][tb] = mfma32_f16(__builtin_bit_cast(halfx8, a), __builtin_bit_cast(halfx8, bt[tb]), acc[fb][tb]);
+        }
       }
     }
     if (more) stash(buf ^ 1);
@@ -142,8 +150,8 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
             val.w = o.w * __uint_as_float(wv.y & 0xffff0000u) * rinv;
           }
           uint2 st;
-          st.x = pack_bf16x2(g0 * val.x, g1 * val.y);
-          st.y = pack_bf16x2(g2 * val.z, g3 * val.w);
+          st.x = pack_f16x2(g0 * val.x, g1 * val.y);
+          st.y = pack_f16x2(g2 * val.z, g3 * val.w);
           *(uint2*)(g.ap + m * (2LL * g.hid) + n) = st;
           if (g.gates_dbg) *(float4*)(g.gates_dbg + m * (2LL * g.hid) + n) = make_float4(g0, g1, g2, g3);
         } else {
@@ -159,12 +167,12 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
 }
 
 // Weight transposes into the GEMMs' [N][K] operand layout.
-//   mode 0: out[2*hid][hid],  out[c][r] = c < hid ? W_gs[r][c] : W_gl[r][c - hid]
-//   mode 1: out[hid][2*hid],  out[c][r] = r < hid ? W_os[r][c] : W_ol[r - hid][c]
+//   mode 0: out[2*hid][hid] bf16,  out[c][r] = c < hid ? W_gs[r][c] : W_gl[r][c - hid]
+//   mode 1: out[hid][2*hid] fp16,  out[c][r] = r < hid ? W_os[r][c] : W_ol[r - hid][c]
 __global__ __launch_bounds__(256) void k_weight_transpose(const bf16_t* __restrict__ s0,
                                                           const bf16_t* __restrict__ s1, int hid, int mode,
-                                                          bf16_t* __restrict__ out) {
-  __shared__ bf16_t t[64][66];
+                                                          uint16_t* __restrict__ out) {
+  __shared__ uint16_t t[64][66];
   const int R = mode == 0 ? hid : 2 * hid;  // source rows
   const int C = mode == 0 ? 2 * hid : hid;  // source cols
   const int tc = blockIdx.x % (C / 64), tr = blockIdx.x / (C / 64);
@@ -175,7 +183,7 @@ __global__ __launch_bounds__(256) void k_weight_transpose(const bf16_t* __restri
     bf16_t val;
     if (mode == 0) val = c < hid ? s0[(long long)r * hid + c] : s1[(long long)r * hid + c - hid];
     else val = r < hid ? s0[(long long)r * hid + c] : s1[(long long)(r - hid) * hid + c];
-    t[rr][cc] = val;
+    t[rr][cc] = mode == 0 ? val : f32_to_f16_sat(bf16_to_f32(val));
   }
   __syncthreads();
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(256) void k_weight_transpose(const bf16_t* __restri
 hipError_t launch_weights_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
   const int hid = d.hid;
   const unsigned grid = (unsigned)((hid / 64) * (2 * hid / 64));
-  hipLaunchKernelGGL(k_weight_transpose, dim3(grid), dim3(256), 0, s, a.wgs, a.wgl, hid, 0, a.wg_t);
+  hipLaunchKernelGGL(k_weight_transpose, dim3(grid), dim3(256), 0, s, a.wgs, a.wgl, hid, 0, (uint16_t*)a.wg_t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_weight_transpose, dim3(grid), dim3(256), 0, s, a.wos, a.wol, hid, 1, a.wo_t);

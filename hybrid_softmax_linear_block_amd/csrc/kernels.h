@@ -30,9 +30,9 @@ struct Bf16Args {
   bf16_t* comb_lo;        // same, residual part
   float* comb_z;          // [B*H][T][D] combined normaliser vector
   float* pre;             // [B*H][T][D*D+D] forward prefix scratch of the scan
-  bf16_t* ap;             // [B*N][2*hid] gated branch outputs (GEMM operand)
-  bf16_t* wg_t;           // [2*hid][hid]  [W_gs | W_gl] transposed
-  bf16_t* wo_t;           // [hid][2*hid]  [W_os ; W_ol] transposed
+  uint16_t* ap;           // [B*N][2*hid] gated branch outputs, fp16 (output GEMM operand)
+  bf16_t* wg_t;           // [2*hid][hid]  [W_gs | W_gl] transposed, bf16
+  uint16_t* wo_t;         // [hid][2*hid]  [W_os ; W_ol] transposed, fp16
   // fp8 softmax branch
   uint8_t *q8, *k8, *v8t, *tk8, *tv8t;  // e4m3 copies (v transposed per 64-key tile)
   float* scales;          // [5][B][H] dequantisation scales

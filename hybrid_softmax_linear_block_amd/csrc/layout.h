@@ -43,8 +43,10 @@ struct SoftRanges {
 };
 
 HYB_HD SoftRanges soft_ranges(const FrameGeom& g, int f) {
+  // built with constant indices only, so device code keeps it in registers
   SoftRanges s;
   s.n = 0;
+  s.lo[0] = s.hi[0] = s.lo[1] = s.hi[1] = s.lo[2] = s.hi[2] = 0;
   if (is_anchor(g, f)) {
     s.lo[0] = 0;
     s.hi[0] = g.T;
@@ -54,12 +56,22 @@ HYB_HD SoftRanges soft_ranges(const FrameGeom& g, int f) {
   const int i0 = interior_begin(g), i1 = interior_end(g);
   const int c = (f - i0) / g.C;
   const int clo = c - g.R < 0 ? 0 : c - g.R;
-  long long w0 = (long long)i0 + (long long)clo * g.C;
+  const long long w0 = (long long)i0 + (long long)clo * g.C;
   long long w1 = (long long)i0 + ((long long)c + g.R + 1) * g.C;
   if (w1 > i1) w1 = i1;
-  if (g.af) { s.lo[s.n] = 0; s.hi[s.n] = 1; ++s.n; }
-  s.lo[s.n] = (int)w0; s.hi[s.n] = (int)w1; ++s.n;
-  if (g.al && g.T - 1 != 0) { s.lo[s.n] = g.T - 1; s.hi[s.n] = g.T; ++s.n; }
+  if (g.af) {
+    s.lo[0] = 0; s.hi[0] = 1;
+    s.lo[1] = (int)w0; s.hi[1] = (int)w1;
+    s.n = 2;
+  } else {
+    s.lo[0] = (int)w0; s.hi[0] = (int)w1;
+    s.n = 1;
+  }
+  if (g.al) {  // f is interior, so T - 1 >= 1 is a distinct anchor
+    if (s.n == 2) { s.lo[2] = g.T - 1; s.hi[2] = g.T; }
+    else { s.lo[1] = g.T - 1; s.hi[1] = g.T; }
+    ++s.n;
+  }
   return s;
 }
 
@@ -87,6 +99,16 @@ HYB_HD int soft_frame_count(const FrameGeom& g, int f) {
   int n = 0;
   for (int i = 0; i < s.n; ++i) n += s.hi[i] - s.lo[i];
   return n;
+}
+
+// Query-frame visiting order of the softmax kernels: anchors first (they see
+// every frame, the longest work items), then the interior frames.
+HYB_HD int frame_by_cost(const FrameGeom& g, int i) {
+  const bool a0 = g.af;
+  const bool a1 = g.al && !(g.af && g.T == 1);
+  if (a0) { if (i == 0) return 0; --i; }
+  if (a1) { if (i == 0) return g.T - 1; --i; }
+  return interior_begin(g) + i;
 }
 
 }  // namespace hyb

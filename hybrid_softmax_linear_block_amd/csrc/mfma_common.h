@@ -19,6 +19,23 @@ __device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, con
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef __attribute__((ext_vector_type(8))) _Float16 halfx8;
+
+// Same lane layout as the bf16 variant.
+__device__ __forceinline__ floatx16 mfma32_f16(const halfx8& a, const halfx8& b, const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// float -> fp16 bits, round to nearest even, saturated to the finite range.
+__device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
+  f = fminf(fmaxf(f, -65504.f), 65504.f);
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return (uint32_t)f32_to_f16_sat(lo) | ((uint32_t)f32_to_f16_sat(hi) << 16);
+}
+
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 
 // Two transposing 8-byte LDS reads -> one bf16x8 MFMA operand.

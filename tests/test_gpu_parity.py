@@ -28,6 +28,42 @@ def test_small_workloads_full(wid):
     _run_and_check(WORKLOADS[wid])
 
 
+# fp8 softmax output against the e4m3-emulating oracle.  Both sides use the
+# same Q/K/V codes.  The kernel rounds P*2^8 to e4m3 against its running row
+# maximum, the emulation against the final one, so a probability can land one
+# e4m3 step (2^-3 relative) apart; with a 3-bit mantissa the rms rounding error
+# is 2^-4/sqrt(3) = 3.6% per probability, which bounds the mean relative gap
+# (measured 2.2-2.4%).  The max bound is 10x below the gap to the unquantised
+# oracle (0.18 on the fp8 workload), so it still catches a wrong code or scale.
+FP8_EMU_TOL = (2e-2, 4e-2)
+
+
+@pytest.mark.parametrize("w", [WORKLOADS[5], WORKLOADS[5].with_(name="fp8-d128-ragged", batch=1, frames=6,
+                                                                  tokens_per_frame=200, text_tokens=40,
+                                                                  heads=2, head_dim=128, seed=51)],
+                         ids=["fp8-softmax", "fp8-d128-ragged"])
+def test_fp8_softmax(w):
+    """fp8 e4m3 softmax branch: layer output and delta within 4e-2 max|ref|
+    of the unquantised oracle; the bf16 parts (linear branch, gates) within
+    the bf16 bounds; dequantisation scales bit-exact; softmax output against
+    the e4m3 emulation."""
+    from oracle import fp8
+    inp = make_inputs(w)
+    g = gu.run_gpu(w, inp)
+    ref = gu.run_oracle(w, inp)
+    rep1, bad1 = gu.compare(w, g, ref, keys=("y", "delta"))
+    rep2, bad2 = gu.compare(w, g, ref, keys=("o_l", "g"), tol=gu.TOL["bf16"])
+    lay = gu.oracle_layout(w)
+    emu = fp8.softmax_branch_fp8(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], lay)
+    e_emu = gu.errors(g["o_soft"], emu)
+    e_raw = gu.errors(g["o_soft"], ref["o_s"])
+    print(w.name, rep1, rep2, "o_s vs emulation", e_emu, "o_s vs unquantised", e_raw, flush=True)
+    assert not bad1, bad1
+    assert not bad2, bad2
+    assert np.array_equal(g["scales"].astype(np.float32), fp8.scales(inp))
+    assert e_emu[0] <= FP8_EMU_TOL[0] and e_emu[1] <= FP8_EMU_TOL[1], e_emu
+
+
 @pytest.mark.parametrize("wid", [3, 4])
 def test_768p_workloads_sampled(wid):
     w = WORKLOADS[wid]
