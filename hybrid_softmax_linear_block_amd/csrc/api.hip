@@ -145,6 +145,8 @@ hyb_status check_tensor(const char* name, const hyb_tensor& t, size_t es, bool r
     return fail(HYB_ERR_INVALID_ARGUMENT, "%s has a negative stride", name);
   if (t.stride_b % q || t.stride_tok % q || t.stride_head % q)
     return fail(HYB_ERR_INVALID_ARGUMENT, "%s strides must be multiples of %lld elements", name, (long long)q);
+  if (t.stride_tok * (int64_t)es >= (1 << 18))
+    return fail(HYB_ERR_UNSUPPORTED, "%s token stride too large (tile loads use 24-bit offsets)", name);
   return HYB_OK;
 }
 

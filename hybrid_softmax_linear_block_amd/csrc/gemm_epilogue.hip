@@ -1,4 +1,4 @@
-// Gated fusion of the two branches into the residual stream, as two bf16 MFMA
+// Gated fusion of the two branches into the residual stream, as two MFMA
 // GEMMs with fused epilogues.
 //
 // VDN-H3 article (tahou.com), section "自适应门控融合双分支输出": the two branch
@@ -37,13 +37,31 @@ struct GemmArgs {
   float* delta_dbg;
 };
 
-template <int WTM, int WFN, int EPI>
-__global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
+typedef __attribute__((address_space(3))) void lds_void_g;
+
+// WG = 4 waves in a 2 (tokens) x 2 (features) grid; each wave computes
+// WTM x WFN blocks of 32 x 32.  BK-deep k-tiles live in a 3-stage LDS ring
+// filled by wave-wide direct-to-LDS loads (1 KB per wave instruction, 16-byte
+// granules XOR-swizzled by row); loads for k-tile t + 2 are in flight while
+// k-tile t is multiplied.  Each stage is its own LDS object and the loop is
+// unrolled by three, so the compiler sees that the loads in flight never
+// alias the tile being read and does not wait for them.
+template <int WTM, int WFN, int BK, int WPE, int EPI>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(WPE, WPE)))
+void k_gemm_bf16(GemmArgs g) {
   constexpr int BM = 2 * WTM * 32, BN = 2 * WFN * 32;
-  constexpr int RA = BM / 32, RB = BN / 32;  // granules per thread per k-tile
-  using SW = Swz<64>;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * 64];
+  constexpr int G = BK / 8, RPC = 64 / G;           // granules per row, rows per 1 KB chunk
+  constexpr int CA = BM / RPC / 4, CB = BN / RPC / 4;  // chunks per wave
+  constexpr int LPT = CA + CB;                       // loads per k-tile per wave
+  static_assert(CA >= 1 && CB >= 1 && (BM / RPC) % 4 == 0 && (BN / RPC) % 4 == 0, "tile/chunk mismatch");
+  static_assert(LPT < 64, "vmcnt range");
+  using SW = Swz<BK>;
+  __shared__ __attribute__((aligned(16))) uint16_t As0[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t As1[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t As2[BM * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs0[BN * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs1[BN * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs2[BN * BK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
@@ -59,51 +77,44 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < WTM; ++j) acc[i][j] = zero16();
 
-  uint4 ra[RA], rb[RB];
-  auto load = [&](int kt) {
-    const int k0 = kt * 64;
+  // per-lane source pointers of the first k-tile; later tiles add k0 elements
+  const uint16_t* asrc[CA];
+  const uint16_t* bsrc[CB];
 #pragma unroll
-    for (int r = 0; r < RA; ++r) {
-      const int gi = tid + 256 * r, row = gi >> 3, col = (gi & 7) * 8;
-      const long long m = m0 + row;
-      ra[r] = m < g.M ? ldg16(g.A + m * g.K + k0 + col) : make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < CA; ++i) {
+    const int row = (wave * CA + i) * RPC + lane / G;
+    long long m = m0 + row;
+    if (m >= g.M) m = g.M - 1;  // rows past the end repeat the last row; never stored
+    asrc[i] = g.A + m * g.K + ((lane % G) ^ SW::key(row)) * 8;
+  }
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const int gi = tid + 256 * r, row = gi >> 3, col = (gi & 7) * 8;
-      rb[r] = ldg16(g.Bt + (long long)(n0 + row) * g.K + k0 + col);
-    }
+  for (int i = 0; i < CB; ++i) {
+    const int row = (wave * CB + i) * RPC + lane / G;
+    bsrc[i] = g.Bt + (long long)(n0 + row) * g.K + ((lane % G) ^ SW::key(row)) * 8;
+  }
+  auto issue = [&](int kt, uint16_t* adst, uint16_t* bdst) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < CA; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + k0),
+                                       (lds_void_g*)(adst + (wave * CA + i) * RPC * BK), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + k0),
+                                       (lds_void_g*)(bdst + (wave * CB + i) * RPC * BK), 16, 0, 0);
   };
-  auto stash = [&](int buf) {
+  // (separate LDS objects per stage let the compiler keep these loads in
+  // flight across the LDS reads of other stages)
+  auto mma = [&](const uint16_t* at, const uint16_t* bt_) {
 #pragma unroll
-    for (int r = 0; r < RA; ++r) {
-      const int gi = tid + 256 * r, row = gi >> 3, col = (gi & 7) * 8;
-      *(uint4*)&As[buf][SW::off(row, col)] = ra[r];
-    }
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const int gi = tid + 256 * r, row = gi >> 3, col = (gi & 7) * 8;
-      *(uint4*)&Bs[buf][SW::off(row, col)] = rb[r];
-    }
-  };
-
-  const int nk = g.K / 64;
-  load(0);
-  stash(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) load(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < BK / 16; ++ks) {
       uint4 bt[WTM];
 #pragma unroll
       for (int tb = 0; tb < WTM; ++tb)
-        bt[tb] = *(const uint4*)&As[buf][SW::off(wm * WTM * 32 + tb * 32 + l32, 16 * ks + 8 * half)];
+        bt[tb] = *(const uint4*)&at[SW::off(wm * WTM * 32 + tb * 32 + l32, 16 * ks + 8 * half)];
 #pragma unroll
       for (int fb = 0; fb < WFN; ++fb) {
-        const uint4 a = *(const uint4*)&Bs[buf][SW::off(wn * WFN * 32 + fb * 32 + l32, 16 * ks + 8 * half)];
+        const uint4 a = *(const uint4*)&bt_[SW::off(wn * WFN * 32 + fb * 32 + l32, 16 * ks + 8 * half)];
 #pragma unroll
         for (int tb = 0; tb < WTM; ++tb) {
           if constexpr (EPI == EPI_GATE)
@@ -113,8 +124,27 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
         }
       }
     }
-    if (more) stash(buf ^ 1);
-    __syncthreads();
+  };
+
+  const int nk = g.K / BK;
+  // step kt: multiply the tile in (ac, bc) while k-tile kt+2 loads into (an, bn)
+  auto step = [&](int kt, const uint16_t* ac, const uint16_t* bc, uint16_t* an, uint16_t* bn) {
+    const bool more = kt + 2 < nk;
+    if (more) issue(kt + 2, an, bn);
+    mma(ac, bc);
+    if (more) wait_vmcnt<LPT>();  // k-tile kt+1 landed; kt+2 may stay in flight
+    else wait_vmcnt<0>();
+    tile_barrier();
+  };
+  issue(0, As0, Bs0);
+  if (nk > 1) issue(1, As1, Bs1);
+  if (nk > 1) wait_vmcnt<LPT>();
+  else wait_vmcnt<0>();
+  tile_barrier();
+  for (int kt = 0; kt < nk; kt += 3) {
+    step(kt, As0, Bs0, As2, Bs2);
+    if (kt + 1 < nk) step(kt + 1, As1, Bs1, As0, Bs0);
+    if (kt + 2 < nk) step(kt + 2, As2, Bs2, As1, Bs1);
   }
 
   // ---- epilogue: lane owns token m, features n0' + 8*jg + 4*half + 0..3
@@ -202,12 +232,12 @@ hipError_t launch_weights_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) 
   return hipGetLastError();
 }
 
-template <int WTM, int WFN, int EPI>
+template <int WTM, int WFN, int BK, int WPE, int EPI>
 static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   constexpr int BM = 2 * WTM * 32, BN = 2 * WFN * 32;
-  if (g.N % BN != 0 || g.K % 64 != 0) return hipErrorInvalidValue;
+  if (g.N % BN != 0 || g.K % BK != 0) return hipErrorInvalidValue;
   const long long grid = ((g.M + BM - 1) / BM) * (g.N / BN);
-  hipLaunchKernelGGL((k_gemm_bf16<WTM, WFN, EPI>), dim3((unsigned)grid), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((k_gemm_bf16<WTM, WFN, BK, WPE, EPI>), dim3((unsigned)grid), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
@@ -232,8 +262,8 @@ hipError_t launch_gate_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s
   g.rmsw = a.rmsw;
   g.ap = a.ap;
   g.gates_dbg = a.gates_dbg;
-  if (g.N % 128 == 0) return launch_gemm<2, 2, EPI_GATE>(g, s);
-  return launch_gemm<2, 1, EPI_GATE>(g, s);
+  if (g.N % 128 == 0) return launch_gemm<4, 2, 32, 2, EPI_GATE>(g, s);
+  return launch_gemm<4, 1, 32, 2, EPI_GATE>(g, s);  // hid multiple of 64 only
 }
 
 hipError_t launch_out_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
@@ -245,8 +275,8 @@ hipError_t launch_out_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s)
   g.x = a.x;
   g.y = a.y;
   g.delta_dbg = a.delta_dbg;
-  if (g.N % 128 == 0) return launch_gemm<2, 2, EPI_OUT>(g, s);
-  return launch_gemm<2, 1, EPI_OUT>(g, s);
+  if (g.N % 128 == 0) return launch_gemm<4, 2, 32, 2, EPI_OUT>(g, s);
+  return launch_gemm<4, 1, 32, 2, EPI_OUT>(g, s);
 }
 
 }  // namespace hyb

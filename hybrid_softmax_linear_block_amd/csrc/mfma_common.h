@@ -54,10 +54,11 @@ __device__ __forceinline__ bf16x8 tr_pair(const bf16_t* p0, const bf16_t* p1) {
 template <int COLS>
 struct Swz {
   static constexpr int G = COLS / 8;
-  static_assert(G == 8 || G == 16, "tile width must be 64 or 128 bf16");
+  static_assert(G == 4 || G == 8 || G == 16, "tile width must be 32, 64 or 128 16-bit elements");
   __device__ static __forceinline__ int key(int row) {
     if constexpr (G == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
-    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    else if constexpr (G == 8) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    else return (row >> 2) & 3;
   }
   // element offset of (row, col); col may be any value, its granule is swizzled
   __device__ static __forceinline__ int off(int row, int col) {
@@ -73,6 +74,36 @@ __device__ __forceinline__ floatx16 zero16() {
 }
 
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *(const uint4*)p; }
+
+// s_waitcnt with only vmcnt = N (expcnt / lgkmcnt left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Direct-to-LDS 16-byte-per-lane load (global_load_lds_dwordx4): lane l's
+// 16 bytes from gbase + voff land at LDS byte lds + 16 * l; gbase and lds
+// are wave-uniform.  Issued from inline asm so that the compiler does not
+// order it against unrelated LDS reads (it cannot tell which LDS buffer the
+// load targets and would otherwise wait for it before every LDS read).  The
+// instruction has no register results; completion is tracked by vmcnt, which
+// callers wait on explicitly (wait_vmcnt) before the tile_barrier that
+// publishes the tile.
+__device__ __forceinline__ void dma16(const void* gbase, unsigned voff, const void* lds) {
+  const unsigned loff =
+      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)((__attribute__((address_space(3))) const char*)lds));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(loff) : "m0");
+}
+
+// Workgroup barrier for LDS tiles filled by dma16: waits for this wave's LDS
+// reads (lgkmcnt) and synchronises, without the full fence of __syncthreads
+// (which would also drain every prefetch still in flight).  The caller waits
+// (wait_vmcnt) for its own loads of the tile the next step reads.
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
 
 // XCD-aware remap: hardware dispatches workgroup i to XCD i % 8.  Return the
 // logical index so that each XCD runs a contiguous range of logical work.
