@@ -22,6 +22,8 @@ sys.path.insert(0, ROOT)
 from hybrid_softmax_linear_block_amd import api  # noqa: E402
 from hybrid_softmax_linear_block_amd.inputs import WORKLOADS, make_inputs, sample_tokens  # noqa: E402
 
+WORKLOADS_ID = {w.name: i for i, w in WORKLOADS.items()}
+
 METRIC = "hybrid-attn layer Mtokens/s + softmax-branch TFLOP/s (768p-shaped, bf16)"
 PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense MFMA TFLOP/s, MI355X published
 HBM_PEAK_GBS = 8000.0
@@ -73,6 +75,51 @@ def traffic_for(kernel_key, workload):
     return rec.get("bytes_per_launch")
 
 
+def _counter_sum(csv_path, kernel_substr, counter):
+    import csv
+    tot, disp = 0.0, set()
+    for r in csv.DictReader(open(csv_path)):
+        if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            tot += float(r["Counter_Value"])
+            disp.add(r["Dispatch_Id"])
+    return tot, len(disp)
+
+
+def write_traffic(pmc_dir, w):
+    """HBM bytes per launch of the softmax kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reports for the
+    plain 1 GiB copy of --calibrate-copy (runtime copy kernel)."""
+    import glob
+
+    def find(sub):
+        return glob.glob(os.path.join(pmc_dir, sub, "*counter_collection.csv"))[0]
+    fetch, nf = _counter_sum(find("fetch"), "k_attn_bf16", "FETCH_SIZE")
+    write, nw = _counter_sum(find("write"), "k_attn_bf16", "WRITE_SIZE")
+    cf, ncf = _counter_sum(find("cfetch"), "copyBuffer", "FETCH_SIZE")
+    cw, ncw = _counter_sum(find("cwrite"), "copyBuffer", "WRITE_SIZE")
+    copy_kib = (1 << 30) / 1024.0
+    f_scale = copy_kib * ncf / cf if cf else None
+    w_scale = copy_kib * ncw / cw if cw else None
+    rd = fetch / nf * 1024 * f_scale
+    wr = write / nw * 1024 * w_scale
+    src = os.path.join(ROOT, "hybrid_softmax_linear_block_amd", "csrc", KERNEL_SOURCES["softmax"])
+    rec = {"kernel": "k_attn_bf16", "workload": w.name, "bytes_per_launch": rd + wr,
+           "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+           "commands": ["rocprofv3 --pmc FETCH_SIZE --kernel-include-regex k_attn_bf16 --output-format csv "
+                        "-d PMC_DIR/fetch -o fetch -- python3 bench.py --workload %d --steps 1 --warmup 0 "
+                        "--no-cpu-baseline" % WORKLOADS_ID[w.name],
+                        "(same with WRITE_SIZE -> PMC_DIR/write)",
+                        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d PMC_DIR/cfetch -o cfetch -- "
+                        "python3 bench.py --calibrate-copy",
+                        "(same with WRITE_SIZE -> PMC_DIR/cwrite)",
+                        "python3 bench.py --workload %d --write-traffic PMC_DIR" % WORKLOADS_ID[w.name]]}
+    out = os.path.join(ROOT, "profiles", "traffic_softmax_%s.json" % w.name)
+    json.dump(rec, open(out, "w"), indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(w, inp, budget_s=20.0):
     """Time the fp64 oracle on the host on a bounded token sample and scale
     to Mtokens/s: full-state build (all tokens) + per-token work measured on
@@ -120,7 +167,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--write-traffic", metavar="PMC_DIR",
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE passes under PMC_DIR (subdirectories fetch, "
+                         "write, cfetch, cwrite) into profiles/traffic_<kernel>_<workload>.json and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args.write_traffic, WORKLOADS[args.workload])
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the layer shards by heads; "
               "see the design notes). Run with --gpus 1.", file=sys.stderr)
