@@ -27,53 +27,6 @@
 
 namespace hyb {
 
-// Key sequence of one query frame: up to three contiguous video frame ranges
-// of S(f) and the text, as 64-key tiles.  Kept in scalars (wave-uniform).
-struct KeySeq {
-  int st0, ln0, nt0, st1, ln1, nt1, st2, ln2, nt2, ntt, total;
-};
-
-template <int BN>
-__device__ __forceinline__ KeySeq key_sequence(const Dims& d, int f) {
-  const SoftRanges sr = soft_ranges(d.g, f);
-  KeySeq ks;
-  ks.st0 = sr.lo[0] * d.n;
-  ks.ln0 = (sr.hi[0] - sr.lo[0]) * d.n;
-  ks.st1 = sr.n > 1 ? sr.lo[1] * d.n : 0;
-  ks.ln1 = sr.n > 1 ? (sr.hi[1] - sr.lo[1]) * d.n : 0;
-  ks.st2 = sr.n > 2 ? sr.lo[2] * d.n : 0;
-  ks.ln2 = sr.n > 2 ? (sr.hi[2] - sr.lo[2]) * d.n : 0;
-  ks.nt0 = (ks.ln0 + BN - 1) / BN;
-  ks.nt1 = (ks.ln1 + BN - 1) / BN;
-  ks.nt2 = (ks.ln2 + BN - 1) / BN;
-  ks.ntt = (d.L + BN - 1) / BN;
-  ks.total = ks.nt0 + ks.nt1 + ks.nt2 + ks.ntt;
-  return ks;
-}
-
-// tile t (BN keys) -> first key, number of valid keys, text or video
-template <int BN>
-__device__ __forceinline__ void locate(const KeySeq& ks, int L, int t, int& key0, int& valid, bool& text) {
-  text = false;
-  if (t < ks.nt0) { key0 = ks.st0 + t * BN; valid = min(BN, ks.ln0 - t * BN); return; }
-  t -= ks.nt0;
-  if (t < ks.nt1) { key0 = ks.st1 + t * BN; valid = min(BN, ks.ln1 - t * BN); return; }
-  t -= ks.nt1;
-  if (t < ks.nt2) { key0 = ks.st2 + t * BN; valid = min(BN, ks.ln2 - t * BN); return; }
-  t -= ks.nt2;
-  text = true;
-  key0 = t * BN;
-  valid = min(BN, L - t * BN);
-}
-
-template <int BN>
-__device__ __forceinline__ int tile_valid(const KeySeq& ks, int L, int t) {
-  int key0, valid;
-  bool text;
-  locate<BN>(ks, L, t, key0, valid, text);
-  return valid;
-}
-
 // Work item of workgroup blockIdx.x.  A group = all query tiles of one
 // (frame, b, h).  Groups are ordered longest first (anchor frames) and dealt
 // to the 8 XCDs round-robin; within an XCD a group's tiles run back to back.
@@ -107,52 +60,125 @@ __device__ __forceinline__ Item decode_item(const Dims& d, int qtiles) {
 // exact enough in bf16 and fp32, and the O rescale is skipped on most tiles.
 constexpr float kRescaleSlack = 8.f;
 
-// Tile loader: a tile is KB blocks of 32 keys.
+// Walk over the keys of one work item in tiles of BN keys: up to three video
+// frame ranges of S(f) (one tensor, one stride), then the text tokens (own
+// tensor and stride).  Everything here is wave-uniform and lives in SGPRs;
+// the common step is one pointer bump per tensor, segment changes (at most
+// four per item) take the slow branch.
+template <int BN>
+struct KeyWalk {
+  const char *kvid, *vvid, *ktxt, *vtxt;  // (b, h) bases of the key/value tensors
+  unsigned kstv, vstv, kstt, vstt;         // byte strides per token
+  int st[3], ln[3], L;                     // video ranges of S(f) in keys (constant indices only)
+  const char *kp, *vp;                     // first key of the current tile
+  unsigned ks, vs;                         // strides of the current segment
+  int rem, seg;                            // keys left from kp in the segment; 0..2 video, 3 text, 4 done
+
+  __device__ __forceinline__ void init(const Dims& d, int f, int b, int h, const Tensor4& k, const Tensor4& v,
+                                       const Tensor4& tk, const Tensor4& tv) {
+    const SoftRanges sr = soft_ranges(d.g, f);
+    kvid = (const char*)((const bf16_t*)k.p + (long long)b * k.sb + (long long)h * k.sh);
+    vvid = (const char*)((const bf16_t*)v.p + (long long)b * v.sb + (long long)h * v.sh);
+    ktxt = (const char*)((const bf16_t*)tk.p + (long long)b * tk.sb + (long long)h * tk.sh);
+    vtxt = (const char*)((const bf16_t*)tv.p + (long long)b * tv.sb + (long long)h * tv.sh);
+    kstv = (unsigned)(k.st * 2);  // byte strides (< 2^18, host-checked)
+    vstv = (unsigned)(v.st * 2);
+    kstt = (unsigned)(tk.st * 2);
+    vstt = (unsigned)(tv.st * 2);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      st[i] = sr.n > i ? sr.lo[i] * d.n : 0;
+      ln[i] = sr.n > i ? (sr.hi[i] - sr.lo[i]) * d.n : 0;
+    }
+    L = d.L;
+    open_from(0);
+  }
+
+  // position at the first key of the first non-empty segment >= s0
+  __device__ __forceinline__ void open_from(int s0) {
+    seg = 4;
+    rem = 0;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      if (seg == 4 && i >= s0 && ln[i] > 0) {
+        seg = i;
+        kp = kvid + (unsigned long long)(unsigned)st[i] * kstv;
+        vp = vvid + (unsigned long long)(unsigned)st[i] * vstv;
+        ks = kstv;
+        vs = vstv;
+        rem = ln[i];
+      }
+    }
+    if (seg == 4 && s0 <= 3 && L > 0) {
+      seg = 3;
+      kp = ktxt;
+      vp = vtxt;
+      ks = kstt;
+      vs = vstt;
+      rem = L;
+    }
+  }
+
+  __device__ __forceinline__ bool done() const { return seg == 4; }
+  __device__ __forceinline__ int valid() const { return min(BN, rem); }
+  __device__ __forceinline__ void advance() {
+    rem -= BN;
+    if (rem > 0) {
+      kp += BN * ks;
+      vp += BN * vs;
+    } else {
+      open_from(seg + 1);
+    }
+  }
+};
+
+// Tile loader: a tile is KB blocks of 32 keys; each of the NW waves fills
+// CPW chunks of RPC rows (1 KB, one wave-wide direct-to-LDS load per chunk).
 template <int D, int NW, int KB>
-struct TileCtx {
+struct TileLoader {
   static constexpr int G = D / 8;           // 16-byte granules per row
-  static constexpr int BN = 32 * KB;       // keys per tile
-  static constexpr int RPC = 64 / G;        // rows per 1 KB chunk (one wave-wide LDS-DMA load)
+  static constexpr int BN = 32 * KB;        // keys per tile
+  static constexpr int RPC = 64 / G;        // rows per chunk
   static constexpr int CHUNKS = BN / RPC;   // chunks per tile
   static constexpr int CPW = CHUNKS / NW;   // chunks per wave
   static constexpr int TILE = BN * D;       // elements per tile
   static_assert(CHUNKS % NW == 0, "tile chunks must split evenly over waves");
 
   unsigned lrow[CPW], lcol[CPW];  // per chunk: row in tile, byte offset of the logical granule
-  unsigned kst2, vst2, tkst2, tvst2;
 
-  __device__ __forceinline__ void init(int wave, int lane, const Tensor4& k, const Tensor4& v, const Tensor4& tk,
-                                       const Tensor4& tv) {
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       lrow[i] = (unsigned)((wave * CPW + i) * RPC + lane / G);
       lcol[i] = (unsigned)(((lane % G) ^ Swz<D>::key((int)lrow[i])) * 16);
     }
-    kst2 = (unsigned)(k.st * 2);  // byte strides (< 2^18, host-checked)
-    vst2 = (unsigned)(v.st * 2);
-    tkst2 = (unsigned)(tk.st * 2);
-    tvst2 = (unsigned)(tv.st * 2);
   }
 
-  // Wave-wide direct-to-LDS loads of this wave's chunks of tile t.  Lane l of
-  // a chunk fills row (l / G), physical granule (l % G), which holds logical
-  // granule (l % G) ^ swizzle(row).  Rows past the tile's valid keys repeat the
-  // last valid row (their scores are masked to -inf).
-  __device__ __forceinline__ void load(const KeySeq& ks, const Dims& d, int b, int h, int wave, const Tensor4& x,
-                                       const Tensor4& tx, unsigned st_x, unsigned st_t, bf16_t* dst, int t) const {
-    int key0, valid;
-    bool text;
-    locate<BN>(ks, d.L, t, key0, valid, text);
-    const Tensor4& src = text ? tx : x;
-    const char* base = (const char*)((const bf16_t*)src.p + tok_off(src, b, key0, h));
-    const unsigned st2 = text ? st_t : st_x;
+  // Lane l of a chunk fills row (l / G), physical granule (l % G), which holds
+  // logical granule (l % G) ^ swizzle(row).  Rows past the tile's valid keys
+  // repeat the last valid row (their scores are masked to -inf).
+  // dst: LDS byte address of the tile
+  __device__ __forceinline__ void load(const char* base, unsigned st2, int valid, int wave, unsigned dst) const {
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
-      const unsigned rs = valid == BN ? lrow[i] : min(lrow[i], (unsigned)(valid - 1));
-      dma16(base, __umul24(rs, st2) + lcol[i], dst + (wave * CPW + i) * RPC * D);
+      const unsigned rs = min(lrow[i], (unsigned)(valid - 1));
+      dma16(base, __umul24(rs, st2) + lcol[i], dst + (wave * CPW + i) * RPC * D * 2);
     }
   }
 };
+
+// Combine a per-lane value with that of lane l ^ 32 (the other half of the
+// query row's keys) with one cross-half lane swap.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 // Softmax of one 32 x (32 KB) score block held as S^T in KB 32x32
 // accumulators: masks keys >= valid, updates the lazily rescaled running max
@@ -162,12 +188,24 @@ template <int KB, int DB>
 __device__ __forceinline__ void softmax_tile(floatx16 (&s)[KB], int valid, int half, float sl2, float& m_run,
                                              float& l_run, floatx16 (&oacc)[DB], bf16x8 (&pf)[2 * KB]) {
   if (valid < 32 * KB) {
+    // key = c + 4 * half with c a compile-time constant per element; the key is
+    // masked when 4 * half - (valid - c) >= 0.  Sign-extend that difference
+    // into a bit mask and bit-select -inf, all in VGPRs (no per-element compare
+    // masks held in scalar registers).
+    const int kbase = 4 * half;
+    const unsigned ninf = 0xff800000u;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int key = kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-        if (key >= valid) s[kb][j] = -INFINITY;
+        const int lim = valid - (kb * 32 + 8 * (j >> 2) + (j & 3));
+        unsigned bits = __float_as_uint(s[kb][j]), m;
+        asm("v_sub_u32 %0, %2, %3\n\t"
+            "v_ashrrev_i32 %0, 31, %0\n\t"
+            "v_bfi_b32 %1, %0, %1, %4"
+            : "=&v"(m), "+v"(bits)
+            : "v"(kbase), "s"(lim), "s"(ninf));
+        s[kb][j] = __uint_as_float(bits);
       }
   }
   float mk[KB];
@@ -181,7 +219,7 @@ __device__ __forceinline__ void softmax_tile(floatx16 (&s)[KB], int valid, int h
   float mx = mk[0];
 #pragma unroll
   for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, mk[kb]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+  mx = xor32_max(mx) * sl2;
   const bool grow = mx > m_run + kRescaleSlack;
   if (__any(grow)) {
     const float m_new = grow ? mx : m_run;
@@ -193,6 +231,9 @@ __device__ __forceinline__ void softmax_tile(floatx16 (&s)[KB], int valid, int h
 #pragma unroll
       for (int j = 0; j < 16; ++j) oacc[i][j] *= alpha;
   }
+  // Row sum of the bf16-rounded probabilities (the weights the P V product
+  // uses), two at a time with a bf16 dot product against (1, 1).
+  const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
   float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
@@ -200,15 +241,13 @@ __device__ __forceinline__ void softmax_tile(floatx16 (&s)[KB], int valid, int h
     for (int hb = 0; hb < 2; ++hb) {
       bf16x8 p;
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hb + e], sl2, -m_run));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hb + e + 1], sl2, -m_run));
-        ls0 += p0;
-        ls1 += p1;
-        p[e] = static_cast<__bf16>(p0);
-        p[e + 1] = static_cast<__bf16>(p1);
-      }
+      for (int e = 0; e < 8; ++e) p[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kb][8 * hb + e], sl2, -m_run)));
       pf[2 * kb + hb] = p;
+      const uint4 pw = __builtin_bit_cast(uint4, p);
+      ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.x), ones, ls0, false);
+      ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.y), ones, ls1, false);
+      ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.z), ones, ls0, false);
+      ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.w), ones, ls1, false);
     }
   l_run += ls0 + ls1;
 }
@@ -217,7 +256,7 @@ __device__ __forceinline__ void softmax_tile(floatx16 (&s)[KB], int valid, int h
 template <int D>
 __device__ __forceinline__ void store_rows(const floatx16 (&oacc)[D / 32], float l_run, bool row_ok, float* op,
                                            int half) {
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xor32_sum(l_run);
   const float inv = 1.f / l_tot;
   if (!row_ok) return;
 #pragma unroll
@@ -232,26 +271,34 @@ __device__ __forceinline__ void store_rows(const floatx16 (&oacc)[D / 32], float
 
 // ---------------------------------------------------------------------------
 // 4 waves, 128 query rows per workgroup; WPE workgroups' waves per SIMD.
-template <int D, int KB, int WPE>
+// PRIO: raise the wave's issue priority while it issues the S = K Q^T MFMAs,
+// so that the matrix pipe is fed first and the other wave's softmax fills in.
+template <int D, int KB, int WPE, bool PRIO>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(WPE, WPE)))
 void k_attn_bf16(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv, float sl2,
                  float* __restrict__ os) {
   constexpr int NW = 4, BM = 32 * NW, KS = D / 16, DB = D / 32, BN = 32 * KB;
-  using Ctx = TileCtx<D, NW, KB>;
+  using Ldr = TileLoader<D, NW, KB>;
   using SW = Swz<D>;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][Ctx::TILE];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][Ctx::TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][Ldr::TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][Ldr::TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5, j16 = lane & 15, lgrp = lane >> 4;
   const Item it = decode_item(d, (d.n + BM - 1) / BM);
-  const KeySeq ks = key_sequence<BN>(d, it.f);
 
-  Ctx ctx;
-  ctx.init(wave, lane, k, v, tk, tv);
-  ctx.load(ks, d, it.b, it.h, wave, k, tk, ctx.kst2, ctx.tkst2, Ks[0], 0);
-  ctx.load(ks, d, it.b, it.h, wave, v, tv, ctx.vst2, ctx.tvst2, Vs[0], 0);
+  // S(f) always holds the query's own frame, so the walk has >= 1 tile.
+  KeyWalk<BN> kw;
+  kw.init(d, it.f, it.b, it.h, k, v, tk, tv);
+  Ldr ldr;
+  ldr.init(wave, lane);
+  const unsigned ks_lds = lds_addr(Ks), vs_lds = lds_addr(Vs);
+  constexpr unsigned kTileBytes = Ldr::TILE * 2;
+  int valid = kw.valid();
+  ldr.load(kw.kp, kw.ks, valid, wave, ks_lds);
+  ldr.load(kw.vp, kw.vs, valid, wave, vs_lds);
+  kw.advance();
 
   const int prow = it.qt * BM + wave * 32 + l32;
   const bool row_ok = prow < d.n;
@@ -272,14 +319,17 @@ void k_attn_bf16(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv
   wait_vmcnt<0>();
   tile_barrier();
 
-  for (int t = 0; t < ks.total; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ks.total) {
-      ctx.load(ks, d, it.b, it.h, wave, k, tk, ctx.kst2, ctx.tkst2, Ks[buf ^ 1], t + 1);
-      ctx.load(ks, d, it.b, it.h, wave, v, tv, ctx.vst2, ctx.tvst2, Vs[buf ^ 1], t + 1);
+  for (int buf = 0;; buf ^= 1) {
+    const bool more = !kw.done();
+    const int valid_next = kw.valid();
+    if (more) {
+      ldr.load(kw.kp, kw.ks, valid_next, wave, ks_lds + (buf ^ 1) * kTileBytes);
+      ldr.load(kw.vp, kw.vs, valid_next, wave, vs_lds + (buf ^ 1) * kTileBytes);
+      kw.advance();
     }
     // ---- S^T = K Q^T: KB blocks of 32 keys
     floatx16 s[KB];
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       s[kb] = zero16();
@@ -290,8 +340,9 @@ void k_attn_bf16(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv
         s[kb] = mfma32(a, qf[st], s[kb]);
       }
     }
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     bf16x8 pf[2 * KB];
-    softmax_tile<KB, DB>(s, tile_valid<BN>(ks, d.L, t), half, sl2, m_run, l_run, oacc, pf);
+    softmax_tile<KB, DB>(s, valid, half, sl2, m_run, l_run, oacc, pf);
     // ---- O^T += V^T P^T; V^T operand via transposing LDS reads
 #pragma unroll
     for (int kk = 0; kk < 2 * KB; ++kk) {
@@ -303,23 +354,25 @@ void k_attn_bf16(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv
         oacc[i] = mfma32(a, pf[kk], oacc[i]);
       }
     }
-    wait_vmcnt<0>();  // this wave's loads of tile t+1 landed
+    if (!more) break;
+    wait_vmcnt<0>();  // this wave's loads of the next tile landed
     tile_barrier();
+    valid = valid_next;
   }
   store_rows<D>(oacc, l_run, row_ok, os + (((long long)it.b * d.N + qtok) * d.H + it.h) * D, half);
 }
 
-template <int D, int KB, int WPE>
+template <int D, int KB, int WPE, bool PRIO>
 static hipError_t launch_attn(const Dims& d, const Bf16Args& a, hipStream_t s) {
   const long long grid = (long long)((d.n + 127) / 128) * d.H * d.B * d.T;
-  hipLaunchKernelGGL((k_attn_bf16<D, KB, WPE>), dim3((unsigned)grid), dim3(256), 0, s, d, a.q, a.k, a.v, a.tk,
+  hipLaunchKernelGGL((k_attn_bf16<D, KB, WPE, PRIO>), dim3((unsigned)grid), dim3(256), 0, s, d, a.q, a.k, a.v, a.tk,
                      a.tv, a.scale_log2, a.os);
   return hipGetLastError();
 }
 
 hipError_t launch_softmax_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
-  if (d.D == 128) return launch_attn<128, 2, 2>(d, a, s);
-  if (d.D == 64) return launch_attn<64, 2, 2>(d, a, s);
+  if (d.D == 128) return launch_attn<128, 2, 2, false>(d, a, s);
+  if (d.D == 64) return launch_attn<64, 2, 2, false>(d, a, s);
   return hipErrorInvalidValue;
 }
 

@@ -82,18 +82,24 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// LDS byte address of a __shared__ object (the generic-to-LDS cast done once,
+// outside any loop).
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
+}
+
 // Direct-to-LDS 16-byte-per-lane load (global_load_lds_dwordx4): lane l's
-// 16 bytes from gbase + voff land at LDS byte lds + 16 * l; gbase and lds
-// are wave-uniform.  Issued from inline asm so that the compiler does not
+// 16 bytes from gbase + voff land at LDS byte address lds + 16 * l; gbase and
+// lds are wave-uniform.  Issued from inline asm so that the compiler does not
 // order it against unrelated LDS reads (it cannot tell which LDS buffer the
 // load targets and would otherwise wait for it before every LDS read).  The
 // instruction has no register results; completion is tracked by vmcnt, which
 // callers wait on explicitly (wait_vmcnt) before the tile_barrier that
 // publishes the tile.
-__device__ __forceinline__ void dma16(const void* gbase, unsigned voff, const void* lds) {
-  const unsigned loff =
-      __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)((__attribute__((address_space(3))) const char*)lds));
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(loff) : "m0");
+__device__ __forceinline__ void dma16(const void* gbase, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "m0");
 }
 
 // Workgroup barrier for LDS tiles filled by dma16: waits for this wave's LDS
