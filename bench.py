@@ -103,7 +103,7 @@ def write_traffic(pmc_dir, w):
     rd = fetch / nf * 1024 * f_scale
     wr = write / nw * 1024 * w_scale
     src = os.path.join(ROOT, "hybrid_softmax_linear_block_amd", "csrc", KERNEL_SOURCES["softmax"])
-    rec = {"kernel": "k_attn_bf16", "workload": w.name, "bytes_per_launch": rd + wr,
+    rec = {"kernel": "k_attn_bf16_sp", "workload": w.name, "bytes_per_launch": rd + wr,
            "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
            "fetch_scale": f_scale, "write_scale": w_scale,
            "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
@@ -244,7 +244,7 @@ def main():
         "softmax_tflops": round(soft_tflops, 2),
         "layer_tflops": round(wc["layer_flop"] / (ms * 1e-3) / 1e12, 2),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "roofline": {"kernel": "k_attn_bf16 (softmax branch)" if not soft else "softmax branch fp8",
+        "roofline": {"kernel": "k_attn_bf16_sp (softmax branch)" if not soft else "softmax branch fp8",
                      "bound": "mfma", "achieved": round(soft_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(soft_tflops / peak, 4), "traffic": traffic_for(soft_key, w.name),
                      "flop_per_launch": wc["softmax_flop"]},

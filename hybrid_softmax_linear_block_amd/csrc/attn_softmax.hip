@@ -21,8 +21,12 @@
 // K/V tiles (KB blocks of 32 keys) are double-buffered in LDS and filled by
 // wave-wide direct-to-LDS loads; the 16-byte granules of each row are
 // XOR-swizzled by row so that both read patterns are bank-conflict free.
-// 4 waves (128 query rows) per workgroup and several workgroups per CU: the
-// hardware overlaps one workgroup's matrix phase with another's softmax.
+// 4 waves (128 query rows) per workgroup, two workgroups per CU.  The loop is
+// software-pipelined (S of the next tile is computed while the current
+// tile's probabilities are formed) so that each wave's instruction stream
+// mixes matrix and vector work evenly.
+#include <type_traits>
+
 #include "kernels_bf16.h"
 
 namespace hyb {
@@ -121,14 +125,16 @@ struct KeyWalk {
 
   __device__ __forceinline__ bool done() const { return seg == 4; }
   __device__ __forceinline__ int valid() const { return min(BN, rem); }
-  __device__ __forceinline__ void advance() {
+  // step to the next tile; true when that opened a new segment (or ended)
+  __device__ __forceinline__ bool advance() {
     rem -= BN;
     if (rem > 0) {
       kp += BN * ks;
       vp += BN * vs;
-    } else {
-      open_from(seg + 1);
+      return false;
     }
+    open_from(seg + 1);
+    return true;
   }
 };
 
@@ -145,6 +151,8 @@ struct TileLoader {
   static_assert(CHUNKS % NW == 0, "tile chunks must split evenly over waves");
 
   unsigned lrow[CPW], lcol[CPW];  // per chunk: row in tile, byte offset of the logical granule
+  unsigned koff[CPW], voff[CPW];  // per chunk: lane byte offset of a full tile at the current strides
+  unsigned kst, vst;              // current byte strides
 
   __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
@@ -153,17 +161,39 @@ struct TileLoader {
       lcol[i] = (unsigned)(((lane % G) ^ Swz<D>::key((int)lrow[i])) * 16);
     }
   }
+  __device__ __forceinline__ void set_k(unsigned st2) {
+    kst = st2;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) koff[i] = __umul24(lrow[i], st2) + lcol[i];
+  }
+  __device__ __forceinline__ void set_v(unsigned st2) {
+    vst = st2;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) voff[i] = __umul24(lrow[i], st2) + lcol[i];
+  }
 
   // Lane l of a chunk fills row (l / G), physical granule (l % G), which holds
   // logical granule (l % G) ^ swizzle(row).  Rows past the tile's valid keys
   // repeat the last valid row (their scores are masked to -inf).
   // dst: LDS byte address of the tile
-  __device__ __forceinline__ void load(const char* base, unsigned st2, int valid, int wave, unsigned dst) const {
+  __device__ __forceinline__ void load(const char* base, const unsigned (&off)[CPW], unsigned st2, int valid,
+                                       int wave, unsigned dst) const {
+    if (valid == BN) {
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const unsigned rs = min(lrow[i], (unsigned)(valid - 1));
-      dma16(base, __umul24(rs, st2) + lcol[i], dst + (wave * CPW + i) * RPC * D * 2);
+      for (int i = 0; i < CPW; ++i) dma16(base, off[i], dst + (wave * CPW + i) * RPC * D * 2);
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        const unsigned rs = min(lrow[i], (unsigned)(valid - 1));
+        dma16(base, __umul24(rs, st2) + lcol[i], dst + (wave * CPW + i) * RPC * D * 2);
+      }
     }
+  }
+  __device__ __forceinline__ void load_k(const char* base, int valid, int wave, unsigned dst) const {
+    load(base, koff, kst, valid, wave, dst);
+  }
+  __device__ __forceinline__ void load_v(const char* base, int valid, int wave, unsigned dst) const {
+    load(base, voff, vst, valid, wave, dst);
   }
 };
 
@@ -181,33 +211,36 @@ __device__ __forceinline__ float xor32_sum(float x) {
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 // Softmax of one 32 x (32 KB) score block held as S^T in KB 32x32
-// accumulators: masks keys >= valid, updates the lazily rescaled running max
-// and the lane's partial row sum, rescales O when the max moved, and emits P as
-// the 2 KB bf16 B-operand fragments of the P V product.
-template <int KB, int DB>
-__device__ __forceinline__ void softmax_tile(floatx16 (&s)[KB], int valid, int half, float sl2, float& m_run,
-                                             float& l_run, floatx16 (&oacc)[DB], bf16x8 (&pf)[2 * KB]) {
-  if (valid < 32 * KB) {
-    // key = c + 4 * half with c a compile-time constant per element; the key is
-    // masked when 4 * half - (valid - c) >= 0.  Sign-extend that difference
-    // into a bit mask and bit-select -inf, all in VGPRs (no per-element compare
-    // masks held in scalar registers).
-    const int kbase = 4 * half;
-    const unsigned ninf = 0xff800000u;
+// accumulators, in four steps: mask keys >= valid, row maximum, lazy rescale
+// of the running state, and the probabilities P as the 2 KB bf16 B-operand
+// fragments of the P V product (plus their row sum).
+
+// Keys >= valid -> -inf.  key = c + 4 * half with c a compile-time constant
+// per element; the key is masked when 4 * half - (valid - c) >= 0.  The sign
+// of that difference becomes a bit mask that selects -inf, all in VGPRs (no
+// per-element compare masks held in scalar registers).
+template <int KB>
+__device__ __forceinline__ void mask_tile(floatx16 (&s)[KB], int valid, int half) {
+  const int kbase = 4 * half;
+  const unsigned ninf = 0xff800000u;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int lim = valid - (kb * 32 + 8 * (j >> 2) + (j & 3));
-        unsigned bits = __float_as_uint(s[kb][j]), m;
-        asm("v_sub_u32 %0, %2, %3\n\t"
-            "v_ashrrev_i32 %0, 31, %0\n\t"
-            "v_bfi_b32 %1, %0, %1, %4"
-            : "=&v"(m), "+v"(bits)
-            : "v"(kbase), "s"(lim), "s"(ninf));
-        s[kb][j] = __uint_as_float(bits);
-      }
-  }
+    for (int j = 0; j < 16; ++j) {
+      const int lim = valid - (kb * 32 + 8 * (j >> 2) + (j & 3));
+      unsigned bits = __float_as_uint(s[kb][j]), m;
+      asm("v_sub_u32 %0, %2, %3\n\t"
+          "v_ashrrev_i32 %0, 31, %0\n\t"
+          "v_bfi_b32 %1, %0, %1, %4"
+          : "=&v"(m), "+v"(bits)
+          : "v"(kbase), "s"(lim), "s"(ninf));
+      s[kb][j] = __uint_as_float(bits);
+    }
+}
+
+// Row maximum in log2 units (scaled by sl2), combined over both lane halves.
+template <int KB>
+__device__ __forceinline__ float tile_max(const floatx16 (&s)[KB], float sl2) {
   float mk[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
@@ -219,7 +252,13 @@ __device__ __forceinline__ void softmax_tile(floatx16 (&s)[KB], int valid, int h
   float mx = mk[0];
 #pragma unroll
   for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, mk[kb]);
-  mx = xor32_max(mx) * sl2;
+  return xor32_max(mx) * sl2;
+}
+
+// Lazy rescale: move the running maximum only when the tile maximum exceeds it
+// by more than the slack, and then scale O and the row sum.
+template <int DB>
+__device__ __forceinline__ void rescale(float mx, float& m_run, float& l_run, floatx16 (&oacc)[DB]) {
   const bool grow = mx > m_run + kRescaleSlack;
   if (__any(grow)) {
     const float m_new = grow ? mx : m_run;
@@ -231,8 +270,14 @@ __device__ __forceinline__ void softmax_tile(floatx16 (&s)[KB], int valid, int h
 #pragma unroll
       for (int j = 0; j < 16; ++j) oacc[i][j] *= alpha;
   }
-  // Row sum of the bf16-rounded probabilities (the weights the P V product
-  // uses), two at a time with a bf16 dot product against (1, 1).
+}
+
+// P = exp2(S sl2 - m) in bf16; the row sum accumulates the bf16-rounded
+// probabilities (the weights the P V product uses), two at a time with a bf16
+// dot product against (1, 1).
+template <int KB>
+__device__ __forceinline__ void exp_tile(const floatx16 (&s)[KB], float sl2, float m_run, float& l_run,
+                                         bf16x8 (&pf)[2 * KB]) {
   const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
   float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
@@ -241,7 +286,8 @@ __device__ __forceinline__ void softmax_tile(floatx16 (&s)[KB], int valid, int h
     for (int hb = 0; hb < 2; ++hb) {
       bf16x8 p;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kb][8 * hb + e], sl2, -m_run)));
+      for (int e = 0; e < 8; ++e)
+        p[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kb][8 * hb + e], sl2, -m_run)));
       pf[2 * kb + hb] = p;
       const uint4 pw = __builtin_bit_cast(uint4, p);
       ls0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.x), ones, ls0, false);
@@ -250,6 +296,41 @@ __device__ __forceinline__ void softmax_tile(floatx16 (&s)[KB], int valid, int h
       ls1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw.w), ones, ls1, false);
     }
   l_run += ls0 + ls1;
+}
+
+// S^T = K Q^T for one tile: KB blocks of 32 keys; K rows from the swizzled
+// LDS tile, Q^T fragments from registers.
+template <int D, int KB>
+__device__ __forceinline__ void qk_tile(floatx16 (&s)[KB], const bf16_t* kt, const bf16x8 (&qf)[D / 16], int l32,
+                                        int half) {
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) s[kb] = zero16();
+  // step-major: the KB accumulation chains alternate, so each MFMA's K operand
+  // read has the previous step's MFMAs to hide behind
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const bf16x8 a = *(const bf16x8*)&kt[Swz<D>::off(kb * 32 + l32, 16 * st + 8 * half)];
+      s[kb] = mfma32(a, qf[st], s[kb]);
+    }
+}
+
+// O^T += V^T P^T for one tile; the V^T operand comes from transposing LDS
+// reads in the key order of the P fragments.
+template <int D, int KB>
+__device__ __forceinline__ void pv_tile(floatx16 (&oacc)[D / 32], const bf16_t* vt, const bf16x8 (&pf)[2 * KB],
+                                        int half, int j16, int dsub) {
+#pragma unroll
+  for (int kk = 0; kk < 2 * KB; ++kk) {
+    const int kb0 = (kk >> 1) * 32 + (kk & 1) * 16 + 4 * half + (j16 >> 2);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      const int col = i * 32 + dsub;
+      const bf16x8 a = tr_pair(&vt[Swz<D>::off(kb0, col)], &vt[Swz<D>::off(kb0 + 8, col)]);
+      oacc[i] = mfma32(a, pf[kk], oacc[i]);
+    }
+  }
 }
 
 // Normalise O^T by the row sum and store fp32 [B*N][H][D].
@@ -270,16 +351,23 @@ __device__ __forceinline__ void store_rows(const floatx16 (&oacc)[D / 32], float
 }
 
 // ---------------------------------------------------------------------------
-// 4 waves, 128 query rows per workgroup; WPE workgroups' waves per SIMD.
-// PRIO: raise the wave's issue priority while it issues the S = K Q^T MFMAs,
-// so that the matrix pipe is fed first and the other wave's softmax fills in.
-template <int D, int KB, int WPE, bool PRIO>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(WPE, WPE)))
-void k_attn_bf16(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv, float sl2,
-                 float* __restrict__ os) {
-  constexpr int NW = 4, BM = 32 * NW, KS = D / 16, DB = D / 32, BN = 32 * KB;
+// Software-pipelined schedule, same work split.  Iteration t issues the
+// S = K Q^T MFMAs of tile t+1 interleaved with the exp work of tile t, then
+// the P V MFMAs of tile t interleaved with the row maximum of tile t+1, so each
+// wave's instruction stream mixes matrix and vector work evenly (the order is
+// pinned with scheduling-group barriers).  The row maximum is taken before the
+// tail mask: padded key rows repeat the last valid key, so they cannot raise
+// it.  K tiles are loaded two tiles ahead and V tiles one tile ahead, with one
+// barrier per tile.
+// NW waves (32 query rows each) per workgroup; PF: LDS operand reads issued
+// ahead of the MFMA that consumes them.
+template <int D, int KB, int NW, int PF>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
+void k_attn_bf16_sp(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv, float sl2,
+                    float* __restrict__ os) {
+  constexpr int BM = 32 * NW, KS = D / 16, DB = D / 32, BN = 32 * KB;
+  constexpr int NMF = KB * KS;  // MFMAs per S tile (= per P V tile)
   using Ldr = TileLoader<D, NW, KB>;
-  using SW = Swz<D>;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][Ldr::TILE];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[2][Ldr::TILE];
 
@@ -288,17 +376,29 @@ void k_attn_bf16(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv
   const int l32 = lane & 31, half = lane >> 5, j16 = lane & 15, lgrp = lane >> 4;
   const Item it = decode_item(d, (d.n + BM - 1) / BM);
 
-  // S(f) always holds the query's own frame, so the walk has >= 1 tile.
-  KeyWalk<BN> kw;
-  kw.init(d, it.f, it.b, it.h, k, v, tk, tv);
+  // kwk: next K tile to load, kwv: next V tile to load.  S(f) always holds
+  // the query's own frame, so there is at least one tile.
+  KeyWalk<BN> kwk;
+  kwk.init(d, it.f, it.b, it.h, k, v, tk, tv);
+  KeyWalk<BN> kwv = kwk;
   Ldr ldr;
   ldr.init(wave, lane);
+  ldr.set_k(kwk.ks);
+  ldr.set_v(kwv.vs);
   const unsigned ks_lds = lds_addr(Ks), vs_lds = lds_addr(Vs);
   constexpr unsigned kTileBytes = Ldr::TILE * 2;
-  int valid = kw.valid();
-  ldr.load(kw.kp, kw.ks, valid, wave, ks_lds);
-  ldr.load(kw.vp, kw.vs, valid, wave, vs_lds);
-  kw.advance();
+
+  const int valid0 = kwk.valid();
+  ldr.load_k(kwk.kp, valid0, wave, ks_lds);
+  if (kwk.advance()) ldr.set_k(kwk.ks);
+  ldr.load_v(kwv.vp, valid0, wave, vs_lds);
+  if (kwv.advance()) ldr.set_v(kwv.vs);
+  int vnext = 0;
+  if (!kwk.done()) {
+    vnext = kwk.valid();
+    ldr.load_k(kwk.kp, vnext, wave, ks_lds + kTileBytes);
+    if (kwk.advance()) ldr.set_k(kwk.ks);
+  }
 
   const int prow = it.qt * BM + wave * 32 + l32;
   const bool row_ok = prow < d.n;
@@ -318,61 +418,85 @@ void k_attn_bf16(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv
 
   wait_vmcnt<0>();
   tile_barrier();
+  floatx16 s[KB];
+  qk_tile<D, KB>(s, Ks[0], qf, l32, half);
+  float mx = tile_max<KB>(s, sl2);
+  int vcur = valid0;
+  tile_barrier();  // K buffer 0 is refilled below
 
-  for (int buf = 0;; buf ^= 1) {
-    const bool more = !kw.done();
-    const int valid_next = kw.valid();
-    if (more) {
-      ldr.load(kw.kp, kw.ks, valid_next, wave, ks_lds + (buf ^ 1) * kTileBytes);
-      ldr.load(kw.vp, kw.vs, valid_next, wave, vs_lds + (buf ^ 1) * kTileBytes);
-      kw.advance();
+  auto step = [&](auto bufc) -> bool {
+    constexpr int BUF = decltype(bufc)::value;
+    if (kwv.done()) return false;  // no tile t + 1
+    // K_{t+2} -> K buffer of tile t, V_{t+1} -> V buffer of tile t-1
+    int vk = 0;
+    if (!kwk.done()) {
+      vk = kwk.valid();
+      ldr.load_k(kwk.kp, vk, wave, ks_lds + BUF * kTileBytes);
+      if (kwk.advance()) ldr.set_k(kwk.ks);
     }
-    // ---- S^T = K Q^T: KB blocks of 32 keys
-    floatx16 s[KB];
-    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      s[kb] = zero16();
-      const int row = kb * 32 + l32;
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const bf16x8 a = *(const bf16x8*)&Ks[buf][SW::off(row, 16 * st + 8 * half)];
-        s[kb] = mfma32(a, qf[st], s[kb]);
-      }
-    }
-    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+    ldr.load_v(kwv.vp, kwv.valid(), wave, vs_lds + (BUF ^ 1) * kTileBytes);
+    if (kwv.advance()) ldr.set_v(kwv.vs);
+
+    rescale<DB>(mx, m_run, l_run, oacc);
+    if (vcur < BN) mask_tile<KB>(s, vcur, half);
+    // S(t+1) = K(t+1) Q^T  ||  P(t) = exp(S(t))
+    floatx16 sn[KB];
+    qk_tile<D, KB>(sn, Ks[BUF ^ 1], qf, l32, half);
     bf16x8 pf[2 * KB];
-    softmax_tile<KB, DB>(s, valid, half, sl2, m_run, l_run, oacc, pf);
-    // ---- O^T += V^T P^T; V^T operand via transposing LDS reads
+    exp_tile<KB>(s, sl2, m_run, l_run, pf);
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // LDS reads ahead
 #pragma unroll
-    for (int kk = 0; kk < 2 * KB; ++kk) {
-      const int kb0 = (kk >> 1) * 32 + (kk & 1) * 16 + 4 * half + (j16 >> 2);
-#pragma unroll
-      for (int i = 0; i < DB; ++i) {
-        const int col = i * 32 + dsub;
-        const bf16x8 a = tr_pair(&Vs[buf][SW::off(kb0, col)], &Vs[buf][SW::off(kb0 + 8, col)]);
-        oacc[i] = mfma32(a, pf[kk], oacc[i]);
-      }
+    for (int i = 0; i < NMF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
     }
-    if (!more) break;
-    wait_vmcnt<0>();  // this wave's loads of the next tile landed
+    // O += P(t) V(t)  ||  row max of S(t+1)
+    pv_tile<D, KB>(oacc, Vs[BUF], pf, half, j16, dsub);
+    mx = tile_max<KB>(sn, sl2);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);  // LDS reads ahead
+#pragma unroll
+    for (int i = 0; i < NMF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = sn[kb];
+    vcur = vnext;
+    vnext = vk;
+    wait_vmcnt<0>();  // this wave's loads of K_{t+2}, V_{t+1} landed
     tile_barrier();
-    valid = valid_next;
+    return true;
+  };
+  int last = 0;
+  for (;;) {
+    if (!step(std::integral_constant<int, 0>{})) break;
+    if (!step(std::integral_constant<int, 1>{})) {
+      last = 1;
+      break;
+    }
   }
+  rescale<DB>(mx, m_run, l_run, oacc);
+  if (vcur < BN) mask_tile<KB>(s, vcur, half);
+  bf16x8 pf[2 * KB];
+  exp_tile<KB>(s, sl2, m_run, l_run, pf);
+  pv_tile<D, KB>(oacc, last ? Vs[1] : Vs[0], pf, half, j16, dsub);
   store_rows<D>(oacc, l_run, row_ok, os + (((long long)it.b * d.N + qtok) * d.H + it.h) * D, half);
 }
 
-template <int D, int KB, int WPE, bool PRIO>
-static hipError_t launch_attn(const Dims& d, const Bf16Args& a, hipStream_t s) {
-  const long long grid = (long long)((d.n + 127) / 128) * d.H * d.B * d.T;
-  hipLaunchKernelGGL((k_attn_bf16<D, KB, WPE, PRIO>), dim3((unsigned)grid), dim3(256), 0, s, d, a.q, a.k, a.v, a.tk,
-                     a.tv, a.scale_log2, a.os);
+template <int D, int KB, int NW, int PF>
+static hipError_t launch_attn_sp(const Dims& d, const Bf16Args& a, hipStream_t s) {
+  constexpr int BM = 32 * NW;
+  const long long grid = (long long)((d.n + BM - 1) / BM) * d.H * d.B * d.T;
+  hipLaunchKernelGGL((k_attn_bf16_sp<D, KB, NW, PF>), dim3((unsigned)grid), dim3(64 * NW), 0, s, d, a.q, a.k, a.v,
+                     a.tk, a.tv, a.scale_log2, a.os);
   return hipGetLastError();
 }
 
 hipError_t launch_softmax_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
-  if (d.D == 128) return launch_attn<128, 2, 2, false>(d, a, s);
-  if (d.D == 64) return launch_attn<64, 2, 2, false>(d, a, s);
+  if (d.D == 128) return launch_attn_sp<128, 2, 4, 2>(d, a, s);
+  if (d.D == 64) return launch_attn_sp<64, 2, 4, 2>(d, a, s);
   return hipErrorInvalidValue;
 }
 
