@@ -84,7 +84,7 @@ void state_split(const hyb::Dims& d, int* split, int* ts, int* tsplit) {
 }
 
 enum {
-  W_OS, W_OL, W_SS, W_PART, W_PRE, W_CHI, W_CLO, W_CZ, W_AP, W_WG, W_WO,
+  W_OS, W_OL, W_SS, W_RINV, W_PART, W_PRE, W_CHI, W_CLO, W_CZ, W_AP, W_WG, W_WO,
   W_Q8, W_K8, W_V8, W_TK8, W_TV8, W_SC, W_AM, W_STATES, W_COMB, W_COUNT
 };
 
@@ -113,6 +113,7 @@ Plan make_plan(const hyb::Dims& d, hyb_dtype act, hyb_dtype soft) {
     sz[W_CHI] = BH * d.T * D * D * 2;
     sz[W_CLO] = BH * d.T * D * D * 2;
     sz[W_CZ] = BH * d.T * D * 4;
+    sz[W_RINV] = BN * 4;
     sz[W_AP] = BN * 2 * hid * 2;
     sz[W_WG] = 2 * hid * hid * 2;
     sz[W_WO] = 2 * hid * hid * 2;
@@ -301,6 +302,7 @@ hyb_status hyb_attn_forward(const hyb_layout* layout, hyb_dtype act, hyb_dtype s
     a.os = (float*)(ws + plan.off[W_OS]);
     a.ol = (float*)(ws + plan.off[W_OL]);
     a.ss = (float*)(ws + plan.off[W_SS]);
+    a.rinv = (float*)(ws + plan.off[W_RINV]);
     a.part = (float*)(ws + plan.off[W_PART]);
     a.pre = (float*)(ws + plan.off[W_PRE]);
     a.comb_hi = (hyb::bf16_t*)(ws + plan.off[W_CHI]);

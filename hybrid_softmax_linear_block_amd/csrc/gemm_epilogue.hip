@@ -13,6 +13,8 @@
 // within its range.  Values beyond +-65504 saturate.
 // Both GEMMs compute C^T = W^T X^T so that a lane owns one token (the RMS
 // factor is a per-lane scalar) and four consecutive features (vector stores).
+#include <type_traits>
+
 #include "kernels_bf16.h"
 
 namespace hyb {
@@ -25,9 +27,8 @@ struct GemmArgs {
   long long M;
   int N, K;
   int hid, H;
-  float eps;
   // gate epilogue
-  const float *os, *ol, *ss;
+  const float *os, *ol, *rinv;
   const bf16_t* rmsw;
   uint16_t* ap;
   float* gates_dbg;
@@ -37,35 +38,32 @@ struct GemmArgs {
   float* delta_dbg;
 };
 
-typedef __attribute__((address_space(3))) void lds_void_g;
-
-// WG = 4 waves in a 2 (tokens) x 2 (features) grid; each wave computes
-// WTM x WFN blocks of 32 x 32.  BK-deep k-tiles live in a 3-stage LDS ring
-// filled by wave-wide direct-to-LDS loads (1 KB per wave instruction, 16-byte
-// granules XOR-swizzled by row); loads for k-tile t + 2 are in flight while
-// k-tile t is multiplied.  Each stage is its own LDS object and the loop is
-// unrolled by three, so the compiler sees that the loads in flight never
-// alias the tile being read and does not wait for them.
-template <int WTM, int WFN, int BK, int WPE, int EPI>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(WPE, WPE)))
+// WG = WM x WN waves; each wave computes WTM x WFN blocks of 32 x 32 (tokens x
+// features).  BK-deep k-tiles live in an ST-stage LDS ring filled by
+// wave-wide direct-to-LDS loads (1 KB per wave instruction, 16-byte granules
+// XOR-swizzled by row); loads for k-tile t + ST - 1 are in flight while
+// k-tile t is multiplied.  The k loop is unrolled by ST so that every LDS
+// address is a per-lane base plus an immediate, and the DMA source is a
+// scalar base (bumped per k-tile) plus a fixed per-lane offset.
+template <int WM, int WN, int WTM, int WFN, int BK, int ST, int WPE, int EPI>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN),
+                          amdgpu_waves_per_eu(WPE, WPE)))
 void k_gemm_bf16(GemmArgs g) {
-  constexpr int BM = 2 * WTM * 32, BN = 2 * WFN * 32;
-  constexpr int G = BK / 8, RPC = 64 / G;           // granules per row, rows per 1 KB chunk
-  constexpr int CA = BM / RPC / 4, CB = BN / RPC / 4;  // chunks per wave
-  constexpr int LPT = CA + CB;                       // loads per k-tile per wave
-  static_assert(CA >= 1 && CB >= 1 && (BM / RPC) % 4 == 0 && (BN / RPC) % 4 == 0, "tile/chunk mismatch");
-  static_assert(LPT < 64, "vmcnt range");
+  constexpr int NWV = WM * WN;
+  constexpr int BM = WM * WTM * 32, BN = WN * WFN * 32;
+  constexpr int G = BK / 8, RPC = 64 / G;                   // granules per row, rows per 1 KB chunk
+  constexpr int CA = BM / RPC / NWV, CB = BN / RPC / NWV;   // chunks per wave
+  constexpr int LPT = CA + CB;                              // loads per k-tile per wave
+  static_assert(CA >= 1 && CB >= 1 && (BM / RPC) % NWV == 0 && (BN / RPC) % NWV == 0, "tile/chunk mismatch");
+  static_assert(LPT * ST < 64, "vmcnt range");
+  constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2, SBYTES = ABYTES + BBYTES;
   using SW = Swz<BK>;
-  __shared__ __attribute__((aligned(16))) uint16_t As0[BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t As1[BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t As2[BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs0[BN * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs1[BN * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs2[BN * BK];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[ST * SBYTES / 2];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
   const int ntn = g.N / BN;
   const unsigned wid = xcd_remap(blockIdx.x, gridDim.x);
   const long long m0 = (long long)(wid / ntn) * BM;
@@ -77,122 +75,152 @@ void k_gemm_bf16(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < WTM; ++j) acc[i][j] = zero16();
 
-  // per-lane source pointers of the first k-tile; later tiles add k0 elements
-  const uint16_t* asrc[CA];
-  const uint16_t* bsrc[CB];
+  // DMA sources: scalar bases at k = 0, per-lane byte offsets (rows past M
+  // repeat the last row; never stored)
+  const long long mlast = g.M - 1 - m0;
+  const char* abase = (const char*)(g.A + m0 * g.K);
+  const char* bbase = (const char*)(g.Bt + (long long)n0 * g.K);
+  unsigned aoff[CA], boff[CB];
 #pragma unroll
   for (int i = 0; i < CA; ++i) {
     const int row = (wave * CA + i) * RPC + lane / G;
-    long long m = m0 + row;
-    if (m >= g.M) m = g.M - 1;  // rows past the end repeat the last row; never stored
-    asrc[i] = g.A + m * g.K + ((lane % G) ^ SW::key(row)) * 8;
+    const long long r = row < mlast ? row : mlast;
+    aoff[i] = (unsigned)(r * g.K * 2) + ((lane % G) ^ SW::key(row)) * 16;
   }
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
     const int row = (wave * CB + i) * RPC + lane / G;
-    bsrc[i] = g.Bt + (long long)(n0 + row) * g.K + ((lane % G) ^ SW::key(row)) * 8;
+    boff[i] = (unsigned)((long long)row * g.K * 2) + ((lane % G) ^ SW::key(row)) * 16;
   }
-  auto issue = [&](int kt, uint16_t* adst, uint16_t* bdst) {
-    const int k0 = kt * BK;
+  const unsigned lds0 = lds_addr(lds);
+  auto issue = [&](int kt, int stage) {
+    const char* ab = abase + (long long)kt * BK * 2;
+    const char* bb = bbase + (long long)kt * BK * 2;
+    const unsigned la = lds0 + stage * SBYTES, lb = la + ABYTES;
 #pragma unroll
-    for (int i = 0; i < CA; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + k0),
-                                       (lds_void_g*)(adst + (wave * CA + i) * RPC * BK), 16, 0, 0);
+    for (int i = 0; i < CA; ++i) dma16(ab, aoff[i], la + (wave * CA + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < CB; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(bsrc[i] + k0),
-                                       (lds_void_g*)(bdst + (wave * CB + i) * RPC * BK), 16, 0, 0);
+    for (int i = 0; i < CB; ++i) dma16(bb, boff[i], lb + (wave * CB + i) * 1024);
   };
-  // (separate LDS objects per stage let the compiler keep these loads in
-  // flight across the LDS reads of other stages)
-  auto mma = [&](const uint16_t* at, const uint16_t* bt_) {
+  // one k-tile: all operand reads first, then the MFMAs
+  auto mma = [&](auto stc) {
+    constexpr int STG = decltype(stc)::value;
+    const uint16_t* at = lds + STG * SBYTES / 2;
+    const uint16_t* bt_ = at + ABYTES / 2;
+    uint4 ta[BK / 16][WTM], tb[BK / 16][WFN];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      uint4 bt[WTM];
 #pragma unroll
-      for (int tb = 0; tb < WTM; ++tb)
-        bt[tb] = *(const uint4*)&at[SW::off(wm * WTM * 32 + tb * 32 + l32, 16 * ks + 8 * half)];
+      for (int i = 0; i < WTM; ++i)
+        ta[ks][i] = *(const uint4*)&at[SW::off(wm * WTM * 32 + i * 32 + l32, 16 * ks + 8 * half)];
 #pragma unroll
-      for (int fb = 0; fb < WFN; ++fb) {
-        const uint4 a = *(const uint4*)&bt_[SW::off(wn * WFN * 32 + fb * 32 + l32, 16 * ks + 8 * half)];
-#pragma unroll
-        for (int tb = 0; tb < WTM; ++tb) {
-          if constexpr (EPI == EPI_GATE)
-            acc[fb][tb] = mfma32(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bt[tb]), acc[fb][tb]);
-          else
-            acc[fb][tb] = mfma32_f16(__builtin_bit_cast(halfx8, a), __builtin_bit_cast(halfx8, bt[tb]), acc[fb][tb]);
-        }
-      }
+      for (int f = 0; f < WFN; ++f)
+        tb[ks][f] = *(const uint4*)&bt_[SW::off(wn * WFN * 32 + f * 32 + l32, 16 * ks + 8 * half)];
     }
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+      for (int f = 0; f < WFN; ++f)
+#pragma unroll
+        for (int i = 0; i < WTM; ++i) {
+          if constexpr (EPI == EPI_GATE)
+            acc[f][i] = mfma32(__builtin_bit_cast(bf16x8, tb[ks][f]), __builtin_bit_cast(bf16x8, ta[ks][i]), acc[f][i]);
+          else
+            acc[f][i] = mfma32_f16(__builtin_bit_cast(halfx8, tb[ks][f]), __builtin_bit_cast(halfx8, ta[ks][i]),
+                                   acc[f][i]);
+        }
   };
 
   const int nk = g.K / BK;
-  // step kt: multiply the tile in (ac, bc) while k-tile kt+2 loads into (an, bn)
-  auto step = [&](int kt, const uint16_t* ac, const uint16_t* bc, uint16_t* an, uint16_t* bn) {
-    const bool more = kt + 2 < nk;
-    if (more) issue(kt + 2, an, bn);
-    mma(ac, bc);
-    if (more) wait_vmcnt<LPT>();  // k-tile kt+1 landed; kt+2 may stay in flight
+  // k-tile kt in stage STG: issue k-tile kt + ST - 1 into the stage read at
+  // kt - 1 (free after the previous barrier), multiply, wait for kt + 1.
+  auto step = [&](int kt, auto stc) {
+    constexpr int STG = decltype(stc)::value;
+    const bool more = kt + ST - 1 < nk;
+    if (more) issue(kt + ST - 1, (STG + ST - 1) % ST);
+    mma(stc);
+    if (more) wait_vmcnt<(ST - 2) * LPT>();  // k-tile kt+1 landed; later ones may stay in flight
     else wait_vmcnt<0>();
     tile_barrier();
   };
-  issue(0, As0, Bs0);
-  if (nk > 1) issue(1, As1, Bs1);
-  if (nk > 1) wait_vmcnt<LPT>();
+#pragma unroll
+  for (int s0 = 0; s0 < ST - 1; ++s0)
+    if (s0 < nk) issue(s0, s0);
+  if (nk >= ST - 1) wait_vmcnt<(ST - 2) * LPT>();
   else wait_vmcnt<0>();
   tile_barrier();
-  for (int kt = 0; kt < nk; kt += 3) {
-    step(kt, As0, Bs0, As2, Bs2);
-    if (kt + 1 < nk) step(kt + 1, As1, Bs1, As0, Bs0);
-    if (kt + 2 < nk) step(kt + 2, As2, Bs2, As1, Bs1);
+  for (int kt = 0; kt < nk; kt += ST) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1 % ST>{});
+    if constexpr (ST > 2)
+      if (kt + 2 < nk) step(kt + 2, std::integral_constant<int, 2 % ST>{});
+    if constexpr (ST > 3)
+      if (kt + 3 < nk) step(kt + 3, std::integral_constant<int, 3 % ST>{});
   }
 
-  // ---- epilogue: lane owns token m, features n0' + 8*jg + 4*half + 0..3
+  // ---- epilogue: lane owns token m, features n0' + 8*jg + 4*half + 0..3.
+  // All loads of one token row are issued before its stores.
 #pragma unroll
-  for (int tb = 0; tb < WTM; ++tb) {
-    const long long m = m0 + wm * WTM * 32 + tb * 32 + l32;
+  for (int i = 0; i < WTM; ++i) {
+    const long long m = m0 + wm * WTM * 32 + i * 32 + l32;
     if (m >= g.M) continue;
-    float rinv = 0.f;
+    const int nw = n0 + wn * WFN * 32 + 4 * half;  // + 32 f + 8 jg
     if constexpr (EPI == EPI_GATE) {
-      float tot = 0.f;
-      for (int hh = 0; hh < g.H; ++hh) tot += g.ss[m * g.H + hh];
-      rinv = rsqrtf(tot / (float)g.hid + g.eps);
-    }
+      float4 val[WFN][4];
+      const bool lin = nw >= g.hid;  // a wave's features are all in one half (hid % BN == 0)
+      if (!lin) {
 #pragma unroll
-    for (int fb = 0; fb < WFN; ++fb)
+        for (int f = 0; f < WFN; ++f)
 #pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        const int n = n0 + wn * WFN * 32 + fb * 32 + 8 * jg + 4 * half;
-        const float c0 = acc[fb][tb][4 * jg], c1 = acc[fb][tb][4 * jg + 1];
-        const float c2 = acc[fb][tb][4 * jg + 2], c3 = acc[fb][tb][4 * jg + 3];
-        if constexpr (EPI == EPI_GATE) {
-          const float g0 = sigmoid_f(c0), g1 = sigmoid_f(c1), g2 = sigmoid_f(c2), g3 = sigmoid_f(c3);
-          float4 val;
-          if (n < g.hid) {
-            val = *(const float4*)(g.os + m * g.hid + n);
-          } else {
-            const int c = n - g.hid;
+          for (int jg = 0; jg < 4; ++jg) val[f][jg] = *(const float4*)(g.os + m * g.hid + nw + 32 * f + 8 * jg);
+      } else {
+        const float rinv = g.rinv[m];
+#pragma unroll
+        for (int f = 0; f < WFN; ++f)
+#pragma unroll
+          for (int jg = 0; jg < 4; ++jg) {
+            const int c = nw - g.hid + 32 * f + 8 * jg;
             const float4 o = *(const float4*)(g.ol + m * g.hid + c);
             const uint2 wv = *(const uint2*)(g.rmsw + c);
-            val.x = o.x * __uint_as_float(wv.x << 16) * rinv;
-            val.y = o.y * __uint_as_float(wv.x & 0xffff0000u) * rinv;
-            val.z = o.z * __uint_as_float(wv.y << 16) * rinv;
-            val.w = o.w * __uint_as_float(wv.y & 0xffff0000u) * rinv;
+            val[f][jg].x = o.x * __uint_as_float(wv.x << 16) * rinv;
+            val[f][jg].y = o.y * __uint_as_float(wv.x & 0xffff0000u) * rinv;
+            val[f][jg].z = o.z * __uint_as_float(wv.y << 16) * rinv;
+            val[f][jg].w = o.w * __uint_as_float(wv.y & 0xffff0000u) * rinv;
           }
+      }
+#pragma unroll
+      for (int f = 0; f < WFN; ++f)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const int n = nw + 32 * f + 8 * jg;
+          const float g0 = sigmoid_f(acc[f][i][4 * jg]), g1 = sigmoid_f(acc[f][i][4 * jg + 1]);
+          const float g2 = sigmoid_f(acc[f][i][4 * jg + 2]), g3 = sigmoid_f(acc[f][i][4 * jg + 3]);
           uint2 st;
-          st.x = pack_f16x2(g0 * val.x, g1 * val.y);
-          st.y = pack_f16x2(g2 * val.z, g3 * val.w);
+          st.x = pack_f16x2(g0 * val[f][jg].x, g1 * val[f][jg].y);
+          st.y = pack_f16x2(g2 * val[f][jg].z, g3 * val[f][jg].w);
           *(uint2*)(g.ap + m * (2LL * g.hid) + n) = st;
           if (g.gates_dbg) *(float4*)(g.gates_dbg + m * (2LL * g.hid) + n) = make_float4(g0, g1, g2, g3);
-        } else {
-          const uint2 xv = *(const uint2*)(g.x + m * g.hid + n);
+        }
+    } else {
+      uint2 xv[WFN][4];
+#pragma unroll
+      for (int f = 0; f < WFN; ++f)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) xv[f][jg] = *(const uint2*)(g.x + m * g.hid + nw + 32 * f + 8 * jg);
+#pragma unroll
+      for (int f = 0; f < WFN; ++f)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const int n = nw + 32 * f + 8 * jg;
+          const float c0 = acc[f][i][4 * jg], c1 = acc[f][i][4 * jg + 1];
+          const float c2 = acc[f][i][4 * jg + 2], c3 = acc[f][i][4 * jg + 3];
           uint2 st;
-          st.x = pack_bf16x2(__uint_as_float(xv.x << 16) + c0, __uint_as_float(xv.x & 0xffff0000u) + c1);
-          st.y = pack_bf16x2(__uint_as_float(xv.y << 16) + c2, __uint_as_float(xv.y & 0xffff0000u) + c3);
+          st.x = pack_bf16x2(__uint_as_float(xv[f][jg].x << 16) + c0, __uint_as_float(xv[f][jg].x & 0xffff0000u) + c1);
+          st.y = pack_bf16x2(__uint_as_float(xv[f][jg].y << 16) + c2, __uint_as_float(xv[f][jg].y & 0xffff0000u) + c3);
           *(uint2*)(g.y + m * g.hid + n) = st;
           if (g.delta_dbg) *(float4*)(g.delta_dbg + m * g.hid + n) = make_float4(c0, c1, c2, c3);
         }
-      }
+    }
   }
 }
 
@@ -232,12 +260,15 @@ hipError_t launch_weights_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) 
   return hipGetLastError();
 }
 
-template <int WTM, int WFN, int BK, int WPE, int EPI>
+template <int WM, int WN, int WTM, int WFN, int BK, int ST, int WPE, int EPI>
 static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
-  constexpr int BM = 2 * WTM * 32, BN = 2 * WFN * 32;
-  if (g.N % BN != 0 || g.K % BK != 0) return hipErrorInvalidValue;
+  constexpr int BM = WM * WTM * 32, BN = WN * WFN * 32;
+  if (g.N % BN != 0 || g.K % BK != 0 || (EPI == EPI_GATE && g.hid % BN != 0)) return hipErrorInvalidValue;
+  // 32-bit per-lane DMA offsets: a tile's rows span < 4 GiB
+  if ((long long)BM * g.K * 2 >= (1LL << 32) || (long long)BN * g.K * 2 >= (1LL << 32)) return hipErrorInvalidValue;
   const long long grid = ((g.M + BM - 1) / BM) * (g.N / BN);
-  hipLaunchKernelGGL((k_gemm_bf16<WTM, WFN, BK, WPE, EPI>), dim3((unsigned)grid), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((k_gemm_bf16<WM, WN, WTM, WFN, BK, ST, WPE, EPI>), dim3((unsigned)grid), dim3(64 * WM * WN), 0,
+                     s, g);
   return hipGetLastError();
 }
 
@@ -246,7 +277,6 @@ static GemmArgs base_args(const Dims& d, const Bf16Args& a) {
   g.M = (long long)d.B * d.N;
   g.hid = d.hid;
   g.H = d.H;
-  g.eps = a.eps;
   return g;
 }
 
@@ -258,12 +288,13 @@ hipError_t launch_gate_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s
   g.K = d.hid;
   g.os = a.os;
   g.ol = a.ol;
-  g.ss = a.ss;
+  g.rinv = a.rinv;
   g.rmsw = a.rmsw;
   g.ap = a.ap;
   g.gates_dbg = a.gates_dbg;
-  if (g.N % 128 == 0) return launch_gemm<4, 2, 32, 2, EPI_GATE>(g, s);
-  return launch_gemm<4, 1, 32, 2, EPI_GATE>(g, s);  // hid multiple of 64 only
+  if (d.hid % 256 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_GATE>(g, s);
+  if (d.hid % 128 == 0) return launch_gemm<2, 2, 4, 2, 32, 3, 2, EPI_GATE>(g, s);
+  return launch_gemm<2, 2, 4, 1, 32, 3, 2, EPI_GATE>(g, s);  // hid multiple of 64 only
 }
 
 hipError_t launch_out_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
@@ -275,8 +306,9 @@ hipError_t launch_out_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s)
   g.x = a.x;
   g.y = a.y;
   g.delta_dbg = a.delta_dbg;
-  if (g.N % 128 == 0) return launch_gemm<4, 2, 32, 2, EPI_OUT>(g, s);
-  return launch_gemm<4, 1, 32, 2, EPI_OUT>(g, s);
+  if (g.N % 256 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_OUT>(g, s);
+  if (g.N % 128 == 0) return launch_gemm<2, 2, 4, 2, 32, 3, 2, EPI_OUT>(g, s);
+  return launch_gemm<2, 2, 4, 1, 32, 3, 2, EPI_OUT>(g, s);
 }
 
 }  // namespace hyb

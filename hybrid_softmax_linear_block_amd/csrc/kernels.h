@@ -25,6 +25,7 @@ struct Bf16Args {
   float* os;              // [B*N][hid] fp32 softmax-branch output
   float* ol;              // [B*N][hid] fp32 linear-branch output
   float* ss;              // [B*N][H]   sum of squares of O_l per head
+  float* rinv;            // [B*N]      1 / sqrt(mean over hid of O_l^2 + eps)
   float* part;            // [B*H][slots][D*D+D] partial frame states: S^T [e][d], then z[d]
   bf16_t* comb_hi;        // [B*H][T][D][D] combined state, transposed [e][d], hi part
   bf16_t* comb_lo;        // same, residual part

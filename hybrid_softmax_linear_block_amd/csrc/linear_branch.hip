@@ -326,6 +326,17 @@ hipError_t launch_scan_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// RMS factor of the linear branch per token: the per-head sums of squares
+// from the readout, summed over heads in order, -> 1 / sqrt(mean + eps).
+__global__ __launch_bounds__(256) void k_rms_rinv(const float* __restrict__ ss, long long M, int H, int hid, float eps,
+                                                  float* __restrict__ rinv) {
+  const long long m = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (m >= M) return;
+  float tot = 0.f;
+  for (int h = 0; h < H; ++h) tot += ss[m * H + h];
+  rinv[m] = rsqrtf(tot / (float)hid + eps);
+}
+
 hipError_t launch_readout_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
   const int tt = 256;
   const long long grid = (long long)d.B * d.H * d.T * ((d.n + tt - 1) / tt);
@@ -335,6 +346,11 @@ hipError_t launch_readout_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) 
   else
     hipLaunchKernelGGL(k_readout_bf16<64>, dim3((unsigned)grid), dim3(256), 0, s, d, a.q, a.comb_hi, a.comb_lo,
                        a.comb_z, a.eps, tt, a.ol, a.ss);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long M = (long long)d.B * d.N;
+  hipLaunchKernelGGL(k_rms_rinv, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, a.ss, M, d.H, d.hid, a.eps,
+                     a.rinv);
   return hipGetLastError();
 }
 
