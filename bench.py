@@ -26,6 +26,7 @@ WORKLOADS_ID = {w.name: i for i, w in WORKLOADS.items()}
 
 METRIC = "hybrid-attn layer Mtokens/s + softmax-branch TFLOP/s (768p-shaped, bf16)"
 PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense MFMA TFLOP/s, MI355X published
+PEAK_HBM_GBS = 8000.0  # HBM3E, MI355X published
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = {"softmax": "attn_softmax.hip", "softmax_fp8": "fp8_softmax.hip"}
 
@@ -51,6 +52,47 @@ def work_counts(w):
     gemm = 2 * (2.0 * B * N * hid * 2 * hid)
     return {"pairs_per_bh": pairs, "softmax_flop": soft, "linear_flop": states + readout, "gemm_flop": gemm,
             "layer_flop": soft + states + readout + gemm}
+
+
+def stage_work(w, soft):
+    """Algorithmic work per stage of the bf16 path: FLOP for the MFMA
+    kernels, the HBM bytes each kernel must move for the others (inputs read
+    once, outputs written once, intermediates in the formats the path uses)."""
+    B, H, D, N, T, L, hid = w.batch, w.heads, w.head_dim, w.n_video, w.frames, w.text_tokens, w.hidden
+    es = 2
+    st = (D * D + D) * 4
+    wc = work_counts(w)
+    gemm_flop = 2.0 * B * N * hid * 2 * hid
+    work = {
+        "weights": ("hbm", 2 * 2 * (2 * hid * hid * 2)),
+        "softmax": ("mfma", wc["softmax_flop"]),
+        "states": ("hbm", 2 * B * (N + L) * hid * es + B * H * (T + 1) * st),
+        "scan": ("hbm", B * H * (T + 1) * st + B * H * T * (2 * D * D * 2 + D * 4)),
+        "readout": ("hbm", B * N * hid * es + B * H * T * (2 * D * D * 2 + D * 4) + B * N * hid * 4 + B * N * H * 4),
+        "gate": ("mfma", gemm_flop),
+        "out": ("mfma", gemm_flop),
+    }
+    if soft:
+        work["quant"] = ("hbm", (3 * B * N + 2 * B * L) * hid * (es + 1))
+    return work
+
+
+def stage_roofline(w, soft, stage_ms):
+    out = {}
+    for k, (bound, amount) in stage_work(w, soft).items():
+        t = stage_ms.get(k, 0.0)
+        if t <= 0:
+            continue
+        if bound == "mfma":
+            peak = PEAK["fp8" if (soft and k == "softmax") else w.act]
+            ach = amount / (t * 1e-3) / 1e12
+            out[k] = {"bound": "mfma", "algorithmic": amount, "unit": "TFLOP/s", "achieved": round(ach, 2),
+                      "peak": peak, "frac": round(ach / peak, 4)}
+        else:
+            ach = amount / (t * 1e-3) / 1e9
+            out[k] = {"bound": "hbm", "algorithmic": amount, "unit": "GB/s", "achieved": round(ach, 1),
+                      "peak": PEAK_HBM_GBS, "frac": round(ach / PEAK_HBM_GBS, 4)}
+    return out
 
 
 def describe(w):
@@ -158,6 +200,20 @@ def cpu_baseline(w, inp, budget_s=20.0):
             "wall_s": round(t_states + t_rows, 2)}
 
 
+def device_info(torch):
+    """Name, CU count and peak shader clock of device 0 (the peaks above are
+    MI355X's published figures: 256 CUs at 2.4 GHz)."""
+    import ctypes
+    props = torch.cuda.get_device_properties(0)
+    clock_khz = ctypes.c_int(0)
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
+    ok = hip.hipDeviceGetAttribute(ctypes.byref(clock_khz), 5, 0) == 0  # hipDeviceAttributeClockRate
+    return {"name": props.name, "arch": props.gcnArchName, "compute_units": props.multi_processor_count,
+            "peak_clock_mhz": clock_khz.value / 1000.0 if ok else None,
+            "peak_basis": "published MI355X dense peaks (256 CUs, 2.4 GHz)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,11 +277,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     stage = {k: [] for k in api.STAGES}
+    span = []
     for t in timers:
         for k, v in t.elapsed_ms().items():
             stage[k].append(v)
+        span.append(t.span_ms())
     for t in timers:
         t.close()
+
+    def pct(v):
+        p10, p50, p90 = np.percentile(np.asarray(v), [10, 50, 90])
+        return {"p10": round(float(p10), 4), "p50": round(float(p50), 4), "p90": round(float(p90), 4)}
     stage_ms = {k: float(np.mean(v)) for k, v in stage.items()}
     ms = wall * 1e3 / args.steps
     wc = work_counts(w)
@@ -244,6 +306,9 @@ def main():
         "softmax_tflops": round(soft_tflops, 2),
         "layer_tflops": round(wc["layer_flop"] / (ms * 1e-3) / 1e12, 2),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "gpu_ms_percentiles": {"forward": pct(span), "softmax": pct(stage["softmax"])},
+        "stage_roofline": stage_roofline(w, soft, stage_ms) if w.act != "f32" else None,
+        "device": device_info(torch),
         "roofline": {"kernel": "k_attn_bf16_sp (softmax branch)" if not soft else "softmax branch fp8",
                      "bound": "mfma", "achieved": round(soft_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(soft_tflops / peak, 4), "traffic": traffic_for(soft_key, w.name),

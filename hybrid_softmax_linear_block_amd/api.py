@@ -222,6 +222,16 @@ class StageTimer:
             out[name] = ms.value
         return out
 
+    def span_ms(self):
+        """Milliseconds from the start of the first stage to the end of the
+        last one (the whole forward on the GPU)."""
+        a, b = self.events[0], self.events[2 * len(STAGES) - 1]
+        self._hip.hipEventSynchronize(b)
+        ms = ctypes.c_float(0)
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
     def close(self):
         for ev in self.events:
             if ev:

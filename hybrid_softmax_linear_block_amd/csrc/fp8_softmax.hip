@@ -15,6 +15,7 @@
 //                 P operand holds them (see slot_of_key)
 //   scales        [5][B][H] fp32 (q, k, v, text_k, text_v)
 #include "kernels_bf16.h"
+#include "work_items.h"
 
 namespace hyb {
 
@@ -194,7 +195,10 @@ __device__ __forceinline__ int swz8(int row, int byte) {
   return row * ROWB + (((g ^ k)) << 4) + (byte & 15);
 }
 
-template <int D, int NW>
+// NS-stage ring of K and V^T tiles in LDS, filled by wave-wide direct-to-LDS
+// loads NS - 1 tiles ahead (a tile is only 4 or 8 KB and carries little
+// arithmetic, so its load latency has to be covered by several tiles).
+template <int D, int NW, int NS>
 __global__ __launch_bounds__(64 * NW) void k_attn_fp8(Dims d, const uint8_t* __restrict__ q8,
                                                        const uint8_t* __restrict__ k8,
                                                        const uint8_t* __restrict__ v8t,
@@ -202,21 +206,22 @@ __global__ __launch_bounds__(64 * NW) void k_attn_fp8(Dims d, const uint8_t* __r
                                                        const uint8_t* __restrict__ tv8t,
                                                        const float* __restrict__ scales, float sl2,
                                                        float* __restrict__ os) {
-  constexpr int BM = 32 * NW, NT = 64 * NW;
+  constexpr int BM = 32 * NW;
   constexpr int KSTEP = D / 64;      // 64-deep k-steps of Q K^T
   constexpr int DB = D / 32;         // d blocks of O^T
-  constexpr int KG = 64 * D / 16;    // 16-byte granules of a K tile (== of a V tile)
-  __shared__ __attribute__((aligned(16))) uint8_t Ks[2][64 * D];
-  __shared__ __attribute__((aligned(16))) uint8_t Vs[2][D * 64];
+  constexpr int TB = 64 * D;         // bytes of a K tile (== of a V^T tile)
+  constexpr int CPW = TB / 1024 / NW;  // 1 KB chunks per wave per tile
+  constexpr int LPT = 2 * CPW;         // loads per tile per wave
+  static_assert(CPW >= 1 && (TB / 1024) % NW == 0, "tile chunks must split evenly over waves");
+  static_assert(LPT * NS < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[NS][TB];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs[NS][TB];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
-  const int qtiles = (d.n + BM - 1) / BM;
-  unsigned w = blockIdx.x;
-  const int qt = w % qtiles; w /= qtiles;
-  const int h = w % d.H; w /= d.H;
-  const int b = w % d.B; w /= d.B;
-  const int f = frame_by_cost(d.g, (int)w);
+  const Item it = decode_item(d, (d.n + BM - 1) / BM);
+  const int qt = it.qt, h = it.h, b = it.b, f = it.f;
   const float sq = scales[(0 * d.B + b) * d.H + h], sk = scales[(1 * d.B + b) * d.H + h];
   const float sv = scales[(2 * d.B + b) * d.H + h];
   const float stk = scales[(3 * d.B + b) * d.H + h], stv = scales[(4 * d.B + b) * d.H + h];
@@ -227,6 +232,67 @@ __global__ __launch_bounds__(64 * NW) void k_attn_fp8(Dims d, const uint8_t* __r
   int nframes = 0;
   for (int r = 0; r < sr.n; ++r) nframes += sr.hi[r] - sr.lo[r];
   const int total = nframes * ntv + ntt;
+  const unsigned kstride = (unsigned)(d.H * D);  // bytes per token row of k8 / tk8
+
+  // Per chunk: the lane's byte offset inside a full tile.  Lane l fills
+  // physical granule (l % G) of row (l / G) of the chunk, which holds logical
+  // granule (l % G) ^ swizzle(row) (the layout swz8 reads).
+  constexpr int GK = D / 16, RK = 64 / GK;  // K: granules per row, rows per chunk
+  unsigned koff[CPW], voff[CPW], krow[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int c = wave * CPW + i;
+    const int row = c * RK + lane / GK;
+    const int sw = D == 64 ? ((row >> 2) & 3) : ((row >> 1) & 7);
+    krow[i] = (unsigned)row;
+    koff[i] = (unsigned)row * kstride + (unsigned)(((lane % GK) ^ sw) * 16);
+    const int vrow = c * 16 + lane / 4;  // V^T rows are 64 bytes: 4 granules
+    voff[i] = (unsigned)(vrow * 64 + ((((lane % 4) ^ ((vrow >> 2) & 3))) * 16));
+  }
+  const unsigned ks_lds = lds_addr(Ks), vs_lds = lds_addr(Vs);
+
+  // tile t -> sources, valid keys, text or video
+  auto tile_info = [&](int t, const uint8_t*& kb, const uint8_t*& vb, int& valid, bool& is_text) {
+    if (t < nframes * ntv) {
+      int fi = t / ntv;
+      const int tt = t - fi * ntv;
+      int g = 0;
+      for (int r = 0; r < sr.n; ++r) {
+        const int len = sr.hi[r] - sr.lo[r];
+        if (fi < len) { g = sr.lo[r] + fi; break; }
+        fi -= len;
+      }
+      valid = min(64, d.n - tt * 64);
+      is_text = false;
+      kb = k8 + (((long long)b * d.N + (long long)g * d.n + tt * 64) * d.H + h) * D;
+      vb = v8t + ((long long)(b * d.H + h) * d.T * ntv + (long long)g * ntv + tt) * (D * 64);
+    } else {
+      const int tt = t - nframes * ntv;
+      valid = min(64, d.L - tt * 64);
+      is_text = true;
+      kb = tk8 + (((long long)b * d.L + tt * 64) * d.H + h) * D;
+      vb = tv8t + ((long long)(b * d.H + h) * ntt + tt) * (D * 64);
+    }
+  };
+  // Rows of K past the valid keys repeat the last valid row (their scores
+  // are masked); the V^T tiles are padded by the quantiser.
+  auto issue = [&](int t) {
+    const uint8_t *kb, *vb;
+    int valid;
+    bool is_text;
+    tile_info(t, kb, vb, valid, is_text);
+    const int stg = t % NS;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      unsigned off = koff[i];
+      if (valid < 64) {
+        const unsigned r = min(krow[i], (unsigned)(valid - 1));
+        off = off - krow[i] * kstride + r * kstride;
+      }
+      dma16(kb, off, ks_lds + stg * TB + (wave * CPW + i) * 1024);
+      dma16(vb, voff[i], vs_lds + stg * TB + (wave * CPW + i) * 1024);
+    }
+  };
 
   const int prow = qt * BM + wave * 32 + l32;
   const bool row_ok = prow < d.n;
@@ -247,67 +313,25 @@ __global__ __launch_bounds__(64 * NW) void k_attn_fp8(Dims d, const uint8_t* __r
   for (int i = 0; i < DB; ++i) { oacc_v[i] = zero16(); oacc_t[i] = zero16(); }
   float m_run = -INFINITY, l_run = 0.f;
 
-  uint4 kreg[(KG + NT - 1) / NT], vreg[(KG + NT - 1) / NT];
-  constexpr int GPT = (KG + NT - 1) / NT;
-  int cur_valid = 0, nxt_valid = 0;
-  bool cur_text = false, nxt_text = false;
-
-  auto fetch = [&](int t, int& valid, bool& is_text) {
-    const uint8_t* kb;
-    const uint8_t* vb;
-    long long kstride = (long long)d.H * D;
-    if (t < nframes * ntv) {
-      int fi = t / ntv, tt = t % ntv;
-      int g = 0;
-      for (int r = 0; r < sr.n; ++r) {
-        const int len = sr.hi[r] - sr.lo[r];
-        if (fi < len) { g = sr.lo[r] + fi; break; }
-        fi -= len;
-      }
-      valid = min(64, d.n - tt * 64);
-      is_text = false;
-      kb = k8 + (((long long)b * d.N + (long long)g * d.n + tt * 64) * d.H + h) * D;
-      vb = v8t + ((long long)(b * d.H + h) * d.T * ntv + (long long)g * ntv + tt) * (D * 64);
-    } else {
-      const int tt = t - nframes * ntv;
-      valid = min(64, d.L - tt * 64);
-      is_text = true;
-      kb = tk8 + (((long long)b * d.L + tt * 64) * d.H + h) * D;
-      vb = tv8t + ((long long)(b * d.H + h) * ntt + tt) * (D * 64);
-    }
 #pragma unroll
-    for (int r = 0; r < GPT; ++r) {
-      const int gi = tid + r * NT;
-      kreg[r] = make_uint4(0, 0, 0, 0);
-      vreg[r] = make_uint4(0, 0, 0, 0);
-      if (gi < KG) {
-        const int row = gi / (D / 16), col = (gi % (D / 16)) * 16;
-        if (row < valid) kreg[r] = *(const uint4*)(kb + (long long)row * kstride + col);
-        vreg[r] = *(const uint4*)(vb + gi * 16);
-      }
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < GPT; ++r) {
-      const int gi = tid + r * NT;
-      if (gi < KG) {
-        const int row = gi / (D / 16), col = (gi % (D / 16)) * 16;
-        *(uint4*)&Ks[buf][swz8<D>(row, col)] = kreg[r];
-        const int vrow = gi / 4, vcol = (gi % 4) * 16;
-        *(uint4*)&Vs[buf][swz8<64>(vrow, vcol)] = vreg[r];
-      }
-    }
-  };
-
-  fetch(0, cur_valid, cur_text);
-  stash(0);
-  __syncthreads();
+  for (int t0 = 0; t0 < NS - 1; ++t0)
+    if (t0 < total) issue(t0);
+  if (total >= NS - 1) wait_vmcnt<(NS - 2) * LPT>();
+  else wait_vmcnt<0>();
+  tile_barrier();
+  // P is rounded to e4m3 as P * 2^8.  The running maximum moves lazily, only
+  // when a tile maximum exceeds it by more than kSlack8 (log2 units), so
+  // P <= 2^kSlack8 and P * 2^8 <= 431 stays inside e4m3's finite range (448).
+  constexpr float kSlack8 = 0.75f;
   const float pscale = 256.f;
   for (int t = 0; t < total; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < total;
-    if (more) fetch(t + 1, nxt_valid, nxt_text);
+    const int buf = t % NS;
+    const bool more = t + NS - 1 < total;
+    if (more) issue(t + NS - 1);  // into the stage read at t - 1
+    const uint8_t *kb_unused, *vb_unused;
+    int cur_valid;
+    bool cur_text;
+    tile_info(t, kb_unused, vb_unused, cur_valid, cur_text);
 
     floatx16 sacc[2];
 #pragma unroll
@@ -332,36 +356,41 @@ __global__ __launch_bounds__(64 * NW) void k_attn_fp8(Dims d, const uint8_t* __r
           if (key >= cur_valid) sacc[kb][j] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    float mx = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * dq);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+      for (int j = (kb == 0 ? 2 : 0); j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
+    mx = xor32_max(mx) * dq;
+    const bool grow = mx > m_run + kSlack8;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < DB; ++i)
+      for (int i = 0; i < DB; ++i)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        oacc_v[i][j] *= alpha;
-        oacc_t[i][j] *= alpha;
-      }
+        for (int j = 0; j < 16; ++j) {
+          oacc_v[i][j] *= alpha;
+          oacc_t[i][j] *= alpha;
+        }
+    }
+    const float m_new = m_run;
     // P (x 2^8) to e4m3, packed in operand order e = 16*kb + j
     int pw[8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; j += 4) {
-        const float p0 = exp2f(fmaf(sacc[kb][j], dq, -m_new));
-        const float p1 = exp2f(fmaf(sacc[kb][j + 1], dq, -m_new));
-        const float p2 = exp2f(fmaf(sacc[kb][j + 2], dq, -m_new));
-        const float p3 = exp2f(fmaf(sacc[kb][j + 3], dq, -m_new));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j], dq, -m_new));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j + 1], dq, -m_new));
+        const float p2 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j + 2], dq, -m_new));
+        const float p3 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j + 3], dq, -m_new));
         l_run += (p0 + p1) + (p2 + p3);
-        int wv = cvt_e4m3x2<false>(p0 * pscale, p1 * pscale, 0);
-        wv = cvt_e4m3x2<true>(p2 * pscale, p3 * pscale, wv);
+        // 0 <= P * 2^8 <= 431: in range, no clamp needed
+        int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p0 * pscale, p1 * pscale, 0, false);
+        wv = __builtin_amdgcn_cvt_pk_fp8_f32(p2 * pscale, p3 * pscale, wv, true);
         pw[(16 * kb + j) / 4] = wv;
       }
     const i32x8 pf = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
@@ -374,13 +403,12 @@ __global__ __launch_bounds__(64 * NW) void k_attn_fp8(Dims d, const uint8_t* __r
       if (cur_text) oacc_t[i] = mfma_f8(a, pf, oacc_t[i]);
       else oacc_v[i] = mfma_f8(a, pf, oacc_v[i]);
     }
-    if (more) stash(buf ^ 1);
-    cur_valid = nxt_valid;
-    cur_text = nxt_text;
-    __syncthreads();
+    if (more) wait_vmcnt<(NS - 2) * LPT>();  // tile t + 1 landed
+    else wait_vmcnt<0>();
+    tile_barrier();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xor32_sum(l_run);
   const float cv = sv / (pscale * l_tot), ct = stv / (pscale * l_tot);
   if (row_ok) {
     float* op = os + (((long long)b * d.N + qtok) * d.H + h) * D;
@@ -429,18 +457,18 @@ hipError_t launch_quant_fp8(const Dims& d, const Bf16Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, int NW>
+template <int D, int NW, int NS>
 static hipError_t launch_attn8(const Dims& d, const Bf16Args& a, hipStream_t s) {
   constexpr int BM = 32 * NW;
   const long long grid = (long long)((d.n + BM - 1) / BM) * d.H * d.B * d.T;
-  hipLaunchKernelGGL((k_attn_fp8<D, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, d, a.q8, a.k8, a.v8t, a.tk8,
+  hipLaunchKernelGGL((k_attn_fp8<D, NW, NS>), dim3((unsigned)grid), dim3(64 * NW), 0, s, d, a.q8, a.k8, a.v8t, a.tk8,
                      a.tv8t, a.scales, a.scale_log2, a.os);
   return hipGetLastError();
 }
 
 hipError_t launch_softmax_fp8(const Dims& d, const Bf16Args& a, hipStream_t s) {
-  if (d.D == 128) return launch_attn8<128, 4>(d, a, s);
-  if (d.D == 64) return launch_attn8<64, 4>(d, a, s);
+  if (d.D == 128) return launch_attn8<128, 4, 4>(d, a, s);
+  if (d.D == 64) return launch_attn8<64, 4, 4>(d, a, s);
   return hipErrorInvalidValue;
 }
 

@@ -97,7 +97,15 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 // callers wait on explicitly (wait_vmcnt) before the tile_barrier that
 // publishes the tile.
 __device__ __forceinline__ void dma16(const void* gbase, unsigned voff, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase),
+  // gbase must be wave-uniform; readfirstlane moves it to scalar registers
+  // where the compiler cannot prove it uniform by itself.  readfirstlane
+  // returns a signed int: each half goes through unsigned before widening so
+  // that the low half is not sign-extended into the high one.
+  const unsigned long long g = (unsigned long long)(uintptr_t)gbase;
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)g);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(g >> 32));
+  const unsigned long long gs = (unsigned long long)lo | ((unsigned long long)hi << 32);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gs),
                "s"(__builtin_amdgcn_readfirstlane(lds))
                : "m0");
 }
