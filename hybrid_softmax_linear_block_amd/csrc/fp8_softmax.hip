@@ -14,6 +14,8 @@
 //                 a frame (or of the text) transposed, keys in the order the
 //                 P operand holds them (see slot_of_key)
 //   scales        [5][B][H] fp32 (q, k, v, text_k, text_v)
+#include <type_traits>
+
 #include "kernels_bf16.h"
 #include "work_items.h"
 
@@ -199,7 +201,7 @@ __device__ __forceinline__ int swz8(int row, int byte) {
 // loads NS - 1 tiles ahead (a tile is only 4 or 8 KB and carries little
 // arithmetic, so its load latency has to be covered by several tiles).
 template <int D, int NW, int NS>
-__global__ __launch_bounds__(64 * NW) void k_attn_fp8(Dims d, const uint8_t* __restrict__ q8,
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2))) void k_attn_fp8(Dims d, const uint8_t* __restrict__ q8,
                                                        const uint8_t* __restrict__ k8,
                                                        const uint8_t* __restrict__ v8t,
                                                        const uint8_t* __restrict__ tk8,
@@ -229,8 +231,8 @@ __global__ __launch_bounds__(64 * NW) void k_attn_fp8(Dims d, const uint8_t* __r
   // key sequence: every frame of S(f) as its own run of tiles, then the text
   const SoftRanges sr = soft_ranges(d.g, f);
   const int ntv = (d.n + 63) / 64, ntt = (d.L + 63) / 64;
-  int nframes = 0;
-  for (int r = 0; r < sr.n; ++r) nframes += sr.hi[r] - sr.lo[r];
+  // constant indices only, so sr stays in scalar registers
+  const int nframes = (sr.hi[0] - sr.lo[0]) + (sr.n > 1 ? sr.hi[1] - sr.lo[1] : 0) + (sr.n > 2 ? sr.hi[2] - sr.lo[2] : 0);
   const int total = nframes * ntv + ntt;
   const unsigned kstride = (unsigned)(d.H * D);  // bytes per token row of k8 / tk8
 
@@ -251,36 +253,46 @@ __global__ __launch_bounds__(64 * NW) void k_attn_fp8(Dims d, const uint8_t* __r
   }
   const unsigned ks_lds = lds_addr(Ks), vs_lds = lds_addr(Vs);
 
-  // tile t -> sources, valid keys, text or video
-  auto tile_info = [&](int t, const uint8_t*& kb, const uint8_t*& vb, int& valid, bool& is_text) {
-    if (t < nframes * ntv) {
-      int fi = t / ntv;
-      const int tt = t - fi * ntv;
-      int g = 0;
-      for (int r = 0; r < sr.n; ++r) {
-        const int len = sr.hi[r] - sr.lo[r];
-        if (fi < len) { g = sr.lo[r] + fi; break; }
-        fi -= len;
+  // Tile cursor: the video tiles of every frame of S(f) in order, then the
+  // text tiles.  All scalar; the next frame is g + 1 unless g closes one of
+  // the (at most three) frame ranges of S(f).
+  struct Cursor {
+    int g, tt, left_v, tt_t;  // frame, tile in frame, video tiles left, text tile
+  };
+  const int nvid = nframes * ntv;
+  auto cur_init = [&](Cursor& c) {
+    c.g = sr.lo[0];
+    c.tt = 0;
+    c.left_v = nvid;
+    c.tt_t = 0;
+  };
+  auto cur_next = [&](Cursor& c) {
+    if (c.left_v > 0) {
+      --c.left_v;
+      if (++c.tt == ntv) {
+        c.tt = 0;
+        int ng = c.g + 1;
+        if (sr.n > 1 && ng == sr.hi[0]) ng = sr.lo[1];
+        else if (sr.n > 2 && ng == sr.hi[1]) ng = sr.lo[2];
+        c.g = ng;
       }
-      valid = min(64, d.n - tt * 64);
-      is_text = false;
-      kb = k8 + (((long long)b * d.N + (long long)g * d.n + tt * 64) * d.H + h) * D;
-      vb = v8t + ((long long)(b * d.H + h) * d.T * ntv + (long long)g * ntv + tt) * (D * 64);
     } else {
-      const int tt = t - nframes * ntv;
-      valid = min(64, d.L - tt * 64);
-      is_text = true;
-      kb = tk8 + (((long long)b * d.L + tt * 64) * d.H + h) * D;
-      vb = tv8t + ((long long)(b * d.H + h) * ntt + tt) * (D * 64);
+      ++c.tt_t;
     }
   };
+  auto cur_valid = [&](const Cursor& c) { return c.left_v > 0 ? min(64, d.n - c.tt * 64) : min(64, d.L - c.tt_t * 64); };
   // Rows of K past the valid keys repeat the last valid row (their scores
   // are masked); the V^T tiles are padded by the quantiser.
-  auto issue = [&](int t) {
+  auto issue = [&](const Cursor& c, int t) {
     const uint8_t *kb, *vb;
-    int valid;
-    bool is_text;
-    tile_info(t, kb, vb, valid, is_text);
+    if (c.left_v > 0) {
+      kb = k8 + (((long long)b * d.N + (long long)c.g * d.n + c.tt * 64) * d.H + h) * D;
+      vb = v8t + ((long long)(b * d.H + h) * d.T * ntv + (long long)c.g * ntv + c.tt) * (D * 64);
+    } else {
+      kb = tk8 + (((long long)b * d.L + c.tt_t * 64) * d.H + h) * D;
+      vb = tv8t + ((long long)(b * d.H + h) * ntt + c.tt_t) * (D * 64);
+    }
+    const int valid = cur_valid(c);
     const int stg = t % NS;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
@@ -313,25 +325,35 @@ __global__ __launch_bounds__(64 * NW) void k_attn_fp8(Dims d, const uint8_t* __r
   for (int i = 0; i < DB; ++i) { oacc_v[i] = zero16(); oacc_t[i] = zero16(); }
   float m_run = -INFINITY, l_run = 0.f;
 
+  Cursor ci, cc;  // issue cursor (NS - 1 tiles ahead), compute cursor
+  cur_init(ci);
+  cur_init(cc);
 #pragma unroll
   for (int t0 = 0; t0 < NS - 1; ++t0)
-    if (t0 < total) issue(t0);
+    if (t0 < total) {
+      issue(ci, t0);
+      cur_next(ci);
+    }
   if (total >= NS - 1) wait_vmcnt<(NS - 2) * LPT>();
   else wait_vmcnt<0>();
   tile_barrier();
-  // P is rounded to e4m3 as P * 2^8.  The running maximum moves lazily, only
-  // when a tile maximum exceeds it by more than kSlack8 (log2 units), so
-  // P <= 2^kSlack8 and P * 2^8 <= 431 stays inside e4m3's finite range (448).
-  constexpr float kSlack8 = 0.75f;
-  const float pscale = 256.f;
-  for (int t = 0; t < total; ++t) {
+  // P is rounded to e4m3 as P * 2^8, the factor folded into the exponent.
+  // The running maximum moves lazily, only when a tile maximum exceeds it by
+  // more than kSlack8 (log2 units), so P <= 2^kSlack8 and P * 2^8 <= 431
+  // stays inside e4m3's finite range (448).  l accumulates P * 2^8.
+  constexpr float kSlack8 = 0.75f, kLogPscale = 8.f;
+
+  // One tile t of the video (TEXT = false) or text keys.
+  auto tile = [&](auto textc, int t, floatx16 (&oacc)[DB], float dq) {
+    constexpr bool TEXT = decltype(textc)::value;
     const int buf = t % NS;
     const bool more = t + NS - 1 < total;
-    if (more) issue(t + NS - 1);  // into the stage read at t - 1
-    const uint8_t *kb_unused, *vb_unused;
-    int cur_valid;
-    bool cur_text;
-    tile_info(t, kb_unused, vb_unused, cur_valid, cur_text);
+    if (more) {  // into the stage read at t - 1
+      issue(ci, t + NS - 1);
+      cur_next(ci);
+    }
+    const int valid = TEXT ? min(64, d.L - cc.tt_t * 64) : min(64, d.n - cc.tt * 64);
+    cur_next(cc);
 
     floatx16 sacc[2];
 #pragma unroll
@@ -346,22 +368,23 @@ __global__ __launch_bounds__(64 * NW) void k_attn_fp8(Dims d, const uint8_t* __r
         sacc[kb] = mfma_f8(a, qf[s], sacc[kb]);
       }
     }
-    const float dq = sq * (cur_text ? stk : sk) * sl2;  // logit scale in log2 units
-    if (cur_valid < 64) {
+    if (valid < 64) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-          if (key >= cur_valid) sacc[kb][j] = -INFINITY;
+          if (key >= valid) sacc[kb][j] = -INFINITY;
         }
     }
-    float mx = fmaxf(sacc[0][0], sacc[0][1]);
+    float m0 = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
+    float m1 = fmaxf(fmaxf(sacc[1][0], sacc[1][1]), sacc[1][2]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = (kb == 0 ? 2 : 0); j < 16; ++j) mx = fmaxf(mx, sacc[kb][j]);
-    mx = xor32_max(mx) * dq;
+    for (int j = 3; j < 15; j += 2) {
+      m0 = fmaxf(fmaxf(m0, sacc[0][j]), sacc[0][j + 1]);
+      m1 = fmaxf(fmaxf(m1, sacc[1][j]), sacc[1][j + 1]);
+    }
+    const float mx = xor32_max(fmaxf(fmaxf(m0, sacc[0][15]), fmaxf(m1, sacc[1][15]))) * dq;
     const bool grow = mx > m_run + kSlack8;
     if (__any(grow)) {
       const float m_new = grow ? mx : m_run;
@@ -376,23 +399,26 @@ __global__ __launch_bounds__(64 * NW) void k_attn_fp8(Dims d, const uint8_t* __r
           oacc_t[i][j] *= alpha;
         }
     }
-    const float m_new = m_run;
-    // P (x 2^8) to e4m3, packed in operand order e = 16*kb + j
+    // P * 2^8 to e4m3, packed in operand order e = 16*kb + j
+    const float moff = kLogPscale - m_run;
     int pw[8];
+    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; j += 4) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j], dq, -m_new));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j + 1], dq, -m_new));
-        const float p2 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j + 2], dq, -m_new));
-        const float p3 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j + 3], dq, -m_new));
-        l_run += (p0 + p1) + (p2 + p3);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j], dq, moff));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j + 1], dq, moff));
+        const float p2 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j + 2], dq, moff));
+        const float p3 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][j + 3], dq, moff));
+        ls0 += p0 + p1;
+        ls1 += p2 + p3;
         // 0 <= P * 2^8 <= 431: in range, no clamp needed
-        int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p0 * pscale, p1 * pscale, 0, false);
-        wv = __builtin_amdgcn_cvt_pk_fp8_f32(p2 * pscale, p3 * pscale, wv, true);
+        int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+        wv = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wv, true);
         pw[(16 * kb + j) / 4] = wv;
       }
+    l_run += ls0 + ls1;
     const i32x8 pf = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
 #pragma unroll
     for (int i = 0; i < DB; ++i) {
@@ -400,16 +426,18 @@ __global__ __launch_bounds__(64 * NW) void k_attn_fp8(Dims d, const uint8_t* __r
       const uint4 a0 = *(const uint4*)&Vs[buf][swz8<64>(row, 32 * half)];
       const uint4 a1 = *(const uint4*)&Vs[buf][swz8<64>(row, 32 * half + 16)];
       const i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-      if (cur_text) oacc_t[i] = mfma_f8(a, pf, oacc_t[i]);
-      else oacc_v[i] = mfma_f8(a, pf, oacc_v[i]);
+      oacc[i] = mfma_f8(a, pf, oacc[i]);
     }
     if (more) wait_vmcnt<(NS - 2) * LPT>();  // tile t + 1 landed
     else wait_vmcnt<0>();
     tile_barrier();
-  }
+  };
+  const float dqv = sq * sk * sl2, dqt = sq * stk * sl2;  // logit scales in log2 units
+  for (int t = 0; t < nvid; ++t) tile(std::integral_constant<bool, false>{}, t, oacc_v, dqv);
+  for (int t = nvid; t < total; ++t) tile(std::integral_constant<bool, true>{}, t, oacc_t, dqt);
 
   const float l_tot = xor32_sum(l_run);
-  const float cv = sv / (pscale * l_tot), ct = stv / (pscale * l_tot);
+  const float cv = sv / l_tot, ct = stv / l_tot;
   if (row_ok) {
     float* op = os + (((long long)b * d.N + qtok) * d.H + h) * D;
 #pragma unroll
