@@ -22,7 +22,7 @@ namespace hyb {
 // split of one frame, or one split of the text.  Output per slot (fp32):
 // S transposed [e][d] followed by z[d].
 template <int D>
-__global__ __launch_bounds__(256) void k_states_bf16(Dims d, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv,
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2))) void k_states_bf16(Dims d, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv,
                                                      int split, int ts, float* __restrict__ part, int slots) {
   constexpr int G = D / 8, GPT = (64 * G) / 256, DB = D / 32;
   constexpr int NB = (DB * DB) / 4;  // 32x32 output blocks per wave
@@ -51,10 +51,11 @@ __global__ __launch_bounds__(256) void k_states_bf16(Dims d, Tensor4 k, Tensor4 
     cnt = min(ts, d.L - p * ts);
   }
   if (cnt < 0) cnt = 0;
-  const Tensor4& kt = text ? tk : k;
-  const Tensor4& vt = text ? tv : v;
-  const bf16_t* kbase = (const bf16_t*)kt.p + tok_off(kt, b, t0, h);
-  const bf16_t* vbase = (const bf16_t*)vt.p + tok_off(vt, b, t0, h);
+  // select field by field (a select between the two structs would put them
+  // in scratch memory)
+  const long long kst = text ? tk.st : k.st, vst = text ? tv.st : v.st;
+  const bf16_t* kbase = text ? (const bf16_t*)tk.p + tok_off(tk, b, t0, h) : (const bf16_t*)k.p + tok_off(k, b, t0, h);
+  const bf16_t* vbase = text ? (const bf16_t*)tv.p + tok_off(tv, b, t0, h) : (const bf16_t*)v.p + tok_off(v, b, t0, h);
 
   // block assignment: wave covers output blocks (mb, nb) = blk / DB, blk % DB
   floatx16 acc[NB];
@@ -65,20 +66,26 @@ __global__ __launch_bounds__(256) void k_states_bf16(Dims d, Tensor4 k, Tensor4 
   for (int i = 0; i < 8; ++i) zacc[i] = 0.f;
 
   const int ntile = (cnt + 63) >> 6;
-  for (int tile = 0; tile < ntile; ++tile) {
+  // tile loads go to registers one tile ahead: the next tile's loads are in
+  // flight while the current tile is multiplied
+  uint4 kr[GPT], vr[GPT];
+  auto load = [&](int tile) {
     const int valid = min(64, cnt - tile * 64);
-    uint4 kr[GPT], vr[GPT];
 #pragma unroll
     for (int r = 0; r < GPT; ++r) {
       const int gi = tid + r * 256, row = gi / G, col = (gi % G) * 8;
       if (row < valid) {
-        kr[r] = ldg16(kbase + (long long)(tile * 64 + row) * kt.st + col);
-        vr[r] = ldg16(vbase + (long long)(tile * 64 + row) * vt.st + col);
+        kr[r] = ldg16(kbase + (long long)(tile * 64 + row) * kst + col);
+        vr[r] = ldg16(vbase + (long long)(tile * 64 + row) * vst + col);
       } else {
         kr[r] = make_uint4(0, 0, 0, 0);
         vr[r] = make_uint4(0, 0, 0, 0);
       }
     }
+  };
+  if (ntile > 0) load(0);
+  for (int tile = 0; tile < ntile; ++tile) {
+    const int valid = min(64, cnt - tile * 64);
     __syncthreads();  // previous tile's reads are done
 #pragma unroll
     for (int r = 0; r < GPT; ++r) {
@@ -98,6 +105,7 @@ __global__ __launch_bounds__(256) void k_states_bf16(Dims d, Tensor4 k, Tensor4 
       *(uint4*)&Vs[SW::off(row, col)] = vr[r];
     }
     __syncthreads();
+    if (tile + 1 < ntile) load(tile + 1);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int r0 = kk * 16 + 4 * half + (j16 >> 2);
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(256) void k_scan_bf16(Dims d, const float* __restri
 // phi(q).z + eps is a per-lane dot product.  Also emits sum_e O_l^2 per
 // (token, head) for the RMSNorm.
 template <int D>
-__global__ __launch_bounds__(256) void k_readout_bf16(Dims d, Tensor4 q, const bf16_t* __restrict__ chi,
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2))) void k_readout_bf16(Dims d, Tensor4 q, const bf16_t* __restrict__ chi,
                                                       const bf16_t* __restrict__ clo, const float* __restrict__ cz,
                                                       float eps, int tt, float* __restrict__ ol,
                                                       float* __restrict__ ss) {
@@ -275,7 +283,9 @@ __global__ __launch_bounds__(256) void k_readout_bf16(Dims d, Tensor4 q, const b
     const float inv = 1.f / (den + eps);
     float sq = 0.f;
     float* op = ol + (((long long)b * d.N + tok) * d.H + h) * D;
-#pragma unroll
+    // one 32-row block of the state at a time (keeps the operand reads of a
+    // single block in flight instead of all of them)
+#pragma unroll 1
     for (int i = 0; i < DB; ++i) {
       floatx16 acc = zero16();
       const int row = i * 32 + l32;
@@ -338,7 +348,7 @@ __global__ __launch_bounds__(256) void k_rms_rinv(const float* __restrict__ ss, 
 }
 
 hipError_t launch_readout_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
-  const int tt = 256;
+  const int tt = 512;
   const long long grid = (long long)d.B * d.H * d.T * ((d.n + tt - 1) / tt);
   if (d.D == 128)
     hipLaunchKernelGGL(k_readout_bf16<128>, dim3((unsigned)grid), dim3(256), 0, s, d, a.q, a.comb_hi, a.comb_lo,
