@@ -45,7 +45,7 @@ struct GemmArgs {
 // k-tile t is multiplied.  The k loop is unrolled by ST so that every LDS
 // address is a per-lane base plus an immediate, and the DMA source is a
 // scalar base (bumped per k-tile) plus a fixed per-lane offset.
-template <int WM, int WN, int WTM, int WFN, int BK, int ST, int WPE, int EPI>
+template <int WM, int WN, int WTM, int WFN, int BK, int ST, int WPE, int EPI, int GM = 1>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void k_gemm_bf16(GemmArgs g) {
@@ -65,9 +65,16 @@ void k_gemm_bf16(GemmArgs g) {
   const int l32 = lane & 31, half = lane >> 5;
   const int wm = wave % WM, wn = wave / WM;
   const int ntn = g.N / BN;
+  // Each XCD takes a contiguous range of tiles (xcd_remap), walked in groups
+  // of GM token tiles: the workgroups running together on an XCD share GM
+  // rows of A and a run of weight tiles, so both stay in its L2.
   const unsigned wid = xcd_remap(blockIdx.x, gridDim.x);
-  const long long m0 = (long long)(wid / ntn) * BM;
-  const int n0 = (int)(wid % ntn) * BN;
+  const unsigned ntm = (unsigned)((g.M + BM - 1) / BM);
+  const unsigned per_group = (unsigned)GM * (unsigned)ntn;
+  const unsigned grp = wid / per_group, in = wid % per_group;
+  const unsigned gm0 = grp * GM, gsz = min((unsigned)GM, ntm - gm0);
+  const long long m0 = (long long)(gm0 + in % gsz) * BM;
+  const int n0 = (int)(in / gsz) * BN;
 
   floatx16 acc[WFN][WTM];
 #pragma unroll
@@ -260,15 +267,15 @@ hipError_t launch_weights_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) 
   return hipGetLastError();
 }
 
-template <int WM, int WN, int WTM, int WFN, int BK, int ST, int WPE, int EPI>
+template <int WM, int WN, int WTM, int WFN, int BK, int ST, int WPE, int EPI, int GM = 1>
 static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   constexpr int BM = WM * WTM * 32, BN = WN * WFN * 32;
   if (g.N % BN != 0 || g.K % BK != 0 || (EPI == EPI_GATE && g.hid % BN != 0)) return hipErrorInvalidValue;
   // 32-bit per-lane DMA offsets: a tile's rows span < 4 GiB
   if ((long long)BM * g.K * 2 >= (1LL << 32) || (long long)BN * g.K * 2 >= (1LL << 32)) return hipErrorInvalidValue;
   const long long grid = ((g.M + BM - 1) / BM) * (g.N / BN);
-  hipLaunchKernelGGL((k_gemm_bf16<WM, WN, WTM, WFN, BK, ST, WPE, EPI>), dim3((unsigned)grid), dim3(64 * WM * WN), 0,
-                     s, g);
+  hipLaunchKernelGGL((k_gemm_bf16<WM, WN, WTM, WFN, BK, ST, WPE, EPI, GM>), dim3((unsigned)grid),
+                     dim3(64 * WM * WN), 0, s, g);
   return hipGetLastError();
 }
 
@@ -292,7 +299,7 @@ hipError_t launch_gate_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s
   g.rmsw = a.rmsw;
   g.ap = a.ap;
   g.gates_dbg = a.gates_dbg;
-  if (d.hid % 256 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_GATE>(g, s);
+  if (d.hid % 256 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_GATE, 4>(g, s);
   if (d.hid % 128 == 0) return launch_gemm<2, 2, 4, 2, 32, 3, 2, EPI_GATE>(g, s);
   return launch_gemm<2, 2, 4, 1, 32, 3, 2, EPI_GATE>(g, s);  // hid multiple of 64 only
 }
@@ -306,7 +313,7 @@ hipError_t launch_out_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s)
   g.x = a.x;
   g.y = a.y;
   g.delta_dbg = a.delta_dbg;
-  if (g.N % 256 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_OUT>(g, s);
+  if (g.N % 256 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_OUT, 2>(g, s);
   if (g.N % 128 == 0) return launch_gemm<2, 2, 4, 2, 32, 3, 2, EPI_OUT>(g, s);
   return launch_gemm<2, 2, 4, 1, 32, 3, 2, EPI_OUT>(g, s);
 }
