@@ -68,7 +68,8 @@ def stage_work(w, soft):
         "softmax": ("mfma", wc["softmax_flop"]),
         "states": ("hbm", 2 * B * (N + L) * hid * es + B * H * (T + 1) * st),
         "scan": ("hbm", B * H * (T + 1) * st + B * H * T * (2 * D * D * 2 + D * 4)),
-        "readout": ("hbm", B * N * hid * es + B * H * T * (2 * D * D * 2 + D * 4) + B * N * hid * 4 + B * N * H * 4),
+        # reads q and the combined states, writes O_l (fp16) and the per-head sums of squares
+        "readout": ("hbm", B * N * hid * es + B * H * T * (2 * D * D * 2 + D * 4) + B * N * hid * 2 + B * N * H * 4),
         "gate": ("mfma", gemm_flop),
         "out": ("mfma", gemm_flop),
     }

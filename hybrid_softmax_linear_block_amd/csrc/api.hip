@@ -97,8 +97,9 @@ Plan make_plan(const hyb::Dims& d, hyb_dtype act, hyb_dtype soft) {
   Plan p;
   size_t sz[W_COUNT] = {0};
   const size_t BN = (size_t)d.B * d.N, hid = d.hid, D = d.D, BH = (size_t)d.B * d.H;
-  sz[W_OS] = BN * hid * 4;
-  sz[W_OL] = BN * hid * 4;
+  // branch outputs: fp32 on the float32 path, fp16 on the bf16 path
+  sz[W_OS] = BN * hid * (act == HYB_F32 ? 4 : 2);
+  sz[W_OL] = BN * hid * (act == HYB_F32 ? 4 : 2);
   sz[W_SS] = BN * d.H * 4;
   if (act == HYB_F32) {
     sz[W_STATES] = BH * (d.T + 1) * D * (D + 1) * 4;
@@ -299,8 +300,8 @@ hyb_status hyb_attn_forward(const hyb_layout* layout, hyb_dtype act, hyb_dtype s
     a.scale_log2 = sl2;
     a.eps = eps;
     a.fp8 = soft == HYB_FP8_E4M3;
-    a.os = (float*)(ws + plan.off[W_OS]);
-    a.ol = (float*)(ws + plan.off[W_OL]);
+    a.os = (uint16_t*)(ws + plan.off[W_OS]);
+    a.ol = (uint16_t*)(ws + plan.off[W_OL]);
     a.ss = (float*)(ws + plan.off[W_SS]);
     a.rinv = (float*)(ws + plan.off[W_RINV]);
     a.part = (float*)(ws + plan.off[W_PART]);
@@ -330,11 +331,17 @@ hyb_status hyb_attn_forward(const hyb_layout* layout, hyb_dtype act, hyb_dtype s
     he = hyb::run_bf16(d, a, s);
     if (he == hipSuccess && dbg && dbg->scales && a.fp8)
       he = hipMemcpyAsync(dbg->scales, a.scales, 5 * (size_t)d.B * d.H * 4, hipMemcpyDeviceToDevice, s);
+    const long long nel = (long long)d.B * d.N * d.hid;
+    if (he == hipSuccess && dbg && dbg->o_soft) he = hyb::launch_f16_to_f32(a.os, (float*)dbg->o_soft, nel, s);
+    if (he == hipSuccess && dbg && dbg->o_lin) he = hyb::launch_f16_to_f32(a.ol, (float*)dbg->o_lin, nel, s);
   }
-  if (he == hipSuccess && dbg && dbg->o_soft)
-    he = hipMemcpyAsync(dbg->o_soft, ws + plan.off[W_OS], (size_t)d.B * d.N * d.hid * 4, hipMemcpyDeviceToDevice, s);
-  if (he == hipSuccess && dbg && dbg->o_lin)
-    he = hipMemcpyAsync(dbg->o_lin, ws + plan.off[W_OL], (size_t)d.B * d.N * d.hid * 4, hipMemcpyDeviceToDevice, s);
+  if (act == HYB_F32) {
+    const size_t bytes = (size_t)d.B * d.N * d.hid * 4;
+    if (he == hipSuccess && dbg && dbg->o_soft)
+      he = hipMemcpyAsync(dbg->o_soft, ws + plan.off[W_OS], bytes, hipMemcpyDeviceToDevice, s);
+    if (he == hipSuccess && dbg && dbg->o_lin)
+      he = hipMemcpyAsync(dbg->o_lin, ws + plan.off[W_OL], bytes, hipMemcpyDeviceToDevice, s);
+  }
   if (he != hipSuccess) return fail(HYB_ERR_HIP, "HIP error: %s", hipGetErrorString(he));
   return HYB_OK;
 }

@@ -295,9 +295,10 @@ __device__ __forceinline__ void pv_tile(floatx16 (&oacc)[D / 32], const bf16_t* 
   }
 }
 
-// Normalise O^T by the row sum and store fp32 [B*N][H][D].
+// Normalise O^T by the row sum and store fp16 [B*N][H][D].  O is a convex
+// combination of value rows, so it lies in the fp16 range whenever V does.
 template <int D>
-__device__ __forceinline__ void store_rows(const floatx16 (&oacc)[D / 32], float l_run, bool row_ok, float* op,
+__device__ __forceinline__ void store_rows(const floatx16 (&oacc)[D / 32], float l_run, bool row_ok, uint16_t* op,
                                            int half) {
   const float l_tot = xor32_sum(l_run);
   const float inv = 1.f / l_tot;
@@ -307,8 +308,8 @@ __device__ __forceinline__ void store_rows(const floatx16 (&oacc)[D / 32], float
 #pragma unroll
     for (int jg = 0; jg < 4; ++jg) {
       const int d0 = i * 32 + 8 * jg + 4 * half;
-      *(float4*)(op + d0) = make_float4(oacc[i][4 * jg] * inv, oacc[i][4 * jg + 1] * inv,
-                                        oacc[i][4 * jg + 2] * inv, oacc[i][4 * jg + 3] * inv);
+      store_f16x4(op + d0, oacc[i][4 * jg] * inv, oacc[i][4 * jg + 1] * inv, oacc[i][4 * jg + 2] * inv,
+                  oacc[i][4 * jg + 3] * inv);
     }
 }
 
@@ -326,7 +327,7 @@ __device__ __forceinline__ void store_rows(const floatx16 (&oacc)[D / 32], float
 template <int D, int KB, int NW, int PF>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 void k_attn_bf16_sp(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv, float sl2,
-                    float* __restrict__ os) {
+                    uint16_t* __restrict__ os) {
   constexpr int BM = 32 * NW, KS = D / 16, DB = D / 32, BN = 32 * KB;
   constexpr int NMF = KB * KS;  // MFMAs per S tile (= per P V tile)
   using Ldr = TileLoader<D, NW, KB>;

@@ -22,6 +22,20 @@ enum { ST_WEIGHTS, ST_QUANT, ST_SOFTMAX, ST_STATES, ST_SCAN, ST_READOUT, ST_GATE
 
 static hipError_t nothing() { return hipSuccess; }
 
+__global__ __launch_bounds__(256) void k_f16_to_f32(const uint16_t* __restrict__ src, float* __restrict__ dst,
+                                                    long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = (float)__builtin_bit_cast(_Float16, src[i]);
+}
+
+hipError_t launch_f16_to_f32(const uint16_t* src, float* dst, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const long long blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_f16_to_f32, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
 hipError_t run_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
   HYB_STAGE(ST_WEIGHTS, launch_weights_bf16(d, a, s));
   if (a.fp8) {

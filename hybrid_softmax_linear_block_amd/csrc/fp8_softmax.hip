@@ -207,7 +207,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
                                                        const uint8_t* __restrict__ tk8,
                                                        const uint8_t* __restrict__ tv8t,
                                                        const float* __restrict__ scales, float sl2,
-                                                       float* __restrict__ os) {
+                                                       uint16_t* __restrict__ os) {
   constexpr int BM = 32 * NW;
   constexpr int KSTEP = D / 64;      // 64-deep k-steps of Q K^T
   constexpr int DB = D / 32;         // d blocks of O^T
@@ -439,7 +439,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
   const float l_tot = xor32_sum(l_run);
   const float cv = sv / l_tot, ct = stv / l_tot;
   if (row_ok) {
-    float* op = os + (((long long)b * d.N + qtok) * d.H + h) * D;
+    uint16_t* op = os + (((long long)b * d.N + qtok) * d.H + h) * D;
 #pragma unroll
     for (int i = 0; i < DB; ++i)
 #pragma unroll
@@ -450,7 +450,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
         o4.y = oacc_v[i][4 * jg + 1] * cv + oacc_t[i][4 * jg + 1] * ct;
         o4.z = oacc_v[i][4 * jg + 2] * cv + oacc_t[i][4 * jg + 2] * ct;
         o4.w = oacc_v[i][4 * jg + 3] * cv + oacc_t[i][4 * jg + 3] * ct;
-        *(float4*)(op + d0) = o4;
+        store_f16x4(op + d0, o4.x, o4.y, o4.z, o4.w);
       }
   }
 }

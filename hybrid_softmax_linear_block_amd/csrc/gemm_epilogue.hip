@@ -28,7 +28,8 @@ struct GemmArgs {
   int N, K;
   int hid, H;
   // gate epilogue
-  const float *os, *ol, *rinv;
+  const uint16_t *os, *ol;  // fp16 branch outputs [M][hid]
+  const float* rinv;
   const bf16_t* rmsw;
   uint16_t* ap;
   float* gates_dbg;
@@ -179,7 +180,7 @@ void k_gemm_bf16(GemmArgs g) {
 #pragma unroll
         for (int f = 0; f < WFN; ++f)
 #pragma unroll
-          for (int jg = 0; jg < 4; ++jg) val[f][jg] = *(const float4*)(g.os + m * g.hid + nw + 32 * f + 8 * jg);
+          for (int jg = 0; jg < 4; ++jg) val[f][jg] = load_f16x4(g.os + m * g.hid + nw + 32 * f + 8 * jg);
       } else {
         const float rinv = g.rinv[m];
 #pragma unroll
@@ -187,7 +188,7 @@ void k_gemm_bf16(GemmArgs g) {
 #pragma unroll
           for (int jg = 0; jg < 4; ++jg) {
             const int c = nw - g.hid + 32 * f + 8 * jg;
-            const float4 o = *(const float4*)(g.ol + m * g.hid + c);
+            const float4 o = load_f16x4(g.ol + m * g.hid + c);
             const uint2 wv = *(const uint2*)(g.rmsw + c);
             val[f][jg].x = o.x * __uint_as_float(wv.x << 16) * rinv;
             val[f][jg].y = o.y * __uint_as_float(wv.x & 0xffff0000u) * rinv;

@@ -22,8 +22,8 @@ struct Bf16Args {
   float scale_log2, eps;
   bool fp8;
   // workspace
-  float* os;              // [B*N][hid] fp32 softmax-branch output
-  float* ol;              // [B*N][hid] fp32 linear-branch output
+  uint16_t* os;           // [B*N][hid] fp16 softmax-branch output
+  uint16_t* ol;           // [B*N][hid] fp16 linear-branch output
   float* ss;              // [B*N][H]   sum of squares of O_l per head
   float* rinv;            // [B*N]      1 / sqrt(mean over hid of O_l^2 + eps)
   float* part;            // [B*H][slots][D*D+D] partial frame states: S^T [e][d], then z[d]
@@ -47,6 +47,8 @@ struct Bf16Args {
 };
 
 hipError_t run_bf16(const Dims& d, const Bf16Args& a, hipStream_t s);
+// fp16 bits -> float32 (debug copies of the fp16 branch outputs)
+hipError_t launch_f16_to_f32(const uint16_t* src, float* dst, long long n, hipStream_t s);
 
 // Workspace sizes (bytes) of each buffer in the plans above.
 struct WsPlan {

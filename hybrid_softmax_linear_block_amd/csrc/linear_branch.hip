@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256) void k_scan_bf16(Dims d, const float* __restri
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2))) void k_readout_bf16(Dims d, Tensor4 q, const bf16_t* __restrict__ chi,
                                                       const bf16_t* __restrict__ clo, const float* __restrict__ cz,
-                                                      float eps, int tt, float* __restrict__ ol,
+                                                      float eps, int tt, uint16_t* __restrict__ ol,
                                                       float* __restrict__ ss) {
   constexpr int G = D / 8, KS = D / 16, DB = D / 32;
   using SW = Swz<D>;
@@ -282,7 +282,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
     den += __shfl_xor(den, 32);
     const float inv = 1.f / (den + eps);
     float sq = 0.f;
-    float* op = ol + (((long long)b * d.N + tok) * d.H + h) * D;
+    uint16_t* op = ol + (((long long)b * d.N + tok) * d.H + h) * D;
     // one 32-row block of the state at a time (keeps the operand reads of a
     // single block in flight instead of all of them)
 #pragma unroll 1
@@ -303,7 +303,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
         float4 o4 = make_float4(acc[4 * jg] * inv, acc[4 * jg + 1] * inv, acc[4 * jg + 2] * inv,
                                 acc[4 * jg + 3] * inv);
         sq += o4.x * o4.x + o4.y * o4.y + o4.z * o4.z + o4.w * o4.w;
-        if (ok) *(float4*)(op + e0) = o4;
+        if (ok) store_f16x4(op + e0, o4.x, o4.y, o4.z, o4.w);
       }
     }
     sq += __shfl_xor(sq, 32);

@@ -36,6 +36,17 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return (uint32_t)f32_to_f16_sat(lo) | ((uint32_t)f32_to_f16_sat(hi) << 16);
 }
 
+// Four floats -> four saturated fp16 in one 8-byte store, and back.
+__device__ __forceinline__ void store_f16x4(uint16_t* p, float a, float b, float c, float d) {
+  *(uint2*)p = make_uint2(pack_f16x2(a, b), pack_f16x2(c, d));
+}
+__device__ __forceinline__ float4 load_f16x4(const uint16_t* p) {
+  typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
+  const uint2 u = *(const uint2*)p;
+  const half2_t lo = __builtin_bit_cast(half2_t, u.x), hi = __builtin_bit_cast(half2_t, u.y);
+  return make_float4((float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]);
+}
+
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 
 // Two transposing 8-byte LDS reads -> one bf16x8 MFMA operand.

@@ -63,8 +63,8 @@ def test_table_validation():
 def test_workspace_size_and_dtype_rules():
     lay = api.Layout(1, 15, 4032, 512, 24, 128)
     n = api.workspace_size(lay, "bf16")
-    # fp32 branch outputs (2 x 743 MB) + bf16 A' (743 MB) dominate
-    assert 2.2e9 < n < 3.0e9
+    # fp16 branch outputs (2 x 372 MB) + fp16 A' (743 MB) dominate
+    assert 1.5e9 < n < 2.0e9
     assert api.workspace_size(lay, "bf16", "fp8") > n
     with pytest.raises(api.HybError) as e:
         api.workspace_size(lay, "f32", "fp8")
