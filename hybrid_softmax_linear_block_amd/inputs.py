@@ -119,6 +119,20 @@ def make_inputs(w: Workload, seed=None):
     return out
 
 
+def make_projection_weights(w: Workload, seed=None):
+    """Seeded Q/K/V projection weights w_q, w_k, w_v [hid, hid] ([in][out]),
+    ~ N(0, weight_std^2), exact in ``w.act``; drawn from PCG64(seed + 3000) so
+    that the layer inputs of ``make_inputs`` are unchanged."""
+    seed = w.seed if seed is None else seed
+    g = np.random.Generator(np.random.PCG64(seed + 3000))
+    hid = w.hidden
+    out = {}
+    for name in ("w_q", "w_k", "w_v"):
+        a = g.standard_normal(size=(hid, hid), dtype=np.float32) * np.float32(w.weight_std)
+        out[name] = _store(a, w.act)
+    return out
+
+
 def sample_tokens(w: Workload, per_frame=64, seed=None):
     """Seeded sorted sample of video-token indices: ``per_frame`` tokens from
     every frame, always including each frame's first and last token."""

@@ -26,9 +26,15 @@ Parity status per function (what pins it, in ``tests/test_oracle_*.py``):
                                       constant-V closed form, phi closed forms.
   hybrid.epilogue                     pinned: zero/one-hot weight closed forms,
                                       RMSNorm scope closed form.
+  projection.project / qkv_projection pinned: one-hot (non-symmetric
+                                      permutation) and diagonal weights, head
+                                      split, a hand-computed example.
+  projection.absmax_per_head          pinned: constructed tensors.
+  projection.round_bf16               pinned: torch bfloat16 conversion.
   Anchor frames as queries (they attend to every frame): parity unpinned --
   the article says only that anchors interact with the other frames.
 """
 from .layout import Layout, frame_sets, tables  # noqa: F401
 from .hybrid import (phi, softmax_branch, linear_states, linear_branch,  # noqa: F401
                      epilogue, hybrid_forward)
+from . import projection  # noqa: F401
