@@ -39,7 +39,7 @@ class _Debug(ctypes.Structure):
                                                 "stage_events")]
 
 
-STAGES = ("weights", "quant", "softmax", "states", "scan", "readout", "gate", "out")
+STAGES = ("weights", "quant", "softmax", "states", "scan", "readout", "gate", "out", "qkv")
 
 
 @dataclass(frozen=True)
@@ -91,6 +91,18 @@ def load(path=None):
     lib.hyb_attn_forward.argtypes = (
         [ctypes.POINTER(_Layout), ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         + [_Tensor] * 5 + [ctypes.c_void_p] * 5 + [ctypes.c_float, ctypes.c_float]
+        + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(_Debug)])
+    lib.hyb_qkv_workspace_size.restype = ctypes.c_int
+    lib.hyb_qkv_workspace_size.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(ctypes.c_size_t)]
+    lib.hyb_qkv_project.restype = ctypes.c_int
+    lib.hyb_qkv_project.argtypes = ([ctypes.POINTER(_Layout)] + [ctypes.c_void_p] * 8
+                                    + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
+    lib.hyb_block_workspace_size.restype = ctypes.c_int
+    lib.hyb_block_workspace_size.argtypes = [ctypes.POINTER(_Layout), ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    lib.hyb_block_forward.restype = ctypes.c_int
+    lib.hyb_block_forward.argtypes = (
+        [ctypes.POINTER(_Layout), ctypes.c_int] + [ctypes.c_void_p] * 4 + [_Tensor] * 2 + [ctypes.c_void_p] * 5
+        + [ctypes.c_float, ctypes.c_float]
         + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(_Debug)])
     lib.hyb_status_string.restype = ctypes.c_char_p
     lib.hyb_status_string.argtypes = [ctypes.c_int]
@@ -185,6 +197,84 @@ def forward(lay: Layout, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin, w_
     return y
 
 
+def qkv_workspace_size(lay: Layout):
+    lib = load()
+    n = ctypes.c_size_t(0)
+    c = lay.c()
+    _check(lib.hyb_qkv_workspace_size(ctypes.byref(c), ctypes.byref(n)))
+    return n.value
+
+
+def qkv_project(lay: Layout, x, w_q, w_k, w_v, q=None, k=None, v=None, absmax=None, workspace=None,
+                stream=None):
+    """q, k, v = x W_q, x W_k, x W_v (bf16) by libhybattn, plus optionally the
+    per-(tensor, batch, head) absmax of the outputs into ``absmax`` (an int32
+    device tensor [3, B, H] receiving float32 bit patterns).  Returns
+    (q, k, v) as [B, N, H, D] tensors."""
+    import torch
+    lib = load()
+    for t in (x, w_q, w_k, w_v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("x and the weights must be contiguous bfloat16 device tensors")
+    B, N, H, D = lay.batch, lay.frames * lay.tokens_per_frame, lay.heads, lay.head_dim
+    outs = []
+    for t in (q, k, v):
+        if t is None:
+            t = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=x.device)
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.numel() != B * N * H * D:
+            raise ValueError("q, k, v must be contiguous bfloat16 [B, N, H, D]")
+        outs.append(t)
+    if absmax is not None and (absmax.dtype != torch.int32 or absmax.numel() != 3 * B * H):
+        raise ValueError("absmax must be an int32 tensor of 3*B*H elements")
+    if workspace is None:
+        workspace = torch.empty(qkv_workspace_size(lay), dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    c = lay.c()
+    _check(lib.hyb_qkv_project(ctypes.byref(c), x.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), w_v.data_ptr(),
+                               outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), _ptr(absmax),
+                               workspace.data_ptr(), workspace.numel(), stream))
+    return tuple(outs)
+
+
+def block_workspace_size(lay: Layout, soft=None):
+    lib = load()
+    n = ctypes.c_size_t(0)
+    c = lay.c()
+    _check(lib.hyb_block_workspace_size(ctypes.byref(c), DTYPES[soft or "bf16"], ctypes.byref(n)))
+    return n.value
+
+
+def block_forward(lay: Layout, x, w_q, w_k, w_v, text_k, text_v, w_gate_soft, w_gate_lin, w_out_soft,
+                  w_out_lin, rms_weight, soft=None, softmax_scale=0.0, eps=1e-6, y=None, workspace=None,
+                  debug=None, stream=None):
+    """The layer with its Q/K/V projection (bf16 activations): y = x + delta
+    with q, k, v = x W_q, x W_k, x W_v computed on the GPU.  Arguments as in
+    ``forward`` plus the projection weights [hid, hid] ([in][out])."""
+    import torch
+    lib = load()
+    for t in (x, w_q, w_k, w_v, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin, rms_weight):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("x, weights and rms_weight must be contiguous bfloat16 device tensors")
+    if y is None:
+        y = torch.empty_like(x)
+    if workspace is None:
+        workspace = torch.empty(block_workspace_size(lay, soft), dtype=torch.uint8, device=x.device)
+    dbg = None
+    if debug:
+        dbg = _Debug(*([_ptr(debug.get(n)) for n in ("o_soft", "o_lin", "delta_f32", "gates", "scales")]
+                       + [debug.get("stage_events")]))
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    c = lay.c()
+    _check(lib.hyb_block_forward(
+        ctypes.byref(c), DTYPES[soft or "bf16"], x.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), w_v.data_ptr(),
+        _tensor4(text_k), _tensor4(text_v), w_gate_soft.data_ptr(), w_gate_lin.data_ptr(), w_out_soft.data_ptr(),
+        w_out_lin.data_ptr(), rms_weight.data_ptr(), float(softmax_scale), float(eps), y.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), stream, ctypes.byref(dbg) if dbg is not None else None))
+    return y
+
+
 class StageTimer:
     """2 HIP events per stage, recorded by the library around each stage on
     the call's stream; ``elapsed_ms()`` returns per-stage milliseconds of the
@@ -223,9 +313,10 @@ class StageTimer:
         return out
 
     def span_ms(self):
-        """Milliseconds from the start of the first stage to the end of the
-        last one (the whole forward on the GPU)."""
-        a, b = self.events[0], self.events[2 * len(STAGES) - 1]
+        """Milliseconds from the first recorded event (the projection stage,
+        recorded first, empty for ``forward``) to the end of the output GEMM:
+        the whole call on the GPU."""
+        a, b = self.events[2 * STAGES.index("qkv")], self.events[2 * STAGES.index("out") + 1]
         self._hip.hipEventSynchronize(b)
         ms = ctypes.c_float(0)
         if self._hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:

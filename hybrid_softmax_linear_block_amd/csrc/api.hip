@@ -217,12 +217,19 @@ hyb_status hyb_workspace_size(const hyb_layout* layout, hyb_dtype act, hyb_dtype
   return HYB_OK;
 }
 
-hyb_status hyb_attn_forward(const hyb_layout* layout, hyb_dtype act, hyb_dtype soft, const void* x, hyb_tensor q,
-                            hyb_tensor k, hyb_tensor v, hyb_tensor text_k, hyb_tensor text_v,
-                            const void* w_gate_soft, const void* w_gate_lin, const void* w_out_soft,
-                            const void* w_out_lin, const void* rms_weight, float softmax_scale, float eps, void* y,
-                            void* workspace, size_t workspace_bytes, void* stream, const hyb_debug* dbg) {
-  g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+
+// The layer.  after_projection: called by hyb_block_forward, whose projection
+// already ran (its stage events are recorded) and, with fp8, already wrote the
+// absmax of q, k, v into the workspace.
+hyb_status attn_forward_impl(const hyb_layout* layout, hyb_dtype act, hyb_dtype soft, const void* x, hyb_tensor q,
+                             hyb_tensor k, hyb_tensor v, hyb_tensor text_k, hyb_tensor text_v,
+                             const void* w_gate_soft, const void* w_gate_lin, const void* w_out_soft,
+                             const void* w_out_lin, const void* rms_weight, float softmax_scale, float eps, void* y,
+                             void* workspace, size_t workspace_bytes, void* stream, const hyb_debug* dbg,
+                             bool after_projection) {
   hyb_status st = check_layout(layout, false);
   if (st != HYB_OK) return st;
   st = check_dtypes(layout, act, soft);
@@ -267,7 +274,13 @@ hyb_status hyb_attn_forward(const hyb_layout* layout, hyb_dtype act, hyb_dtype s
   const float tau = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)d.D);
   const float sl2 = tau * 1.4426950408889634f;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t he;
+  hipError_t he = hipSuccess;
+  if (dbg && dbg->stage_events && !after_projection) {  // no projection stage here: empty interval
+    hipEvent_t* ev = (hipEvent_t*)dbg->stage_events;
+    he = hipEventRecord(ev[2 * HYB_STAGE_QKV], s);
+    if (he == hipSuccess) he = hipEventRecord(ev[2 * HYB_STAGE_QKV + 1], s);
+    if (he != hipSuccess) return fail(HYB_ERR_HIP, "HIP error: %s", hipGetErrorString(he));
+  }
   if (act == HYB_F32) {
     hyb::F32Args a;
     a.q = t4(q); a.k = t4(k); a.v = t4(v);
@@ -300,6 +313,7 @@ hyb_status hyb_attn_forward(const hyb_layout* layout, hyb_dtype act, hyb_dtype s
     a.scale_log2 = sl2;
     a.eps = eps;
     a.fp8 = soft == HYB_FP8_E4M3;
+    a.qkv_absmax_ready = a.fp8 && after_projection;
     a.os = (uint16_t*)(ws + plan.off[W_OS]);
     a.ol = (uint16_t*)(ws + plan.off[W_OL]);
     a.ss = (float*)(ws + plan.off[W_SS]);
@@ -344,6 +358,178 @@ hyb_status hyb_attn_forward(const hyb_layout* layout, hyb_dtype act, hyb_dtype s
   }
   if (he != hipSuccess) return fail(HYB_ERR_HIP, "HIP error: %s", hipGetErrorString(he));
   return HYB_OK;
+}
+
+// Workspace of the projection: [W_q | W_k | W_v] transposed, bf16.
+size_t qkv_weight_bytes(const hyb::Dims& d) { return align_up((size_t)3 * d.hid * d.hid * 2, 256); }
+
+hyb_status check_projection(const hyb_layout* layout) {
+  hyb_status st = check_layout(layout, false);
+  if (st != HYB_OK) return st;
+  if (layout->head_dim != 64 && layout->head_dim != 128)
+    return fail(HYB_ERR_UNSUPPORTED, "the projection needs head_dim 64 or 128");
+  return HYB_OK;
+}
+
+// q, k, v = x [W_q | W_k | W_v] into contiguous [B*N][hid] bf16 buffers.
+hipError_t run_projection(const hyb::Dims& d, const void* x, const void* w_q, const void* w_k, const void* w_v,
+                          char* wt, void* q, void* k, void* v, uint32_t* absmax, hipStream_t s) {
+  hipError_t e = hyb::launch_qkv_weights((const hyb::bf16_t*)w_q, (const hyb::bf16_t*)w_k,
+                                         (const hyb::bf16_t*)w_v, d.hid, (hyb::bf16_t*)wt, s);
+  if (e != hipSuccess) return e;
+  return hyb::launch_qkv_gemm(d, (const hyb::bf16_t*)x, (const hyb::bf16_t*)wt, (hyb::bf16_t*)q,
+                              (hyb::bf16_t*)k, (hyb::bf16_t*)v, absmax, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+hyb_status hyb_attn_forward(const hyb_layout* layout, hyb_dtype act, hyb_dtype soft, const void* x, hyb_tensor q,
+                            hyb_tensor k, hyb_tensor v, hyb_tensor text_k, hyb_tensor text_v,
+                            const void* w_gate_soft, const void* w_gate_lin, const void* w_out_soft,
+                            const void* w_out_lin, const void* rms_weight, float softmax_scale, float eps, void* y,
+                            void* workspace, size_t workspace_bytes, void* stream, const hyb_debug* dbg) {
+  g_err[0] = 0;
+  return attn_forward_impl(layout, act, soft, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin, w_out_soft,
+                           w_out_lin, rms_weight, softmax_scale, eps, y, workspace, workspace_bytes, stream, dbg,
+                           false);
+}
+
+hyb_status hyb_qkv_workspace_size(const hyb_layout* layout, size_t* bytes) {
+  g_err[0] = 0;
+  hyb_status st = check_projection(layout);
+  if (st != HYB_OK) return st;
+  if (!bytes) return fail(HYB_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = qkv_weight_bytes(make_dims(layout));
+  return HYB_OK;
+}
+
+hyb_status hyb_qkv_project(const hyb_layout* layout, const void* x, const void* w_q, const void* w_k,
+                           const void* w_v, void* q, void* k, void* v, uint32_t* absmax, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  hyb_status st = check_projection(layout);
+  if (st != HYB_OK) return st;
+  const hyb::Dims d = make_dims(layout);
+  const void* ptrs[] = {x, w_q, w_k, w_v, q, k, v, workspace};
+  const char* names[] = {"x", "w_q", "w_k", "w_v", "q", "k", "v", "workspace"};
+  for (int i = 0; i < 8; ++i) {
+    if (!ptrs[i]) return fail(HYB_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (!aligned(ptrs[i], i == 7 ? 256 : 16))
+      return fail(HYB_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", names[i], i == 7 ? 256 : 16);
+  }
+  if (absmax && !aligned(absmax, 4)) return fail(HYB_ERR_INVALID_ARGUMENT, "absmax is not 4-byte aligned");
+  {  // outputs must not overlap x or each other
+    const size_t bytes = (size_t)d.B * d.N * d.hid * 2;
+    const uintptr_t lo[4] = {(uintptr_t)x, (uintptr_t)q, (uintptr_t)k, (uintptr_t)v};
+    for (int i = 0; i < 4; ++i)
+      for (int j = i + 1; j < 4; ++j)
+        if (lo[i] < lo[j] + bytes && lo[j] < lo[i] + bytes)
+          return fail(HYB_ERR_INVALID_ARGUMENT, "x, q, k and v must not overlap");
+  }
+  if (workspace_bytes < qkv_weight_bytes(d))
+    return fail(HYB_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                qkv_weight_bytes(d));
+  const hipError_t he = run_projection(d, x, w_q, w_k, w_v, (char*)workspace, q, k, v, absmax, (hipStream_t)stream);
+  if (he != hipSuccess) return fail(HYB_ERR_HIP, "HIP error: %s", hipGetErrorString(he));
+  return HYB_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Block workspace: [layer plan | projection weights | q | k | v].
+struct BlockPlan {
+  Plan layer;
+  size_t wt, q, k, v, total;
+};
+
+BlockPlan make_block_plan(const hyb::Dims& d, hyb_dtype soft) {
+  BlockPlan b;
+  b.layer = make_plan(d, HYB_BF16, soft);
+  const size_t act = align_up((size_t)d.B * d.N * d.hid * 2, 256);
+  b.wt = b.layer.total;
+  b.q = b.wt + qkv_weight_bytes(d);
+  b.k = b.q + act;
+  b.v = b.k + act;
+  b.total = b.v + act;
+  return b;
+}
+
+}  // namespace
+
+extern "C" {
+
+hyb_status hyb_block_workspace_size(const hyb_layout* layout, hyb_dtype soft, size_t* bytes) {
+  g_err[0] = 0;
+  hyb_status st = check_projection(layout);
+  if (st != HYB_OK) return st;
+  st = check_dtypes(layout, HYB_BF16, soft);
+  if (st != HYB_OK) return st;
+  if (!bytes) return fail(HYB_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = make_block_plan(make_dims(layout), soft).total;
+  return HYB_OK;
+}
+
+hyb_status hyb_block_forward(const hyb_layout* layout, hyb_dtype soft, const void* x, const void* w_q,
+                             const void* w_k, const void* w_v, hyb_tensor text_k, hyb_tensor text_v,
+                             const void* w_gate_soft, const void* w_gate_lin, const void* w_out_soft,
+                             const void* w_out_lin, const void* rms_weight, float softmax_scale, float eps, void* y,
+                             void* workspace, size_t workspace_bytes, void* stream, const hyb_debug* dbg) {
+  g_err[0] = 0;
+  hyb_status st = check_projection(layout);
+  if (st != HYB_OK) return st;
+  st = check_dtypes(layout, HYB_BF16, soft);
+  if (st != HYB_OK) return st;
+  const void* ptrs[] = {x, w_q, w_k, w_v, workspace};
+  const char* names[] = {"x", "w_q", "w_k", "w_v", "workspace"};
+  for (int i = 0; i < 5; ++i) {
+    if (!ptrs[i]) return fail(HYB_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (!aligned(ptrs[i], i == 4 ? 256 : 16))
+      return fail(HYB_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", names[i], i == 4 ? 256 : 16);
+  }
+  const hyb::Dims d = make_dims(layout);
+  const BlockPlan bp = make_block_plan(d, soft);
+  if (workspace_bytes < bp.total)
+    return fail(HYB_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, bp.total);
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  // q, k, v views of the workspace buffers: contiguous [B, N, H, D]
+  hyb_tensor tq, tk, tv;
+  const int64_t sb = (int64_t)d.N * d.hid, stok = d.hid, sh = d.D;
+  tq.ptr = ws + bp.q; tk.ptr = ws + bp.k; tv.ptr = ws + bp.v;
+  tq.stride_b = tk.stride_b = tv.stride_b = sb;
+  tq.stride_tok = tk.stride_tok = tv.stride_tok = stok;
+  tq.stride_head = tk.stride_head = tv.stride_head = sh;
+  // Validate the layer's own arguments before launching anything.
+  {
+    const bool has_text = d.L > 0;
+    if ((st = check_tensor("text_k", text_k, 2, has_text)) != HYB_OK) return st;
+    if ((st = check_tensor("text_v", text_v, 2, has_text)) != HYB_OK) return st;
+    if ((st = check_tensor("q", tq, 2, true)) != HYB_OK) return st;
+    const void* lp[] = {w_gate_soft, w_gate_lin, w_out_soft, w_out_lin, rms_weight, y};
+    const char* ln[] = {"w_gate_soft", "w_gate_lin", "w_out_soft", "w_out_lin", "rms_weight", "y"};
+    for (int i = 0; i < 6; ++i) {
+      if (!lp[i]) return fail(HYB_ERR_INVALID_ARGUMENT, "%s is NULL", ln[i]);
+      if (!aligned(lp[i], 16)) return fail(HYB_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", ln[i]);
+    }
+    if (!(eps > 0.f) || !isfinite(eps)) return fail(HYB_ERR_INVALID_ARGUMENT, "eps must be finite and > 0");
+    if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale))
+      return fail(HYB_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  }
+  hipEvent_t* ev = dbg ? (hipEvent_t*)dbg->stage_events : nullptr;
+  hipError_t he = hipSuccess;
+  if (ev) he = hipEventRecord(ev[2 * HYB_STAGE_QKV], s);
+  // fp8: the projection writes the absmax of q, k, v straight into the layer's absmax buffer
+  uint32_t* amx = soft == HYB_FP8_E4M3 ? (uint32_t*)(ws + bp.layer.off[W_AM]) : nullptr;
+  if (he == hipSuccess) he = run_projection(d, x, w_q, w_k, w_v, ws + bp.wt, ws + bp.q, ws + bp.k, ws + bp.v, amx, s);
+  if (he == hipSuccess && ev) he = hipEventRecord(ev[2 * HYB_STAGE_QKV + 1], s);
+  if (he != hipSuccess) return fail(HYB_ERR_HIP, "HIP error: %s", hipGetErrorString(he));
+  return attn_forward_impl(layout, HYB_BF16, soft, x, tq, tk, tv, text_k, text_v, w_gate_soft, w_gate_lin,
+                           w_out_soft, w_out_lin, rms_weight, softmax_scale, eps, y, workspace, bp.layer.total,
+                           stream, dbg, true);
 }
 
 }  // extern "C"

@@ -463,16 +463,31 @@ static QuantSrc quant_src(const Dims& d, const Bf16Args& a) {
   return s;
 }
 
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_u32, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_fp8(const Dims& d, const Bf16Args& a, hipStream_t s) {
   const QuantSrc src = quant_src(d, a);
   const int n = 5 * d.B * d.H;
-  hipLaunchKernelGGL(k_zero_u32, dim3((n + 255) / 256), dim3(256), 0, s, a.absmax, n);
-  hipError_t e = hipGetLastError();
+  // With the projection's absmax of q, k, v already in place, only the text
+  // tensors are scanned here.
+  const int first = a.qkv_absmax_ready ? 3 : 0;
+  QuantSrc amx = src;
+  for (int t = 0; t < first; ++t) amx.tokens[t] = 0;
+  hipError_t e = launch_zero_u32(a.absmax + first * d.B * d.H, n - first * d.B * d.H, s);
   if (e != hipSuccess) return e;
-  long long chunks = 0;
-  for (int t = 0; t < 5; ++t) chunks += (long long)((src.tokens[t] + 255) / 256) * d.B * d.H;
-  hipLaunchKernelGGL(k_absmax, dim3((unsigned)chunks), dim3(256), 0, s, d, src, a.absmax);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  long long achunks = 0, chunks = 0;
+  for (int t = 0; t < 5; ++t) {
+    achunks += (long long)((amx.tokens[t] + 255) / 256) * d.B * d.H;
+    chunks += (long long)((src.tokens[t] + 255) / 256) * d.B * d.H;
+  }
+  if (achunks > 0) {
+    hipLaunchKernelGGL(k_absmax, dim3((unsigned)achunks), dim3(256), 0, s, d, amx, a.absmax);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_scales, dim3((n + 255) / 256), dim3(256), 0, s, a.absmax, a.scales, n);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_quant_rows, dim3((unsigned)chunks), dim3(256), 0, s, d, src, a.absmax, a.q8, a.k8, a.tk8);

@@ -19,7 +19,7 @@
 
 namespace hyb {
 
-enum { EPI_GATE = 0, EPI_OUT = 1 };
+enum { EPI_GATE = 0, EPI_OUT = 1, EPI_QKV = 2 };
 
 struct GemmArgs {
   const uint16_t* A;   // [M][K] token rows (bf16 or fp16 bits)
@@ -37,6 +37,10 @@ struct GemmArgs {
   const bf16_t* x;
   bf16_t* y;
   float* delta_dbg;
+  // projection epilogue: q, k, v [M][hid] and absmax [3][B][H] (nullable)
+  bf16_t *qo, *ko, *vo;
+  uint32_t* absmax;
+  int B, n_video, D;
 };
 
 // WG = WM x WN waves; each wave computes WTM x WFN blocks of 32 x 32 (tokens x
@@ -131,11 +135,11 @@ void k_gemm_bf16(GemmArgs g) {
       for (int f = 0; f < WFN; ++f)
 #pragma unroll
         for (int i = 0; i < WTM; ++i) {
-          if constexpr (EPI == EPI_GATE)
-            acc[f][i] = mfma32(__builtin_bit_cast(bf16x8, tb[ks][f]), __builtin_bit_cast(bf16x8, ta[ks][i]), acc[f][i]);
-          else
+          if constexpr (EPI == EPI_OUT)  // fp16 operands (A' and W_o)
             acc[f][i] = mfma32_f16(__builtin_bit_cast(halfx8, tb[ks][f]), __builtin_bit_cast(halfx8, ta[ks][i]),
                                    acc[f][i]);
+          else
+            acc[f][i] = mfma32(__builtin_bit_cast(bf16x8, tb[ks][f]), __builtin_bit_cast(bf16x8, ta[ks][i]), acc[f][i]);
         }
   };
 
@@ -166,6 +170,61 @@ void k_gemm_bf16(GemmArgs g) {
       if (kt + 3 < nk) step(kt + 3, std::integral_constant<int, 3 % ST>{});
   }
 
+  if constexpr (EPI == EPI_QKV) {
+    // q / k / v column block of this tile (hid % BN == 0: one tensor per tile)
+    const int t = n0 / g.hid;
+    bf16_t* outp = t == 0 ? g.qo : (t == 1 ? g.ko : g.vo);
+    const int cw = n0 - t * g.hid + wn * WFN * 32;  // first column of this wave
+    uint32_t mx[WTM][WFN];  // largest |bf16 value| (float bits) per token group and 32-column block
+#pragma unroll
+    for (int i = 0; i < WTM; ++i) {
+      const long long m = m0 + wm * WTM * 32 + i * 32 + l32;
+      const bool ok = m < g.M;
+#pragma unroll
+      for (int f = 0; f < WFN; ++f) {
+        uint32_t a = 0;
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const uint32_t lo = pack_bf16x2(acc[f][i][4 * jg], acc[f][i][4 * jg + 1]);
+          const uint32_t hi = pack_bf16x2(acc[f][i][4 * jg + 2], acc[f][i][4 * jg + 3]);
+          if (ok) *(uint2*)(outp + m * g.hid + cw + 32 * f + 8 * jg + 4 * half) = make_uint2(lo, hi);
+          a = max(a, max(max((lo & 0x7fffu) << 16, lo & 0x7fff0000u), max((hi & 0x7fffu) << 16, hi & 0x7fff0000u)));
+        }
+        mx[i][f] = ok ? a : 0u;
+      }
+    }
+    if (g.absmax) {
+      const long long mw0 = m0 + wm * WTM * 32;  // first token of this wave
+      if (mw0 < g.M) {
+        const long long mw1 = min(g.M - 1, mw0 + WTM * 32 - 1);
+        const int b0 = (int)(mw0 / g.n_video), b1 = (int)(mw1 / g.n_video);
+        if (b0 == b1) {
+          // one batch: reduce over the wave, one atomic per 32-column block
+#pragma unroll
+          for (int f = 0; f < WFN; ++f) {
+            uint32_t v = mx[0][f];
+#pragma unroll
+            for (int i = 1; i < WTM; ++i) v = max(v, mx[i][f]);
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off));
+            if (lane == 0) atomicMax(g.absmax + ((long long)t * g.B + b0) * g.H + (cw + 32 * f) / g.D, v);
+          }
+        } else {
+          // the wave straddles a batch boundary: per-lane atomics
+#pragma unroll
+          for (int i = 0; i < WTM; ++i) {
+            const long long m = mw0 + i * 32 + l32;
+            if (m >= g.M) continue;
+            const int b = (int)(m / g.n_video);
+#pragma unroll
+            for (int f = 0; f < WFN; ++f)
+              atomicMax(g.absmax + ((long long)t * g.B + b) * g.H + (cw + 32 * f) / g.D, mx[i][f]);
+          }
+        }
+      }
+    }
+    return;
+  }
   // ---- epilogue: lane owns token m, features n0' + 8*jg + 4*half + 0..3.
   // All loads of one token row are issued before its stores.
 #pragma unroll
@@ -235,11 +294,12 @@ void k_gemm_bf16(GemmArgs g) {
 // Weight transposes into the GEMMs' [N][K] operand layout.
 //   mode 0: out[2*hid][hid] bf16,  out[c][r] = c < hid ? W_gs[r][c] : W_gl[r][c - hid]
 //   mode 1: out[hid][2*hid] fp16,  out[c][r] = r < hid ? W_os[r][c] : W_ol[r - hid][c]
+//   mode 2: out[hid][hid] bf16,    out[c][r] = W[r][c]  (s0 only)
 __global__ __launch_bounds__(256) void k_weight_transpose(const bf16_t* __restrict__ s0,
                                                           const bf16_t* __restrict__ s1, int hid, int mode,
                                                           uint16_t* __restrict__ out) {
   __shared__ uint16_t t[64][66];
-  const int R = mode == 0 ? hid : 2 * hid;  // source rows
+  const int R = mode == 1 ? 2 * hid : hid;  // source rows
   const int C = mode == 0 ? 2 * hid : hid;  // source cols
   const int tc = blockIdx.x % (C / 64), tr = blockIdx.x / (C / 64);
   const int r0 = tr * 64, c0 = tc * 64;
@@ -248,8 +308,9 @@ __global__ __launch_bounds__(256) void k_weight_transpose(const bf16_t* __restri
     const int r = r0 + rr, c = c0 + cc;
     bf16_t val;
     if (mode == 0) val = c < hid ? s0[(long long)r * hid + c] : s1[(long long)r * hid + c - hid];
-    else val = r < hid ? s0[(long long)r * hid + c] : s1[(long long)(r - hid) * hid + c];
-    t[rr][cc] = mode == 0 ? val : f32_to_f16_sat(bf16_to_f32(val));
+    else if (mode == 1) val = r < hid ? s0[(long long)r * hid + c] : s1[(long long)(r - hid) * hid + c];
+    else val = s0[(long long)r * hid + c];
+    t[rr][cc] = mode == 1 ? f32_to_f16_sat(bf16_to_f32(val)) : val;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
@@ -271,7 +332,8 @@ hipError_t launch_weights_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) 
 template <int WM, int WN, int WTM, int WFN, int BK, int ST, int WPE, int EPI, int GM = 1>
 static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   constexpr int BM = WM * WTM * 32, BN = WN * WFN * 32;
-  if (g.N % BN != 0 || g.K % BK != 0 || (EPI == EPI_GATE && g.hid % BN != 0)) return hipErrorInvalidValue;
+  if (g.N % BN != 0 || g.K % BK != 0 || ((EPI == EPI_GATE || EPI == EPI_QKV) && g.hid % BN != 0))
+    return hipErrorInvalidValue;
   // 32-bit per-lane DMA offsets: a tile's rows span < 4 GiB
   if ((long long)BM * g.K * 2 >= (1LL << 32) || (long long)BN * g.K * 2 >= (1LL << 32)) return hipErrorInvalidValue;
   const long long grid = ((g.M + BM - 1) / BM) * (g.N / BN);
@@ -303,6 +365,48 @@ hipError_t launch_gate_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s
   if (d.hid % 256 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_GATE, 4>(g, s);
   if (d.hid % 128 == 0) return launch_gemm<2, 2, 4, 2, 32, 3, 2, EPI_GATE>(g, s);
   return launch_gemm<2, 2, 4, 1, 32, 3, 2, EPI_GATE>(g, s);  // hid multiple of 64 only
+}
+
+// [W_q | W_k | W_v] transposed into [3*hid][hid] (one mode-2 transpose each).
+hipError_t launch_qkv_weights(const bf16_t* wq, const bf16_t* wk, const bf16_t* wv, int hid, bf16_t* out,
+                              hipStream_t s) {
+  const bf16_t* src[3] = {wq, wk, wv};
+  const unsigned grid = (unsigned)((hid / 64) * (hid / 64));
+  for (int t = 0; t < 3; ++t) {
+    hipLaunchKernelGGL(k_weight_transpose, dim3(grid), dim3(256), 0, s, src[t], src[t], hid, 2,
+                       (uint16_t*)out + (long long)t * hid * hid);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// q, k, v = x [W_q | W_k | W_v]; absmax (nullable) receives the per-(tensor,
+// batch, head) maximum |value| of the stored bf16 outputs (zeroed here).
+hipError_t launch_qkv_gemm(const Dims& d, const bf16_t* x, const bf16_t* wt, bf16_t* q, bf16_t* k, bf16_t* v,
+                           uint32_t* absmax, hipStream_t s) {
+  if (absmax) {
+    hipError_t e = launch_zero_u32(absmax, 3 * d.B * d.H, s);
+    if (e != hipSuccess) return e;
+  }
+  GemmArgs g = {};
+  g.M = (long long)d.B * d.N;
+  g.hid = d.hid;
+  g.H = d.H;
+  g.B = d.B;
+  g.n_video = d.N;
+  g.D = d.D;
+  g.A = x;
+  g.Bt = wt;
+  g.N = 3 * d.hid;
+  g.K = d.hid;
+  g.qo = q;
+  g.ko = k;
+  g.vo = v;
+  g.absmax = absmax;
+  if (d.hid % 256 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_QKV, 4>(g, s);
+  if (d.hid % 128 == 0) return launch_gemm<2, 2, 4, 2, 32, 3, 2, EPI_QKV>(g, s);
+  return launch_gemm<2, 2, 4, 1, 32, 3, 2, EPI_QKV>(g, s);  // hid multiple of 64 only
 }
 
 hipError_t launch_out_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {

@@ -38,6 +38,7 @@ struct Bf16Args {
   uint8_t *q8, *k8, *v8t, *tk8, *tv8t;  // e4m3 copies (v transposed per 64-key tile)
   float* scales;          // [5][B][H] dequantisation scales
   uint32_t* absmax;       // [5][B][H] absmax bit patterns
+  bool qkv_absmax_ready;  // absmax[0 .. 3*B*H) already holds q, k, v (from the projection)
   bf16_t* y;
   float *gates_dbg, *delta_dbg;
   hipEvent_t* ev;         // NULL or 2 events per stage (timing hook)
@@ -47,6 +48,13 @@ struct Bf16Args {
 };
 
 hipError_t run_bf16(const Dims& d, const Bf16Args& a, hipStream_t s);
+// Q/K/V input projection (gemm_epilogue.hip): weights [W_q | W_k | W_v]
+// transposed to [3*hid][hid], then q, k, v = x W (bf16, [B*N][hid] each) with
+// the per-(tensor, batch, head) absmax of the stored values (nullable).
+hipError_t launch_qkv_weights(const bf16_t* wq, const bf16_t* wk, const bf16_t* wv, int hid, bf16_t* out,
+                              hipStream_t s);
+hipError_t launch_qkv_gemm(const Dims& d, const bf16_t* x, const bf16_t* wt, bf16_t* q, bf16_t* k, bf16_t* v,
+                           uint32_t* absmax, hipStream_t s);
 // fp16 bits -> float32 (debug copies of the fp16 branch outputs)
 hipError_t launch_f16_to_f32(const uint16_t* src, float* dst, long long n, hipStream_t s);
 

@@ -14,5 +14,6 @@ hipError_t launch_readout_bf16(const Dims& d, const Bf16Args& a, hipStream_t s);
 hipError_t launch_weights_bf16(const Dims& d, const Bf16Args& a, hipStream_t s);
 hipError_t launch_gate_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s);
 hipError_t launch_out_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s);
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
 
 }  // namespace hyb

@@ -95,7 +95,8 @@ enum {
   HYB_STAGE_READOUT = 5,   /* phi(Q) readout */
   HYB_STAGE_GATE = 6,      /* gate GEMM + RMSNorm/gating epilogue */
   HYB_STAGE_OUT = 7,       /* output GEMM + residual */
-  HYB_STAGE_COUNT = 8
+  HYB_STAGE_QKV = 8,       /* Q/K/V projection (hyb_block_forward only; recorded first) */
+  HYB_STAGE_COUNT = 9
 };
 
 /* Optional float32 copies of intermediate results (each pointer may be NULL):
@@ -108,7 +109,9 @@ enum {
  *   stage_events  NULL or an array of 2*HYB_STAGE_COUNT hipEvent_t created by
  *                 the caller; events 2s and 2s+1 are recorded on `stream`
  *                 right before and after stage s (for timing; a stage that
- *                 does not run records both back to back). */
+ *                 does not run records both back to back).
+ * With fp8 softmax the dequantisation scales are absmax / 448 (1 for an
+ * all-zero tensor). */
 typedef struct {
   void *o_soft, *o_lin, *delta_f32, *gates, *scales;
   void* stage_events;
@@ -151,6 +154,51 @@ hyb_status hyb_attn_forward(const hyb_layout* layout, hyb_dtype act, hyb_dtype s
                             const void* rms_weight, float softmax_scale, float eps,
                             void* y, void* workspace, size_t workspace_bytes,
                             void* stream, const hyb_debug* dbg);
+
+/*
+ * Q/K/V input projection -- the step before the layer.  Article section
+ * "分阶段适配预训练模型" (staged adaptation): both attention branches read one
+ * set of Q/K/V projections of the block input (stages A2 and B).  The
+ * performance section's "FP8 version" quantises the softmax branch's Q/K/V;
+ * the per-(tensor, batch, head) absmax that sets those scales is taken here,
+ * in the projection GEMM's epilogue, instead of by a separate pass.
+ *
+ *   q = x W_q, k = x W_k, v = x W_v   (bf16 operands, fp32 accumulation,
+ *                                      outputs rounded to bf16, no bias)
+ *   x            [B, N, hid] bf16 contiguous
+ *   w_q, w_k, w_v [hid][hid] bf16 row-major ([in][out]); feature h*D + d of
+ *                an output is head h, dim d
+ *   q, k, v      [B, N, H, D] bf16 contiguous outputs; must not overlap x or
+ *                each other
+ *   absmax       NULL or uint32 [3][B][H]: the float32 bit pattern of the
+ *                largest |value| of the stored q (index 0), k (1), v (2) per
+ *                (batch, head); NaN inputs propagate into it
+ *   workspace    at least hyb_qkv_workspace_size() bytes, 256-byte aligned
+ *                (the transposed weights)
+ * head_dim 64 or 128; enqueued on `stream`, no synchronisation; same error
+ * behaviour as hyb_attn_forward().
+ */
+hyb_status hyb_qkv_workspace_size(const hyb_layout* layout, size_t* bytes);
+hyb_status hyb_qkv_project(const hyb_layout* layout, const void* x, const void* w_q, const void* w_k,
+                           const void* w_v, void* q, void* k, void* v, uint32_t* absmax, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * The layer with its input projection: q, k, v = hyb_qkv_project(x) into the
+ * workspace, then hyb_attn_forward() on them (activations bf16; soft is
+ * HYB_BF16 or HYB_FP8_E4M3).  With fp8 the projection's absmax is the one
+ * the softmax branch's quantisation uses, so the layer scans only the text
+ * tensors for theirs.  Arguments as in hyb_attn_forward(); the workspace
+ * (hyb_block_workspace_size(), 256-byte aligned) also holds q, k, v; dbg's
+ * stage_events include HYB_STAGE_QKV.
+ */
+hyb_status hyb_block_workspace_size(const hyb_layout* layout, hyb_dtype soft, size_t* bytes);
+hyb_status hyb_block_forward(const hyb_layout* layout, hyb_dtype soft, const void* x, const void* w_q,
+                             const void* w_k, const void* w_v, hyb_tensor text_k, hyb_tensor text_v,
+                             const void* w_gate_soft, const void* w_gate_lin, const void* w_out_soft,
+                             const void* w_out_lin, const void* rms_weight, float softmax_scale, float eps,
+                             void* y, void* workspace, size_t workspace_bytes, void* stream,
+                             const hyb_debug* dbg);
 
 /* Static description of a status code. */
 const char* hyb_status_string(hyb_status status);

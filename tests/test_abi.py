@@ -28,7 +28,8 @@ def test_exports_every_declared_symbol():
     lib = api.load()
     names = declared_functions()
     assert names == sorted(["hyb_attn_forward", "hyb_last_error", "hyb_layout_tables",
-                            "hyb_status_string", "hyb_workspace_size"])
+                            "hyb_status_string", "hyb_workspace_size", "hyb_qkv_workspace_size",
+                            "hyb_qkv_project", "hyb_block_workspace_size", "hyb_block_forward"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -124,3 +125,60 @@ def test_forward_validation_errors():
     assert _call(bad)[0] == api.HYB_ERR_INVALID_ARGUMENT
     assert _call(api.Layout(0, 15, 1024, 128, 8, 64))[0] == api.HYB_ERR_INVALID_ARGUMENT
     assert api.load().hyb_status_string(3) == b"workspace too small"
+
+
+def _qkv_call(lay, **over):
+    """hyb_qkv_project with fake aligned addresses; must fail validation."""
+    lib = api.load()
+    c = lay.c()
+    base = 1 << 40
+    args = dict(x=base, wq=base + (1 << 34), wk=base + (2 << 34), wv=base + (3 << 34), q=base + (4 << 34),
+                k=base + (5 << 34), v=base + (6 << 34), amax=None, ws=base + (7 << 34), wsb=1 << 40)
+    args.update(over)
+    r = lib.hyb_qkv_project(ctypes.byref(c), args["x"], args["wq"], args["wk"], args["wv"], args["q"], args["k"],
+                            args["v"], args["amax"], args["ws"], args["wsb"], None)
+    return r, lib.hyb_last_error().decode()
+
+
+def test_qkv_project_validation_errors():
+    lay = api.Layout(1, 15, 1024, 128, 8, 64)
+    assert _qkv_call(lay, x=None)[0] == api.HYB_ERR_INVALID_ARGUMENT
+    assert _qkv_call(lay, wk=(1 << 40) + 8)[0] == api.HYB_ERR_INVALID_ARGUMENT      # misaligned
+    assert _qkv_call(lay, ws=(1 << 40) + 16)[0] == api.HYB_ERR_INVALID_ARGUMENT     # workspace alignment
+    assert _qkv_call(lay, amax=(1 << 40) + 2)[0] == api.HYB_ERR_INVALID_ARGUMENT
+    r, msg = _qkv_call(lay, k=(1 << 40) + (4 << 34) + 4096)                         # k overlaps q
+    assert r == api.HYB_ERR_INVALID_ARGUMENT and "overlap" in msg
+    r, msg = _qkv_call(lay, wsb=1000)
+    assert r == api.HYB_ERR_WORKSPACE_TOO_SMALL and "needs" in msg
+    assert _qkv_call(api.Layout(1, 15, 64, 16, 2, 32))[0] == api.HYB_ERR_UNSUPPORTED   # head_dim 32
+    hid = 8 * 64
+    assert api.qkv_workspace_size(lay) == 3 * hid * hid * 2
+
+
+def test_block_forward_validation_errors():
+    lib = api.load()
+    lay = api.Layout(1, 15, 1024, 128, 8, 64)
+    c = lay.c()
+    base = 1 << 40
+    T4 = api._Tensor
+    st = (128 * 512, 512, 64)
+
+    def call(**over):
+        a = dict(soft=1, x=base, wq=base + (1 << 34), wk=base + (2 << 34), wv=base + (3 << 34),
+                 tk=T4(base + (4 << 34), *st), tv=T4(base + (5 << 34), *st), wgs=base + (6 << 34),
+                 wgl=base + (7 << 34), wos=base + (8 << 34), wol=base + (9 << 34), rms=base + (10 << 34),
+                 scale=0.0, eps=1e-6, y=base + (11 << 34), ws=base + (12 << 34), wsb=1 << 40)
+        a.update(over)
+        return lib.hyb_block_forward(ctypes.byref(c), a["soft"], a["x"], a["wq"], a["wk"], a["wv"], a["tk"],
+                                     a["tv"], a["wgs"], a["wgl"], a["wos"], a["wol"], a["rms"], a["scale"],
+                                     a["eps"], a["y"], a["ws"], a["wsb"], None, None)
+
+    assert call(wq=None) == api.HYB_ERR_INVALID_ARGUMENT
+    assert call(wgs=None) == api.HYB_ERR_INVALID_ARGUMENT
+    assert call(tk=T4(None, 0, 0, 0)) == api.HYB_ERR_INVALID_ARGUMENT
+    assert call(eps=0.0) == api.HYB_ERR_INVALID_ARGUMENT
+    assert call(soft=0) == api.HYB_ERR_UNSUPPORTED                  # float32 softmax with bf16 activations
+    assert call(wsb=1000) == api.HYB_ERR_WORKSPACE_TOO_SMALL
+    n = api.block_workspace_size(lay)
+    assert n > api.workspace_size(lay, "bf16") + 3 * 15 * 1024 * 512 * 2
+    assert api.block_workspace_size(lay, "fp8") > n
