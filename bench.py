@@ -1,10 +1,13 @@
 """Throughput of the hybrid attention layer on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--no-cpu-baseline] [--block]
 
 One step = one full forward of the layer (softmax branch, state build, scan,
 readout, gate GEMM + epilogue, output GEMM + residual) over one batch of
 seeded synthetic inputs already resident in HBM.  Prints one JSON line.
+With --block a step starts one stage earlier, at the layer input x: the
+Q/K/V projection (one GEMM with the fp8 absmax in its epilogue) and then the
+layer, and the line carries that metric instead.
 """
 import argparse
 import ctypes
@@ -20,11 +23,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from hybrid_softmax_linear_block_amd import api  # noqa: E402
-from hybrid_softmax_linear_block_amd.inputs import WORKLOADS, make_inputs, sample_tokens  # noqa: E402
+from hybrid_softmax_linear_block_amd.inputs import (WORKLOADS, make_inputs, make_projection_weights,  # noqa: E402
+                                                    sample_tokens)
 
 WORKLOADS_ID = {w.name: i for i, w in WORKLOADS.items()}
 
 METRIC = "hybrid-attn layer Mtokens/s + softmax-branch TFLOP/s (768p-shaped, bf16)"
+METRIC_BLOCK = "hybrid-attn layer with its Q/K/V projection Mtokens/s (768p-shaped, bf16)"
 PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense MFMA TFLOP/s, MI355X published
 PEAK_HBM_GBS = 8000.0  # HBM3E, MI355X published
 HBM_PEAK_GBS = 8000.0
@@ -54,7 +59,7 @@ def work_counts(w):
             "layer_flop": soft + states + readout + gemm}
 
 
-def stage_work(w, soft):
+def stage_work(w, soft, block=False):
     """Algorithmic work per stage of the bf16 path: FLOP for the MFMA
     kernels, the HBM bytes each kernel must move for the others (inputs read
     once, outputs written once, intermediates in the formats the path uses)."""
@@ -75,12 +80,15 @@ def stage_work(w, soft):
     }
     if soft:
         work["quant"] = ("hbm", (3 * B * N + 2 * B * L) * hid * (es + 1))
+    if block:
+        # x [B*N][hid] @ [hid][3 hid]: 2 * B*N * hid * 3 hid
+        work["qkv"] = ("mfma", 2.0 * B * N * hid * 3 * hid)
     return work
 
 
-def stage_roofline(w, soft, stage_ms):
+def stage_roofline(w, soft, stage_ms, block=False):
     out = {}
-    for k, (bound, amount) in stage_work(w, soft).items():
+    for k, (bound, amount) in stage_work(w, soft, block).items():
         t = stage_ms.get(k, 0.0)
         if t <= 0:
             continue
@@ -181,7 +189,7 @@ def cpu_baseline(w, inp, budget_s=20.0):
         t0 = time.perf_counter()
         st = oracle.linear_states(inp["k"], inp["v"], inp["text_k"], inp["text_v"], lay)
         t_states = time.perf_counter() - t0
-        per = 16
+        per = 64
         tok = sample_tokens(w, per_frame=per)
         t0 = time.perf_counter()
         o_s = oracle.softmax_branch(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], lay, tokens=tok)
@@ -222,6 +230,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--block", action="store_true",
+                    help="time the layer with its Q/K/V projection (x -> q, k, v -> y) instead of the layer")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--write-traffic", metavar="PMC_DIR",
@@ -256,15 +266,28 @@ def main():
     dev = {k: torch.from_numpy(v).to("cuda").to(dt) for k, v in inp.items()}
     lay = layout_of(w)
     soft = "fp8" if w.soft == "fp8" else None
-    ws = torch.empty(api.workspace_size(lay, "f32" if w.act == "f32" else "bf16", soft), dtype=torch.uint8,
-                     device="cuda")
+    if args.block:
+        if w.act != "bf16":
+            print("--block runs the bf16 path", file=sys.stderr)
+            sys.exit(2)
+        pw = {k: torch.from_numpy(v).to("cuda").to(dt) for k, v in make_projection_weights(w).items()}
+        ws_bytes = api.block_workspace_size(lay, soft)
+    else:
+        ws_bytes = api.workspace_size(lay, "f32" if w.act == "f32" else "bf16", soft)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     y = torch.empty_like(dev["x"])
     stream = torch.cuda.current_stream().cuda_stream
 
     def step(timer=None):
-        api.forward(lay, dev["x"], dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"], dev["w_gs"],
-                    dev["w_gl"], dev["w_os"], dev["w_ol"], dev["rms_w"], soft=soft, y=y, workspace=ws,
-                    stream=stream, debug={"stage_events": timer.address} if timer else None)
+        dbg = {"stage_events": timer.address} if timer else None
+        if args.block:
+            api.block_forward(lay, dev["x"], pw["w_q"], pw["w_k"], pw["w_v"], dev["text_k"], dev["text_v"],
+                              dev["w_gs"], dev["w_gl"], dev["w_os"], dev["w_ol"], dev["rms_w"], soft=soft, y=y,
+                              workspace=ws, stream=stream, debug=dbg)
+        else:
+            api.forward(lay, dev["x"], dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"], dev["w_gs"],
+                        dev["w_gl"], dev["w_os"], dev["w_ol"], dev["rms_w"], soft=soft, y=y, workspace=ws,
+                        stream=stream, debug=dbg)
 
     for _ in range(args.warmup):
         step()
@@ -289,7 +312,7 @@ def main():
     def pct(v):
         p10, p50, p90 = np.percentile(np.asarray(v), [10, 50, 90])
         return {"p10": round(float(p10), 4), "p50": round(float(p50), 4), "p90": round(float(p90), 4)}
-    stage_ms = {k: float(np.mean(v)) for k, v in stage.items()}
+    stage_ms = {k: float(np.mean(v)) for k, v in stage.items() if args.block or k != "qkv"}
     ms = wall * 1e3 / args.steps
     wc = work_counts(w)
     soft_key = "softmax_fp8" if soft else "softmax"
@@ -297,18 +320,19 @@ def main():
     soft_tflops = wc["softmax_flop"] / (soft_ms * 1e-3) / 1e12
     peak = PEAK["fp8" if soft else w.act]
     value = w.batch * w.n_video / (ms * 1e-3) / 1e6
+    layer_flop = wc["layer_flop"] + (stage_work(w, soft, True)["qkv"][1] if args.block else 0.0)
     out = {
-        "metric": METRIC, "value": round(value, 4), "unit": "Mtokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC_BLOCK if args.block else METRIC, "value": round(value, 4), "unit": "Mtokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.act, "data": "synthetic",
         "config": {"workload": describe(w), "batch": w.batch, "video_tokens": w.n_video,
                    "text_tokens": w.text_tokens, "heads": w.heads, "head_dim": w.head_dim,
                    "parallelism": "none (1 GPU)"},
         "softmax_tflops": round(soft_tflops, 2),
-        "layer_tflops": round(wc["layer_flop"] / (ms * 1e-3) / 1e12, 2),
+        "layer_tflops": round(layer_flop / (ms * 1e-3) / 1e12, 2),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "gpu_ms_percentiles": {"forward": pct(span), "softmax": pct(stage["softmax"])},
-        "stage_roofline": stage_roofline(w, soft, stage_ms) if w.act != "f32" else None,
+        "stage_roofline": stage_roofline(w, soft, stage_ms, args.block) if w.act != "f32" else None,
         "device": device_info(torch),
         "roofline": {"kernel": "k_attn_bf16_sp (softmax branch)" if not soft else "softmax branch fp8",
                      "bound": "mfma", "achieved": round(soft_tflops, 2), "peak": peak, "unit": "TFLOP/s",
