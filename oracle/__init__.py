@@ -31,6 +31,12 @@ Parity status per function (what pins it, in ``tests/test_oracle_*.py``):
                                       split, a hand-computed example.
   projection.absmax_per_head          pinned: constructed tensors.
   projection.round_bf16               pinned: torch bfloat16 conversion.
+  backward.hybrid_backward and its    pinned: central finite differences of
+  reverse steps (softmax_backward,    the forward oracle along random
+  linear_backward, epilogue_backward) directions for every input, per step
+                                      and for the whole layer, on three frame
+                                      layouts; planted mistakes are caught.
+  backward.softmax_lse                pinned: closed forms (q = 0, constant keys).
   Anchor frames as queries (they attend to every frame): parity unpinned --
   the article says only that anchors interact with the other frames.
 """
@@ -38,3 +44,4 @@ from .layout import Layout, frame_sets, tables  # noqa: F401
 from .hybrid import (phi, softmax_branch, linear_states, linear_branch,  # noqa: F401
                      epilogue, hybrid_forward)
 from . import projection  # noqa: F401
+from . import backward  # noqa: F401
