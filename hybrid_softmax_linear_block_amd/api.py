@@ -40,6 +40,11 @@ class _Debug(ctypes.Structure):
 
 
 STAGES = ("weights", "quant", "softmax", "states", "scan", "readout", "gate", "out", "qkv")
+BWD_STAGES = ("forward", "epilogue", "wgrad", "rms", "softmax", "linear")
+
+
+class _BwdDebug(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("d_os", "d_ol", "lse2", "stage_events")]
 
 
 @dataclass(frozen=True)
@@ -104,6 +109,13 @@ def load(path=None):
         [ctypes.POINTER(_Layout), ctypes.c_int] + [ctypes.c_void_p] * 4 + [_Tensor] * 2 + [ctypes.c_void_p] * 5
         + [ctypes.c_float, ctypes.c_float]
         + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(_Debug)])
+    lib.hyb_backward_workspace_size.restype = ctypes.c_int
+    lib.hyb_backward_workspace_size.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(ctypes.c_size_t)]
+    lib.hyb_attn_backward.restype = ctypes.c_int
+    lib.hyb_attn_backward.argtypes = (
+        [ctypes.POINTER(_Layout), ctypes.c_void_p] + [_Tensor] * 5 + [ctypes.c_void_p] * 5
+        + [ctypes.c_float, ctypes.c_float] + [ctypes.c_void_p] * 7 + [ctypes.c_void_p] * 5
+        + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(_BwdDebug)])
     lib.hyb_status_string.restype = ctypes.c_char_p
     lib.hyb_status_string.argtypes = [ctypes.c_int]
     lib.hyb_last_error.restype = ctypes.c_char_p
@@ -278,17 +290,20 @@ def block_forward(lay: Layout, x, w_q, w_k, w_v, text_k, text_v, w_gate_soft, w_
 class StageTimer:
     """2 HIP events per stage, recorded by the library around each stage on
     the call's stream; ``elapsed_ms()`` returns per-stage milliseconds of the
-    last recorded call."""
+    last recorded call.  ``stages`` is STAGES (forward and block calls) or
+    BWD_STAGES (backward calls); ``span_ms`` runs from the start of stage
+    ``first`` to the end of stage ``last``."""
 
-    def __init__(self):
+    def __init__(self, stages=STAGES, first="qkv", last="out"):
         import torch
+        self.stages, self.first, self.last = stages, first, last
         self._hip = ctypes.CDLL("libamdhip64.so")
         self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                   ctypes.c_void_p]
         self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        n = 2 * len(STAGES)
+        n = 2 * len(stages)
         self.events = (ctypes.c_void_p * n)()
         for i in range(n):
             ev = ctypes.c_void_p()
@@ -303,7 +318,7 @@ class StageTimer:
 
     def elapsed_ms(self):
         out = {}
-        for i, name in enumerate(STAGES):
+        for i, name in enumerate(self.stages):
             a, b = self.events[2 * i], self.events[2 * i + 1]
             self._hip.hipEventSynchronize(b)
             ms = ctypes.c_float(0)
@@ -313,10 +328,10 @@ class StageTimer:
         return out
 
     def span_ms(self):
-        """Milliseconds from the first recorded event (the projection stage,
-        recorded first, empty for ``forward``) to the end of the output GEMM:
-        the whole call on the GPU."""
-        a, b = self.events[2 * STAGES.index("qkv")], self.events[2 * STAGES.index("out") + 1]
+        """Milliseconds from the start of stage ``first`` to the end of stage
+        ``last``: the whole call on the GPU (for forward calls the projection
+        stage is recorded first, empty unless the call projects)."""
+        a, b = self.events[2 * self.stages.index(self.first)], self.events[2 * self.stages.index(self.last) + 1]
         self._hip.hipEventSynchronize(b)
         ms = ctypes.c_float(0)
         if self._hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
@@ -328,3 +343,67 @@ class StageTimer:
             if ev:
                 self._hip.hipEventDestroy(ev)
         self.events = None
+
+
+def backward_workspace_size(lay: Layout):
+    lib = load()
+    n = ctypes.c_size_t(0)
+    c = lay.c()
+    _check(lib.hyb_backward_workspace_size(ctypes.byref(c), ctypes.byref(n)))
+    return n.value
+
+
+WEIGHT_GRADS = ("w_gate_soft", "w_gate_lin", "w_out_soft", "w_out_lin", "rms_weight")
+
+
+def backward(lay: Layout, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin,
+             rms_weight, dy, softmax_scale=0.0, eps=1e-6, weight_grads=WEIGHT_GRADS, grads=None,
+             workspace=None, debug=None, stream=None):
+    """Gradients of sum(dy * y) for the layer (bf16 activations), by libhybattn.
+
+    Returns a dict: dx, dq, dk, dv, dtext_k, dtext_v (bf16, contiguous
+    [B, tokens, H, D] / [B, N, hid]) and, for the names in ``weight_grads``,
+    "d" + name as float32 tensors (weights [hid, hid], rms_weight [hid]).
+    ``grads`` may pre-supply any of those output tensors.  ``debug`` may map
+    "d_os", "d_ol" (float32 [B, N, H, D]), "lse2" (float32 [B, H, N]) and
+    "stage_events" (address of 2 * len(BWD_STAGES) hipEvent_t, see
+    ``StageTimer``)."""
+    import torch
+    lib = load()
+    for t in (x, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin, rms_weight, dy):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("x, weights, rms_weight and dy must be contiguous bfloat16 device tensors")
+    B, N, H, D = lay.batch, lay.n_video, lay.heads, lay.head_dim
+    L, hid = lay.text_tokens, lay.hidden
+    out = dict(grads or {})
+    bf = dict(dtype=torch.bfloat16, device=x.device)
+    f32 = dict(dtype=torch.float32, device=x.device)
+    for name, shape in (("dx", (B, N, hid)), ("dq", (B, N, H, D)), ("dk", (B, N, H, D)), ("dv", (B, N, H, D)),
+                        ("dtext_k", (B, L, H, D)), ("dtext_v", (B, L, H, D))):
+        if name not in out:
+            out[name] = torch.empty(shape, **bf)
+    wptr = []
+    for name in WEIGHT_GRADS:
+        key = "d" + name
+        if name in weight_grads:
+            if key not in out:
+                out[key] = torch.empty((hid,) if name == "rms_weight" else (hid, hid), **f32)
+            wptr.append(out[key].data_ptr())
+        else:
+            wptr.append(None)
+    if workspace is None:
+        workspace = torch.empty(backward_workspace_size(lay), dtype=torch.uint8, device=x.device)
+    dbg = None
+    if debug:
+        dbg = _BwdDebug(*([_ptr(debug.get(n)) for n in ("d_os", "d_ol", "lse2")] + [debug.get("stage_events")]))
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    c = lay.c()
+    tptr = [out[n].data_ptr() if out[n].numel() else None for n in ("dtext_k", "dtext_v")]
+    _check(lib.hyb_attn_backward(
+        ctypes.byref(c), x.data_ptr(), _tensor4(q), _tensor4(k), _tensor4(v), _tensor4(text_k), _tensor4(text_v),
+        w_gate_soft.data_ptr(), w_gate_lin.data_ptr(), w_out_soft.data_ptr(), w_out_lin.data_ptr(),
+        rms_weight.data_ptr(), float(softmax_scale), float(eps), dy.data_ptr(), out["dx"].data_ptr(),
+        out["dq"].data_ptr(), out["dk"].data_ptr(), out["dv"].data_ptr(), tptr[0], tptr[1], *wptr,
+        workspace.data_ptr(), workspace.numel(), stream, ctypes.byref(dbg) if dbg is not None else None))
+    return out

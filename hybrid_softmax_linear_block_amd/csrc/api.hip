@@ -533,3 +533,278 @@ hyb_status hyb_block_forward(const hyb_layout* layout, hyb_dtype soft, const voi
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward pass.
+namespace {
+
+enum {
+  B_LSE, B_G16, B_WO, B_WG, B_DYT, B_XT, B_APT, B_DZT, B_WPART, B_DOS, B_DZ, B_DR, B_TC, B_DOL, B_RMSP, B_DVR,
+  B_DQS, B_DKS, B_DVS, B_DTKS, B_DTVS, B_DNUM, B_DDEN, B_LPART, B_DCF, B_DSH, B_DSL, B_DSZ, B_COUNT
+};
+
+constexpr int kWgradSplit = 4;
+
+struct BwdPlan {
+  Plan fwd;
+  size_t off[B_COUNT];
+  size_t total;
+  long long mpad;
+  int rms_blocks, lin_split;
+};
+
+BwdPlan make_bwd_plan(const hyb::Dims& d) {
+  BwdPlan p;
+  p.fwd = make_plan(d, HYB_BF16, HYB_BF16);
+  const size_t M = (size_t)d.B * d.N, hid = d.hid, D = d.D, BH = (size_t)d.B * d.H, E = D * D + D;
+  const size_t ML = (size_t)d.B * d.L;
+  p.mpad = (long long)((M + 64 * kWgradSplit - 1) / (64 * kWgradSplit) * (64 * kWgradSplit));
+  const long long rb = ((long long)M + 3) / 4;
+  p.rms_blocks = (int)(rb < 1024 ? rb : 1024);
+  int split, ts, tsplit;
+  state_split(d, &split, &ts, &tsplit);
+  p.lin_split = split;
+  size_t sz[B_COUNT] = {0};
+  sz[B_LSE] = BH * d.N * 4 + 256;  // padded: the key-centric kernel reads up to 31 rows past a frame
+  sz[B_G16] = M * 2 * hid * 2;
+  sz[B_WO] = 2 * hid * hid * 2;
+  sz[B_WG] = 2 * hid * hid * 2;
+  sz[B_DYT] = hid * (size_t)p.mpad * 2;
+  sz[B_XT] = hid * (size_t)p.mpad * 2;
+  sz[B_APT] = 2 * hid * (size_t)p.mpad * 2;
+  sz[B_DZT] = 2 * hid * (size_t)p.mpad * 2;
+  sz[B_WPART] = (size_t)kWgradSplit * 2 * hid * hid * 4;
+  sz[B_DOS] = M * hid * 2;
+  sz[B_DZ] = M * 2 * hid * 2;
+  sz[B_DR] = M * hid * 2;
+  sz[B_TC] = M * 4;
+  sz[B_DOL] = M * hid * 4;
+  sz[B_RMSP] = (size_t)p.rms_blocks * hid * 4;
+  sz[B_DVR] = BH * d.N * 4 + 256;
+  sz[B_DQS] = M * hid * 4;
+  sz[B_DKS] = M * hid * 4;
+  sz[B_DVS] = M * hid * 4;
+  sz[B_DTKS] = ML * hid * 4;
+  sz[B_DTVS] = ML * hid * 4;
+  sz[B_DNUM] = M * hid * 2;
+  sz[B_DDEN] = M * d.H * 4;
+  sz[B_LPART] = BH * d.T * (size_t)split * E * 4;
+  sz[B_DCF] = BH * d.T * E * 4;
+  sz[B_DSH] = BH * (d.T + 1) * D * D * 2;
+  sz[B_DSL] = BH * (d.T + 1) * D * D * 2;
+  sz[B_DSZ] = BH * (d.T + 1) * D * 4;
+  size_t o = p.fwd.total;
+  for (int i = 0; i < B_COUNT; ++i) {
+    p.off[i] = o;
+    o = align_up(o + sz[i], 256);
+  }
+  p.total = o;
+  return p;
+}
+
+hyb_status check_backward_layout(const hyb_layout* layout) {
+  hyb_status st = check_layout(layout, false);
+  if (st != HYB_OK) return st;
+  if (layout->head_dim != 64 && layout->head_dim != 128)
+    return fail(HYB_ERR_UNSUPPORTED, "the backward pass needs head_dim 64 or 128");
+  if ((long long)layout->heads * layout->head_dim > 16384)
+    return fail(HYB_ERR_UNSUPPORTED, "the backward pass supports hidden sizes up to 16384");
+  return HYB_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+  const char* name;
+};
+
+}  // namespace
+
+extern "C" {
+
+hyb_status hyb_backward_workspace_size(const hyb_layout* layout, size_t* bytes) {
+  g_err[0] = 0;
+  hyb_status st = check_backward_layout(layout);
+  if (st != HYB_OK) return st;
+  if (!bytes) return fail(HYB_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = make_bwd_plan(make_dims(layout)).total;
+  return HYB_OK;
+}
+
+hyb_status hyb_attn_backward(const hyb_layout* layout, const void* x, hyb_tensor q, hyb_tensor k, hyb_tensor v,
+                             hyb_tensor text_k, hyb_tensor text_v, const void* w_gate_soft, const void* w_gate_lin,
+                             const void* w_out_soft, const void* w_out_lin, const void* rms_weight,
+                             float softmax_scale, float eps, const void* dy, void* dx, void* dq, void* dk, void* dv,
+                             void* dtext_k, void* dtext_v, float* dw_gate_soft, float* dw_gate_lin,
+                             float* dw_out_soft, float* dw_out_lin, float* drms_weight, void* workspace,
+                             size_t workspace_bytes, void* stream, const hyb_bwd_debug* dbg) {
+  g_err[0] = 0;
+  hyb_status st = check_backward_layout(layout);
+  if (st != HYB_OK) return st;
+  const hyb::Dims d = make_dims(layout);
+  const bool has_text = d.L > 0;
+  if ((st = check_tensor("q", q, 2, true)) != HYB_OK) return st;
+  if ((st = check_tensor("k", k, 2, true)) != HYB_OK) return st;
+  if ((st = check_tensor("v", v, 2, true)) != HYB_OK) return st;
+  if ((st = check_tensor("text_k", text_k, 2, has_text)) != HYB_OK) return st;
+  if ((st = check_tensor("text_v", text_v, 2, has_text)) != HYB_OK) return st;
+  {
+    const void* req[] = {x, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin, rms_weight, dy, dx, dq, dk, dv,
+                         has_text ? dtext_k : x, has_text ? dtext_v : x, workspace};
+    const char* names[] = {"x", "w_gate_soft", "w_gate_lin", "w_out_soft", "w_out_lin", "rms_weight", "dy", "dx",
+                           "dq", "dk", "dv", "dtext_k", "dtext_v", "workspace"};
+    for (int i = 0; i < 14; ++i) {
+      if (!req[i]) return fail(HYB_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+      if (!aligned(req[i], i == 13 ? 256 : 16))
+        return fail(HYB_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", names[i], i == 13 ? 256 : 16);
+    }
+    const void* opt[] = {dw_gate_soft, dw_gate_lin, dw_out_soft, dw_out_lin, drms_weight};
+    for (int i = 0; i < 5; ++i)
+      if (opt[i] && !aligned(opt[i], 16)) return fail(HYB_ERR_INVALID_ARGUMENT, "weight gradient %d not 16-byte aligned", i);
+  }
+  if (!(eps > 0.f) || !isfinite(eps)) return fail(HYB_ERR_INVALID_ARGUMENT, "eps must be finite and > 0");
+  if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale))
+    return fail(HYB_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  if (dbg) {
+    const void* dp[] = {dbg->d_os, dbg->d_ol, dbg->lse2};
+    for (int i = 0; i < 3; ++i)
+      if (dp[i] && !aligned(dp[i], 16)) return fail(HYB_ERR_INVALID_ARGUMENT, "debug buffer %d not 16-byte aligned", i);
+  }
+  {  // outputs: no overlap with each other or with any input
+    const size_t act = (size_t)d.B * d.N * d.hid * 2, tact = (size_t)d.B * d.L * d.hid * 2, ww = (size_t)d.hid * d.hid * 4;
+    Range outs[] = {{(uintptr_t)dx, (uintptr_t)dx + act, "dx"}, {(uintptr_t)dq, (uintptr_t)dq + act, "dq"},
+                    {(uintptr_t)dk, (uintptr_t)dk + act, "dk"}, {(uintptr_t)dv, (uintptr_t)dv + act, "dv"},
+                    {(uintptr_t)dtext_k, (uintptr_t)dtext_k + tact, "dtext_k"},
+                    {(uintptr_t)dtext_v, (uintptr_t)dtext_v + tact, "dtext_v"},
+                    {(uintptr_t)dw_gate_soft, (uintptr_t)dw_gate_soft + ww, "dw_gate_soft"},
+                    {(uintptr_t)dw_gate_lin, (uintptr_t)dw_gate_lin + ww, "dw_gate_lin"},
+                    {(uintptr_t)dw_out_soft, (uintptr_t)dw_out_soft + ww, "dw_out_soft"},
+                    {(uintptr_t)dw_out_lin, (uintptr_t)dw_out_lin + ww, "dw_out_lin"},
+                    {(uintptr_t)drms_weight, (uintptr_t)drms_weight + (size_t)d.hid * 4, "drms_weight"}};
+    const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
+    Range ins[9];
+    int nin = 0;
+    const hyb_tensor* ts[] = {&q, &k, &v};
+    for (int i = 0; i < 3; ++i) {
+      extent(*ts[i], d.B, d.N, d.H, d.D, 2, &ins[nin].lo, &ins[nin].hi);
+      ins[nin++].name = "q/k/v";
+    }
+    if (has_text) {
+      extent(text_k, d.B, d.L, d.H, d.D, 2, &ins[nin].lo, &ins[nin].hi);
+      ins[nin++].name = "text_k";
+      extent(text_v, d.B, d.L, d.H, d.D, 2, &ins[nin].lo, &ins[nin].hi);
+      ins[nin++].name = "text_v";
+    }
+    ins[nin++] = {(uintptr_t)x, (uintptr_t)x + act, "x"};
+    ins[nin++] = {(uintptr_t)dy, (uintptr_t)dy + act, "dy"};
+    ins[nin++] = {(uintptr_t)workspace, (uintptr_t)workspace + workspace_bytes, "workspace"};
+    for (int i = 0; i < nout; ++i) {
+      if (!outs[i].lo || outs[i].hi == outs[i].lo) continue;
+      for (int j = i + 1; j < nout; ++j)
+        if (outs[j].lo && outs[j].hi > outs[j].lo && outs[i].lo < outs[j].hi && outs[j].lo < outs[i].hi)
+          return fail(HYB_ERR_INVALID_ARGUMENT, "%s overlaps %s", outs[i].name, outs[j].name);
+      for (int j = 0; j < nin; ++j)
+        if (outs[i].lo < ins[j].hi && ins[j].lo < outs[i].hi)
+          return fail(HYB_ERR_INVALID_ARGUMENT, "%s overlaps input %s", outs[i].name, ins[j].name);
+    }
+  }
+  const BwdPlan plan = make_bwd_plan(d);
+  if (workspace_bytes < plan.total)
+    return fail(HYB_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, plan.total);
+
+  char* ws = (char*)workspace;
+  const float tau = softmax_scale > 0.f ? softmax_scale : 1.f / sqrtf((float)d.D);
+  const float sl2 = tau * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+
+  // forward recompute arguments (the forward plan sits at the workspace start)
+  hyb::Bf16Args f;
+  memset(&f, 0, sizeof(f));
+  f.q = t4(q); f.k = t4(k); f.v = t4(v);
+  f.tk = t4(text_k); f.tv = t4(text_v);
+  f.x = (const hyb::bf16_t*)x;
+  f.wgs = (const hyb::bf16_t*)w_gate_soft; f.wgl = (const hyb::bf16_t*)w_gate_lin;
+  f.wos = (const hyb::bf16_t*)w_out_soft; f.wol = (const hyb::bf16_t*)w_out_lin;
+  f.rmsw = (const hyb::bf16_t*)rms_weight;
+  f.scale_log2 = sl2;
+  f.eps = eps;
+  const Plan& fp = plan.fwd;
+  f.os = (uint16_t*)(ws + fp.off[W_OS]);
+  f.ol = (uint16_t*)(ws + fp.off[W_OL]);
+  f.ss = (float*)(ws + fp.off[W_SS]);
+  f.rinv = (float*)(ws + fp.off[W_RINV]);
+  f.part = (float*)(ws + fp.off[W_PART]);
+  f.pre = (float*)(ws + fp.off[W_PRE]);
+  f.comb_hi = (hyb::bf16_t*)(ws + fp.off[W_CHI]);
+  f.comb_lo = (hyb::bf16_t*)(ws + fp.off[W_CLO]);
+  f.comb_z = (float*)(ws + fp.off[W_CZ]);
+  f.ap = (uint16_t*)(ws + fp.off[W_AP]);
+  f.wg_t = (hyb::bf16_t*)(ws + fp.off[W_WG]);
+  f.wo_t = (uint16_t*)(ws + fp.off[W_WO]);
+  f.lse = (float*)(ws + plan.off[B_LSE]);
+  f.gates16 = (uint16_t*)(ws + plan.off[B_G16]);
+  {
+    int split, ts, tsplit;
+    state_split(d, &split, &ts, &tsplit);
+    f.state_split = split;
+    f.text_split = tsplit;
+    f.state_slots = d.T * split + tsplit;
+  }
+
+  hyb::BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = f.q; a.k = f.k; a.v = f.v; a.tk = f.tk; a.tv = f.tv;
+  a.x = f.x; a.wgs = f.wgs; a.wgl = f.wgl; a.wos = f.wos; a.wol = f.wol; a.rmsw = f.rmsw;
+  a.dy = (const hyb::bf16_t*)dy;
+  a.scale_log2 = sl2;
+  a.tau = tau;
+  a.eps = eps;
+  a.os = f.os; a.ol = f.ol; a.ap = f.ap; a.gates16 = f.gates16;
+  a.rinv = f.rinv; a.lse = f.lse;
+  a.comb_hi = f.comb_hi; a.comb_lo = f.comb_lo; a.comb_z = f.comb_z;
+  a.dx = (hyb::bf16_t*)dx; a.dq = (hyb::bf16_t*)dq; a.dk = (hyb::bf16_t*)dk; a.dv = (hyb::bf16_t*)dv;
+  a.dtk = (hyb::bf16_t*)dtext_k; a.dtv = (hyb::bf16_t*)dtext_v;
+  a.dwgs = dw_gate_soft; a.dwgl = dw_gate_lin; a.dwos = dw_out_soft; a.dwol = dw_out_lin; a.drmsw = drms_weight;
+  a.wo_cat = (hyb::bf16_t*)(ws + plan.off[B_WO]);
+  a.wg_cat = (hyb::bf16_t*)(ws + plan.off[B_WG]);
+  a.dyT = (hyb::bf16_t*)(ws + plan.off[B_DYT]);
+  a.xT = (hyb::bf16_t*)(ws + plan.off[B_XT]);
+  a.apT = (hyb::bf16_t*)(ws + plan.off[B_APT]);
+  a.dzT = (hyb::bf16_t*)(ws + plan.off[B_DZT]);
+  a.mpad = plan.mpad;
+  a.ksplit = kWgradSplit;
+  a.wpart = (float*)(ws + plan.off[B_WPART]);
+  a.dos = (hyb::bf16_t*)(ws + plan.off[B_DOS]);
+  a.dz = (hyb::bf16_t*)(ws + plan.off[B_DZ]);
+  a.dr = (hyb::bf16_t*)(ws + plan.off[B_DR]);
+  a.tcoef = (float*)(ws + plan.off[B_TC]);
+  a.dol = (float*)(ws + plan.off[B_DOL]);
+  a.rms_part = (float*)(ws + plan.off[B_RMSP]);
+  a.rms_blocks = plan.rms_blocks;
+  a.dvr = (float*)(ws + plan.off[B_DVR]);
+  a.dq_s = (float*)(ws + plan.off[B_DQS]);
+  a.dk_s = (float*)(ws + plan.off[B_DKS]);
+  a.dv_s = (float*)(ws + plan.off[B_DVS]);
+  a.dtk_s = (float*)(ws + plan.off[B_DTKS]);
+  a.dtv_s = (float*)(ws + plan.off[B_DTVS]);
+  a.dnum = (hyb::bf16_t*)(ws + plan.off[B_DNUM]);
+  a.dden = (float*)(ws + plan.off[B_DDEN]);
+  a.lpart = (float*)(ws + plan.off[B_LPART]);
+  a.lin_split = plan.lin_split;
+  a.dcf = (float*)(ws + plan.off[B_DCF]);
+  a.dsh = (hyb::bf16_t*)(ws + plan.off[B_DSH]);
+  a.dsl = (hyb::bf16_t*)(ws + plan.off[B_DSL]);
+  a.dsz = (float*)(ws + plan.off[B_DSZ]);
+  a.ev = dbg ? (hipEvent_t*)dbg->stage_events : nullptr;
+
+  hipError_t he = hyb::run_bwd_bf16(d, f, a, s);
+  const long long nel = (long long)d.B * d.N * d.hid;
+  if (he == hipSuccess && dbg && dbg->d_os) he = hyb::launch_bf16_to_f32(a.dos, (float*)dbg->d_os, nel, s);
+  if (he == hipSuccess && dbg && dbg->d_ol)
+    he = hipMemcpyAsync(dbg->d_ol, a.dol, (size_t)nel * 4, hipMemcpyDeviceToDevice, s);
+  if (he == hipSuccess && dbg && dbg->lse2)
+    he = hipMemcpyAsync(dbg->lse2, a.lse, (size_t)d.B * d.H * d.N * 4, hipMemcpyDeviceToDevice, s);
+  if (he != hipSuccess) return fail(HYB_ERR_HIP, "HIP error: %s", hipGetErrorString(he));
+  return HYB_OK;
+}
+
+}  // extern "C"

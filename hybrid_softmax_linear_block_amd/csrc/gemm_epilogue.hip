@@ -19,13 +19,15 @@
 
 namespace hyb {
 
-enum { EPI_GATE = 0, EPI_OUT = 1, EPI_QKV = 2 };
+enum { EPI_GATE = 0, EPI_OUT = 1, EPI_QKV = 2, EPI_DA = 3, EPI_RES = 4, EPI_WGRAD = 5 };
 
 struct GemmArgs {
-  const uint16_t* A;   // [M][K] token rows (bf16 or fp16 bits)
-  const uint16_t* Bt;  // [N][K] feature rows (weights transposed, same type)
+  const uint16_t* A;   // [M][ldk] token rows (bf16 or fp16 bits)
+  const uint16_t* Bt;  // [N][ldk] feature rows (weights transposed, same type)
   long long M;
-  int N, K;
+  int N, K;            // K: contraction length of one split
+  int ldk;             // row stride of A and Bt in elements (0: K)
+  int ksplit;          // contraction splits (EPI_WGRAD; 1 otherwise): split z covers [z K, (z+1) K)
   int hid, H;
   // gate epilogue
   const uint16_t *os, *ol;  // fp16 branch outputs [M][hid]
@@ -33,6 +35,7 @@ struct GemmArgs {
   const bf16_t* rmsw;
   uint16_t* ap;
   float* gates_dbg;
+  uint16_t* gates16;  // nullable: [M][2 hid] fp16 copy of the gates (saved for the backward pass)
   // output epilogue
   const bf16_t* x;
   bf16_t* y;
@@ -41,6 +44,13 @@ struct GemmArgs {
   bf16_t *qo, *ko, *vo;
   uint32_t* absmax;
   int B, n_video, D;
+  // backward of the output GEMM (EPI_DA): dA' = dy [W_os; W_ol]^T, then
+  //   c <  hid: dO_s = dA'_s G_s,            dZ_s = dA'_s O_s G_s (1 - G_s)
+  //   c >= hid: dR   = dA'_l G_l,            dZ_l = dA'_l R G_l (1 - G_l),  R = O_l w rinv
+  const uint16_t* gsv;  // [M][2 hid] fp16 saved gates
+  bf16_t *dos, *dz, *dr;  // [M][hid], [M][2 hid], [M][hid] bf16
+  // weight gradients (EPI_WGRAD): fp32 partial sums [ksplit][M][N]
+  float* part;
 };
 
 // WG = WM x WN waves; each wave computes WTM x WFN blocks of 32 x 32 (tokens x
@@ -73,8 +83,15 @@ void k_gemm_bf16(GemmArgs g) {
   // Each XCD takes a contiguous range of tiles (xcd_remap), walked in groups
   // of GM token tiles: the workgroups running together on an XCD share GM
   // rows of A and a run of weight tiles, so both stay in its L2.
-  const unsigned wid = xcd_remap(blockIdx.x, gridDim.x);
+  unsigned wid = xcd_remap(blockIdx.x, gridDim.x);
   const unsigned ntm = (unsigned)((g.M + BM - 1) / BM);
+  const int ldk = g.ldk;
+  unsigned kz = 0;
+  if constexpr (EPI == EPI_WGRAD) {
+    const unsigned tiles = ntm * (unsigned)ntn;
+    kz = wid / tiles;
+    wid -= kz * tiles;
+  }
   const unsigned per_group = (unsigned)GM * (unsigned)ntn;
   const unsigned grp = wid / per_group, in = wid % per_group;
   const unsigned gm0 = grp * GM, gsz = min((unsigned)GM, ntm - gm0);
@@ -90,19 +107,19 @@ void k_gemm_bf16(GemmArgs g) {
   // DMA sources: scalar bases at k = 0, per-lane byte offsets (rows past M
   // repeat the last row; never stored)
   const long long mlast = g.M - 1 - m0;
-  const char* abase = (const char*)(g.A + m0 * g.K);
-  const char* bbase = (const char*)(g.Bt + (long long)n0 * g.K);
+  const char* abase = (const char*)(g.A + m0 * ldk + (long long)kz * g.K);
+  const char* bbase = (const char*)(g.Bt + (long long)n0 * ldk + (long long)kz * g.K);
   unsigned aoff[CA], boff[CB];
 #pragma unroll
   for (int i = 0; i < CA; ++i) {
     const int row = (wave * CA + i) * RPC + lane / G;
     const long long r = row < mlast ? row : mlast;
-    aoff[i] = (unsigned)(r * g.K * 2) + ((lane % G) ^ SW::key(row)) * 16;
+    aoff[i] = (unsigned)(r * ldk * 2) + ((lane % G) ^ SW::key(row)) * 16;
   }
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
     const int row = (wave * CB + i) * RPC + lane / G;
-    boff[i] = (unsigned)((long long)row * g.K * 2) + ((lane % G) ^ SW::key(row)) * 16;
+    boff[i] = (unsigned)((long long)row * ldk * 2) + ((lane % G) ^ SW::key(row)) * 16;
   }
   const unsigned lds0 = lds_addr(lds);
   auto issue = [&](int kt, int stage) {
@@ -170,6 +187,71 @@ void k_gemm_bf16(GemmArgs g) {
       if (kt + 3 < nk) step(kt + 3, std::integral_constant<int, 3 % ST>{});
   }
 
+  if constexpr (EPI == EPI_WGRAD) {
+    // fp32 partial of split kz: lane owns row m, columns n .. n+3
+    float* outp = g.part + (long long)kz * g.M * g.N;
+#pragma unroll
+    for (int i = 0; i < WTM; ++i) {
+      const long long m = m0 + wm * WTM * 32 + i * 32 + l32;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int f = 0; f < WFN; ++f)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const int n = n0 + wn * WFN * 32 + 32 * f + 8 * jg + 4 * half;
+          *(float4*)(outp + m * g.N + n) =
+              make_float4(acc[f][i][4 * jg], acc[f][i][4 * jg + 1], acc[f][i][4 * jg + 2], acc[f][i][4 * jg + 3]);
+        }
+    }
+    return;
+  }
+  if constexpr (EPI == EPI_DA) {
+    // a tile lies in one half of [0, 2 hid) (hid % BN == 0)
+    const bool lin = n0 >= g.hid;
+#pragma unroll
+    for (int i = 0; i < WTM; ++i) {
+      const long long m = m0 + wm * WTM * 32 + i * 32 + l32;
+      if (m >= g.M) continue;
+      const float rinv = lin ? g.rinv[m] : 0.f;
+      float4 ov[WFN][4], gv[WFN][4];
+#pragma unroll
+      for (int f = 0; f < WFN; ++f)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const int n = n0 + wn * WFN * 32 + 32 * f + 8 * jg + 4 * half;
+          gv[f][jg] = load_f16x4(g.gsv + m * (2LL * g.hid) + n);
+          if (!lin) {
+            ov[f][jg] = load_f16x4(g.os + m * g.hid + n);
+          } else {
+            const int c = n - g.hid;
+            const float4 o = load_f16x4(g.ol + m * g.hid + c);
+            const uint2 wv = *(const uint2*)(g.rmsw + c);
+            ov[f][jg] = make_float4(o.x * __uint_as_float(wv.x << 16) * rinv,
+                                    o.y * __uint_as_float(wv.x & 0xffff0000u) * rinv,
+                                    o.z * __uint_as_float(wv.y << 16) * rinv,
+                                    o.w * __uint_as_float(wv.y & 0xffff0000u) * rinv);
+          }
+        }
+#pragma unroll
+      for (int f = 0; f < WFN; ++f)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const int n = n0 + wn * WFN * 32 + 32 * f + 8 * jg + 4 * half;
+          const float a0 = acc[f][i][4 * jg], a1 = acc[f][i][4 * jg + 1];
+          const float a2 = acc[f][i][4 * jg + 2], a3 = acc[f][i][4 * jg + 3];
+          const float4 gg = gv[f][jg], o = ov[f][jg];
+          // dA * gate -> dO_s (softmax half) or dR (linear half)
+          const uint2 dg = make_uint2(pack_bf16x2(a0 * gg.x, a1 * gg.y), pack_bf16x2(a2 * gg.z, a3 * gg.w));
+          // dA * branch value * sigmoid'(z) -> dZ
+          const uint2 dzv = make_uint2(pack_bf16x2(a0 * o.x * gg.x * (1.f - gg.x), a1 * o.y * gg.y * (1.f - gg.y)),
+                                       pack_bf16x2(a2 * o.z * gg.z * (1.f - gg.z), a3 * o.w * gg.w * (1.f - gg.w)));
+          *(uint2*)(g.dz + m * (2LL * g.hid) + n) = dzv;
+          if (!lin) *(uint2*)(g.dos + m * g.hid + n) = dg;
+          else *(uint2*)(g.dr + m * g.hid + (n - g.hid)) = dg;
+        }
+    }
+    return;
+  }
   if constexpr (EPI == EPI_QKV) {
     // q / k / v column block of this tile (hid % BN == 0: one tensor per tile)
     const int t = n0 / g.hid;
@@ -267,6 +349,7 @@ void k_gemm_bf16(GemmArgs g) {
           st.y = pack_f16x2(g2 * val[f][jg].z, g3 * val[f][jg].w);
           *(uint2*)(g.ap + m * (2LL * g.hid) + n) = st;
           if (g.gates_dbg) *(float4*)(g.gates_dbg + m * (2LL * g.hid) + n) = make_float4(g0, g1, g2, g3);
+          if (g.gates16) store_f16x4(g.gates16 + m * (2LL * g.hid) + n, g0, g1, g2, g3);
         }
     } else {
       uint2 xv[WFN][4];
@@ -330,13 +413,19 @@ hipError_t launch_weights_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) 
 }
 
 template <int WM, int WN, int WTM, int WFN, int BK, int ST, int WPE, int EPI, int GM = 1>
-static hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+static hipError_t launch_gemm(GemmArgs g, hipStream_t s) {
   constexpr int BM = WM * WTM * 32, BN = WN * WFN * 32;
-  if (g.N % BN != 0 || g.K % BK != 0 || ((EPI == EPI_GATE || EPI == EPI_QKV) && g.hid % BN != 0))
+  if (g.ldk == 0) g.ldk = g.K;
+  if (g.ksplit < 1 || EPI != EPI_WGRAD) g.ksplit = 1;
+  if (g.N % BN != 0 || g.K % BK != 0 || g.K < BK ||
+      ((EPI == EPI_GATE || EPI == EPI_QKV || EPI == EPI_DA) && g.hid % BN != 0) ||
+      (long long)g.K * g.ksplit > g.ldk)
     return hipErrorInvalidValue;
   // 32-bit per-lane DMA offsets: a tile's rows span < 4 GiB
-  if ((long long)BM * g.K * 2 >= (1LL << 32) || (long long)BN * g.K * 2 >= (1LL << 32)) return hipErrorInvalidValue;
-  const long long grid = ((g.M + BM - 1) / BM) * (g.N / BN);
+  if ((long long)BM * g.ldk * 2 >= (1LL << 32) || (long long)BN * g.ldk * 2 >= (1LL << 32))
+    return hipErrorInvalidValue;
+  const long long grid = ((g.M + BM - 1) / BM) * (g.N / BN) * g.ksplit;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_gemm_bf16<WM, WN, WTM, WFN, BK, ST, WPE, EPI, GM>), dim3((unsigned)grid),
                      dim3(64 * WM * WN), 0, s, g);
   return hipGetLastError();
@@ -362,6 +451,7 @@ hipError_t launch_gate_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s
   g.rmsw = a.rmsw;
   g.ap = a.ap;
   g.gates_dbg = a.gates_dbg;
+  g.gates16 = a.gates16;
   if (d.hid % 256 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_GATE, 4>(g, s);
   if (d.hid % 128 == 0) return launch_gemm<2, 2, 4, 2, 32, 3, 2, EPI_GATE>(g, s);
   return launch_gemm<2, 2, 4, 1, 32, 3, 2, EPI_GATE>(g, s);  // hid multiple of 64 only
@@ -421,6 +511,74 @@ hipError_t launch_out_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s)
   if (g.N % 256 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_OUT, 2>(g, s);
   if (g.N % 128 == 0) return launch_gemm<2, 2, 4, 2, 32, 3, 2, EPI_OUT>(g, s);
   return launch_gemm<2, 2, 4, 1, 32, 3, 2, EPI_OUT>(g, s);
+}
+
+// ---- backward pass ---------------------------------------------------------
+
+// dA' = dy [W_os ; W_ol]^T with the gate / RMSNorm-input gradients in the
+// epilogue.  wo_cat: [2 hid][hid] bf16 = W_os rows then W_ol rows (the
+// [in][out] weights are already the [N][K] operand).
+hipError_t launch_da_gemm(const Dims& d, const bf16_t* dy, const bf16_t* wo_cat, const uint16_t* gsv,
+                          const uint16_t* os, const uint16_t* ol, const float* rinv, const bf16_t* rmsw,
+                          bf16_t* dos, bf16_t* dz, bf16_t* dr, hipStream_t s) {
+  GemmArgs g = {};
+  g.M = (long long)d.B * d.N;
+  g.hid = d.hid;
+  g.H = d.H;
+  g.A = dy;
+  g.Bt = wo_cat;
+  g.N = 2 * d.hid;
+  g.K = d.hid;
+  g.gsv = gsv;
+  g.os = os;
+  g.ol = ol;
+  g.rinv = rinv;
+  g.rmsw = rmsw;
+  g.dos = dos;
+  g.dz = dz;
+  g.dr = dr;
+  if (d.hid % 256 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_DA, 4>(g, s);
+  if (d.hid % 128 == 0) return launch_gemm<2, 2, 4, 2, 32, 3, 2, EPI_DA>(g, s);
+  return launch_gemm<2, 2, 4, 1, 32, 3, 2, EPI_DA>(g, s);
+}
+
+// dx = dy + dZ [W_gs | W_gl]^T.  wg_cat: [hid][2 hid] bf16, row i = (W_gs[i], W_gl[i]).
+hipError_t launch_res_gemm(const Dims& d, const bf16_t* dz, const bf16_t* wg_cat, const bf16_t* dy, bf16_t* dx,
+                           hipStream_t s) {
+  GemmArgs g = {};
+  g.M = (long long)d.B * d.N;
+  g.hid = d.hid;
+  g.H = d.H;
+  g.A = dz;
+  g.Bt = wg_cat;
+  g.N = d.hid;
+  g.K = 2 * d.hid;
+  g.x = dy;
+  g.y = dx;
+  if (g.N % 256 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_RES, 2>(g, s);
+  if (g.N % 128 == 0) return launch_gemm<2, 2, 4, 2, 32, 3, 2, EPI_RES>(g, s);
+  return launch_gemm<2, 2, 4, 1, 32, 3, 2, EPI_RES>(g, s);
+}
+
+// Weight gradient C[Mop][Nop] = sum_t A^T[.][t] B^T[.][t] over t < kpad from
+// token-transposed operands aT [Mop][kpad], bT [Nop][kpad] (bf16, zero past
+// the last token), as ksplit fp32 partials part[ksplit][Mop][Nop].
+// kpad % (64 ksplit) == 0.
+hipError_t launch_wgrad_gemm(const bf16_t* aT, const bf16_t* bT, int Mop, int Nop, long long kpad, int ksplit,
+                             float* part, hipStream_t s) {
+  if (ksplit < 1 || kpad % (64LL * ksplit) != 0 || kpad > 0x7fffffffLL) return hipErrorInvalidValue;
+  GemmArgs g = {};
+  g.M = Mop;
+  g.N = Nop;
+  g.K = (int)(kpad / ksplit);
+  g.ldk = (int)kpad;
+  g.ksplit = ksplit;
+  g.A = aT;
+  g.Bt = bT;
+  g.part = part;
+  if (Nop % 256 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_WGRAD, 4>(g, s);
+  if (Nop % 128 == 0) return launch_gemm<2, 2, 4, 2, 32, 3, 2, EPI_WGRAD>(g, s);
+  return launch_gemm<2, 2, 4, 1, 32, 3, 2, EPI_WGRAD>(g, s);
 }
 
 }  // namespace hyb

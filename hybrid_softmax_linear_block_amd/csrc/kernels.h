@@ -32,6 +32,8 @@ struct Bf16Args {
   float* comb_z;          // [B*H][T][D] combined normaliser vector
   float* pre;             // [B*H][T][D*D+D] forward prefix scratch of the scan
   uint16_t* ap;           // [B*N][2*hid] gated branch outputs, fp16 (output GEMM operand)
+  float* lse;             // nullable: [B][H][N] log2-sum-exp2 of the softmax rows (for the backward)
+  uint16_t* gates16;      // nullable: [B*N][2*hid] fp16 gates (for the backward)
   bf16_t* wg_t;           // [2*hid][hid]  [W_gs | W_gl] transposed, bf16
   uint16_t* wo_t;         // [hid][2*hid]  [W_os ; W_ol] transposed, fp16
   // fp8 softmax branch
@@ -57,6 +59,46 @@ hipError_t launch_qkv_gemm(const Dims& d, const bf16_t* x, const bf16_t* wt, bf1
                            uint32_t* absmax, hipStream_t s);
 // fp16 bits -> float32 (debug copies of the fp16 branch outputs)
 hipError_t launch_f16_to_f32(const uint16_t* src, float* dst, long long n, hipStream_t s);
+
+// ---- backward pass (bf16 activations) ----
+// Forward values it reads are recomputed into the forward workspace by the
+// same kernels (softmax also saving its row log2-sum-exp2, the gate GEMM its
+// gates); the fields below point into that workspace and the backward's own.
+struct BwdArgs {
+  Tensor4 q, k, v, tk, tv;
+  const bf16_t *x, *wgs, *wgl, *wos, *wol, *rmsw, *dy;
+  float scale_log2, tau, eps;
+  // saved forward values
+  const uint16_t *os, *ol, *ap, *gates16;  // fp16 [M][hid], [M][hid], [M][2hid], [M][2hid]
+  const float *rinv, *lse;                 // [M], [B][H][N] (+ padding)
+  const bf16_t *comb_hi, *comb_lo;         // [B*H][T][e][d]
+  const float* comb_z;                     // [B*H][T][D]
+  // outputs (contiguous [B][tokens][H][D] / [B][N][hid]); weight gradients nullable
+  bf16_t *dx, *dq, *dk, *dv, *dtk, *dtv;
+  float *dwgs, *dwgl, *dwos, *dwol, *drmsw;
+  // scratch
+  bf16_t *wo_cat, *wg_cat;                 // [2hid][hid] = [W_os; W_ol], [hid][2hid] rows (W_gs[i], W_gl[i])
+  bf16_t *dyT, *xT, *apT, *dzT;            // token-transposed operands [C][mpad] (zero past M)
+  long long mpad;
+  int ksplit;
+  float* wpart;                            // weight-gradient partials [ksplit][rows][cols]
+  bf16_t *dos, *dz, *dr;                   // [M][hid] dO_s, [M][2hid] dZ, [M][hid] dR (bf16)
+  float *tcoef, *dol;                      // [M] rinv^3 sum(dR w O_l) / hid, [M][hid] dO_l
+  float* rms_part;                         // [rms_blocks][hid]
+  int rms_blocks;
+  float* dvr;                              // [B][H][N] (+ padding) rowsum(dO_s * O_s)
+  float *dq_s, *dk_s, *dv_s, *dtk_s, *dtv_s;  // softmax-branch gradients fp32 [tokens][hid]
+  bf16_t* dnum;                            // [M][hid]
+  float* dden;                             // [M][H]
+  float* lpart;                            // [B*H][T*lin_split][D*D+D]
+  int lin_split;
+  float* dcf;                              // [B*H][T][D*D+D]
+  bf16_t *dsh, *dsl;                       // [B*H][T+1][d][e]
+  float* dsz;                              // [B*H][T+1][D]
+  hipEvent_t* ev;                          // NULL or 2 events per backward stage
+};
+hipError_t run_bwd_bf16(const Dims& d, const Bf16Args& fwd, const BwdArgs& a, hipStream_t s);
+hipError_t launch_bf16_to_f32(const bf16_t* src, float* dst, long long n, hipStream_t s);
 
 // Workspace sizes (bytes) of each buffer in the plans above.
 struct WsPlan {

@@ -18,16 +18,23 @@ namespace hyb {
 // ---------------------------------------------------------------------------
 // State build on MFMA: C[d][e] = sum_t phi(K)[t][d] V[t][e].  The contraction
 // runs over tokens, so both operands come from row-major LDS tiles through
-// the transposing LDS read.  One workgroup = (b, h, slot); a slot is one token
+// the transposing LDS read.  phi(K) is a computed value: it is split into bf16
+// hi + lo and both halves are multiplied (V is exact in bf16), so the states
+// carry near-fp32 products -- the backward pass differentiates through
+// C - c O, which cancels most of C and would magnify a bf16 rounding of phi(K).  One workgroup = (b, h, slot); a slot is one token
 // split of one frame, or one split of the text.  Output per slot (fp32):
-// S transposed [e][d] followed by z[d].
-template <int D>
+// S transposed [e][d] followed by z[d].  With ZW, z accumulates
+// phi(K)[t][d] * zw[t] (per-token weights [B*N][H]); the backward pass uses
+// this form for dC = sum phi(q) dnum^T and dc = sum phi(q) dden.
+template <int D, bool ZW = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2))) void k_states_bf16(Dims d, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv,
-                                                     int split, int ts, float* __restrict__ part, int slots) {
+                                                     int split, int ts, float* __restrict__ part, int slots,
+                                                     const float* __restrict__ zw) {
   constexpr int G = D / 8, GPT = (64 * G) / 256, DB = D / 32;
   constexpr int NB = (DB * DB) / 4;  // 32x32 output blocks per wave
   using SW = Swz<D>;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[64 * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Kl[64 * D];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[64 * D];
   __shared__ float zred[256 / G][D];
 
@@ -69,6 +76,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   // tile loads go to registers one tile ahead: the next tile's loads are in
   // flight while the current tile is multiplied
   uint4 kr[GPT], vr[GPT];
+  float wr[GPT];
   auto load = [&](int tile) {
     const int valid = min(64, cnt - tile * 64);
 #pragma unroll
@@ -77,9 +85,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
       if (row < valid) {
         kr[r] = ldg16(kbase + (long long)(tile * 64 + row) * kst + col);
         vr[r] = ldg16(vbase + (long long)(tile * 64 + row) * vst + col);
+        if constexpr (ZW) wr[r] = zw[((long long)b * d.N + t0 + tile * 64 + row) * d.H + h];
       } else {
         kr[r] = make_uint4(0, 0, 0, 0);
         vr[r] = make_uint4(0, 0, 0, 0);
+        if constexpr (ZW) wr[r] = 0.f;
       }
     }
   };
@@ -92,22 +102,30 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
       const int gi = tid + r * 256, row = gi / G, col = (gi % G) * 8;
       const bool ok = row < valid;
       const uint32_t* u = (const uint32_t*)&kr[r];
-      uint32_t o[4];
+      uint32_t o[4], ol[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float lo = ok ? phi_f(__uint_as_float(u[i] << 16)) : 0.f;
         const float hi = ok ? phi_f(__uint_as_float(u[i] & 0xffff0000u)) : 0.f;
-        zacc[2 * i] += lo;
-        zacc[2 * i + 1] += hi;
+        if constexpr (ZW) {
+          zacc[2 * i] = fmaf(lo, wr[r], zacc[2 * i]);
+          zacc[2 * i + 1] = fmaf(hi, wr[r], zacc[2 * i + 1]);
+        } else {
+          zacc[2 * i] += lo;
+          zacc[2 * i + 1] += hi;
+        }
         o[i] = pack_bf16x2(lo, hi);
+        ol[i] = pack_bf16x2(lo - bf16_to_f32((bf16_t)(o[i] & 0xffffu)), hi - bf16_to_f32((bf16_t)(o[i] >> 16)));
       }
       *(uint4*)&Ks[SW::off(row, col)] = make_uint4(o[0], o[1], o[2], o[3]);
+      *(uint4*)&Kl[SW::off(row, col)] = make_uint4(ol[0], ol[1], ol[2], ol[3]);
       *(uint4*)&Vs[SW::off(row, col)] = vr[r];
     }
     __syncthreads();
     if (tile + 1 < ntile) load(tile + 1);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);  // one 16-token step's operand reads in flight at a time
       const int r0 = kk * 16 + 4 * half + (j16 >> 2);
       const int csub = (grp & 1) * 16 + 4 * (j16 & 3);
 #pragma unroll
@@ -115,8 +133,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
         const int blk = wave * NB + i;
         const int mb = blk / DB, nb = blk % DB;
         const bf16x8 a = tr_pair(&Ks[SW::off(r0, mb * 32 + csub)], &Ks[SW::off(r0 + 8, mb * 32 + csub)]);
+        const bf16x8 al = tr_pair(&Kl[SW::off(r0, mb * 32 + csub)], &Kl[SW::off(r0 + 8, mb * 32 + csub)]);
         const bf16x8 bb = tr_pair(&Vs[SW::off(r0, nb * 32 + csub)], &Vs[SW::off(r0 + 8, nb * 32 + csub)]);
         acc[i] = mfma32(a, bb, acc[i]);
+        acc[i] = mfma32(al, bb, acc[i]);
       }
     }
   }
@@ -315,11 +335,11 @@ hipError_t launch_states_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
   const long long ts = 64LL * ((((long long)d.n + 63) / 64 + a.state_split - 1) / a.state_split);
   const long long grid = (long long)d.B * d.H * a.state_slots;
   if (d.D == 128)
-    hipLaunchKernelGGL(k_states_bf16<128>, dim3((unsigned)grid), dim3(256), 0, s, d, a.k, a.v, a.tk, a.tv,
-                       a.state_split, (int)ts, a.part, a.state_slots);
+    hipLaunchKernelGGL((k_states_bf16<128, false>), dim3((unsigned)grid), dim3(256), 0, s, d, a.k, a.v, a.tk, a.tv,
+                       a.state_split, (int)ts, a.part, a.state_slots, nullptr);
   else
-    hipLaunchKernelGGL(k_states_bf16<64>, dim3((unsigned)grid), dim3(256), 0, s, d, a.k, a.v, a.tk, a.tv,
-                       a.state_split, (int)ts, a.part, a.state_slots);
+    hipLaunchKernelGGL((k_states_bf16<64, false>), dim3((unsigned)grid), dim3(256), 0, s, d, a.k, a.v, a.tk, a.tv,
+                       a.state_split, (int)ts, a.part, a.state_slots, nullptr);
   return hipGetLastError();
 }
 
@@ -361,6 +381,28 @@ hipError_t launch_readout_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) 
   const long long M = (long long)d.B * d.N;
   hipLaunchKernelGGL(k_rms_rinv, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, a.ss, M, d.H, d.hid, a.eps,
                      a.rinv);
+  return hipGetLastError();
+}
+
+// Weighted state build over the video tokens only (backward pass): per
+// (b, h, frame split) partials of sum_t phi(q_t) dnum_t^T ([e][d]) and
+// sum_t phi(q_t) dden_t.  dnum: [B*N][hid] bf16; dden: [B*N][H].
+hipError_t launch_states_weighted(const Dims& d, Tensor4 q, const bf16_t* dnum, const float* dden, int split,
+                                  float* part, hipStream_t s) {
+  const long long ts = 64LL * ((((long long)d.n + 63) / 64 + split - 1) / split);
+  const int slots = d.T * split;
+  const long long grid = (long long)d.B * d.H * slots;
+  Tensor4 dn;
+  dn.p = dnum;
+  dn.sb = d.N * d.hid;
+  dn.st = d.hid;
+  dn.sh = d.D;
+  if (d.D == 128)
+    hipLaunchKernelGGL((k_states_bf16<128, true>), dim3((unsigned)grid), dim3(256), 0, s, d, q, dn, q, dn, split,
+                       (int)ts, part, slots, dden);
+  else
+    hipLaunchKernelGGL((k_states_bf16<64, true>), dim3((unsigned)grid), dim3(256), 0, s, d, q, dn, q, dn, split,
+                       (int)ts, part, slots, dden);
   return hipGetLastError();
 }
 

@@ -133,6 +133,15 @@ def make_projection_weights(w: Workload, seed=None):
     return out
 
 
+def make_grad_output(w: Workload, seed=None):
+    """Seeded gradient of the layer output, dy [B, N, hid] ~ N(0, 1), exact in
+    ``w.act``; drawn from PCG64(seed + 4000)."""
+    seed = w.seed if seed is None else seed
+    g = np.random.Generator(np.random.PCG64(seed + 4000))
+    a = g.standard_normal(size=(w.batch, w.n_video, w.hidden), dtype=np.float32)
+    return _store(a, w.act)
+
+
 def sample_tokens(w: Workload, per_frame=64, seed=None):
     """Seeded sorted sample of video-token indices: ``per_frame`` tokens from
     every frame, always including each frame's first and last token."""

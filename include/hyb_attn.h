@@ -1,6 +1,6 @@
 /*
  * hyb_attn.h -- C ABI of the MI355X (gfx950) VDN-H3 dual-branch hybrid
- * attention layer (forward pass).
+ * attention layer (forward and backward passes).
  *
  * The layer is defined in the VDN-H3 open-source article (tahou.com, article
  * 216474224916730885):
@@ -199,6 +199,63 @@ hyb_status hyb_block_forward(const hyb_layout* layout, hyb_dtype soft, const voi
                              const void* w_out_lin, const void* rms_weight, float softmax_scale, float eps,
                              void* y, void* workspace, size_t workspace_bytes, void* stream,
                              const hyb_debug* dbg);
+
+/*
+ * Backward pass of the layer -- article section "分阶段适配预训练模型" (staged
+ * adaptation): stages A1 and A2 train the new linear branch inside the frozen
+ * denoiser, stage B adds LoRA adapters on the Q/K/V and output projections
+ * and unfreezes the softmax gate; all of them run this pass.  It returns the
+ * chain-rule gradients of L = sum(dy * y) for the forward of
+ * hyb_attn_forward() (bf16 activations, bf16 softmax branch, same readings).
+ *
+ * Stages of one call (see hyb_bwd_debug.stage_events): */
+enum {
+  HYB_BSTAGE_FORWARD = 0,   /* forward recompute: O_s with softmax row statistics, states, O_l, gates, A' */
+  HYB_BSTAGE_EPILOGUE = 1,  /* dA' = dy W_o^T with the gate/RMSNorm-input gradients; dx = dy + dZ W_g^T */
+  HYB_BSTAGE_WGRAD = 2,     /* weight gradients of W_gs, W_gl, W_os, W_ol (those requested) */
+  HYB_BSTAGE_RMS = 3,       /* RMSNorm backward: dO_l and drms_weight */
+  HYB_BSTAGE_SOFTMAX = 4,   /* softmax-branch backward: dq, dk, dv, dtext_k, dtext_v parts */
+  HYB_BSTAGE_LINEAR = 5,    /* linear-branch backward, adds the softmax parts, writes dq, dk, dv, dtext_* */
+  HYB_BSTAGE_COUNT = 6
+};
+
+/* Optional outputs for checking intermediates (each may be NULL):
+ *   d_os  float32 [B, N, H, D]  dL/dO_s (the softmax-branch output)
+ *   d_ol  float32 [B, N, H, D]  dL/dO_l (the linear-branch output, before RMSNorm)
+ *   lse2  float32 [B, H, N]     log2 sum_j exp(tau q_i . k_j) over each query's key set
+ *   stage_events  NULL or 2*HYB_BSTAGE_COUNT hipEvent_t, recorded around each stage */
+typedef struct {
+  void *d_os, *d_ol, *lse2;
+  void* stage_events;
+} hyb_bwd_debug;
+
+/* Bytes of device workspace hyb_attn_backward() needs (bf16 activations). */
+hyb_status hyb_backward_workspace_size(const hyb_layout* layout, size_t* bytes);
+
+/*
+ *   inputs        as hyb_attn_forward() with act = soft = HYB_BF16 (q, k, v,
+ *                 text_k, text_v may be strided views); dy [B, N, hid] bf16
+ *                 contiguous, the gradient of y
+ *   dx            [B, N, hid] bf16: dL/dx (residual + both gate projections)
+ *   dq, dk, dv    [B, N, H, D] bf16 contiguous
+ *   dtext_k, dtext_v [B, L, H, D] bf16 contiguous (may be NULL when L == 0)
+ *   dw_gate_soft, dw_gate_lin, dw_out_soft, dw_out_lin  float32 [hid][hid]
+ *                 ([in][out], like the weights), each NULL when that weight
+ *                 is frozen (its gradient is then not computed)
+ *   drms_weight   float32 [hid] or NULL
+ *   workspace     at least hyb_backward_workspace_size() bytes, 256-byte
+ *                 aligned; contents on entry ignored
+ * All outputs must be 16-byte aligned and must not overlap any input or each
+ * other.  head_dim 64 or 128, hidden size at most 16384.  Enqueued on
+ * `stream`; no synchronisation; same error behaviour as hyb_attn_forward().
+ */
+hyb_status hyb_attn_backward(const hyb_layout* layout, const void* x, hyb_tensor q, hyb_tensor k, hyb_tensor v,
+                             hyb_tensor text_k, hyb_tensor text_v, const void* w_gate_soft, const void* w_gate_lin,
+                             const void* w_out_soft, const void* w_out_lin, const void* rms_weight,
+                             float softmax_scale, float eps, const void* dy, void* dx, void* dq, void* dk, void* dv,
+                             void* dtext_k, void* dtext_v, float* dw_gate_soft, float* dw_gate_lin,
+                             float* dw_out_soft, float* dw_out_lin, float* drms_weight, void* workspace,
+                             size_t workspace_bytes, void* stream, const hyb_bwd_debug* dbg);
 
 /* Static description of a status code. */
 const char* hyb_status_string(hyb_status status);

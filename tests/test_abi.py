@@ -29,7 +29,8 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["hyb_attn_forward", "hyb_last_error", "hyb_layout_tables",
                             "hyb_status_string", "hyb_workspace_size", "hyb_qkv_workspace_size",
-                            "hyb_qkv_project", "hyb_block_workspace_size", "hyb_block_forward"])
+                            "hyb_qkv_project", "hyb_block_workspace_size", "hyb_block_forward",
+                            "hyb_backward_workspace_size", "hyb_attn_backward"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -182,3 +183,56 @@ def test_block_forward_validation_errors():
     n = api.block_workspace_size(lay)
     assert n > api.workspace_size(lay, "bf16") + 3 * 15 * 1024 * 512 * 2
     assert api.block_workspace_size(lay, "fp8") > n
+
+
+def test_backward_validation_errors():
+    """hyb_attn_backward with fake aligned addresses: every bad argument is
+    rejected before anything is launched."""
+    lib = api.load()
+    lay = api.Layout(1, 15, 1024, 128, 8, 64)
+    c = lay.c()
+    base = 1 << 40
+    T4 = api._Tensor
+    st = (15 * 1024 * 512, 512, 64)
+    tst = (128 * 512, 512, 64)
+    slot = iter(range(1, 64))
+
+    def nxt():
+        return base + (next(slot) << 34)
+    a0 = dict(x=nxt(), q=T4(nxt(), *st), k=T4(nxt(), *st), v=T4(nxt(), *st), tk=T4(nxt(), *tst),
+              tv=T4(nxt(), *tst), wgs=nxt(), wgl=nxt(), wos=nxt(), wol=nxt(), rms=nxt(), scale=0.0, eps=1e-6,
+              dy=nxt(), dx=nxt(), dq=nxt(), dk=nxt(), dv=nxt(), dtk=nxt(), dtv=nxt(), dwgs=nxt(), dwgl=nxt(),
+              dwos=nxt(), dwol=nxt(), drms=nxt(), ws=nxt(), wsb=1 << 40)
+
+    def call(lay_c=c, **over):
+        a = dict(a0)
+        a.update(over)
+        r = lib.hyb_attn_backward(ctypes.byref(lay_c), a["x"], a["q"], a["k"], a["v"], a["tk"], a["tv"], a["wgs"],
+                                  a["wgl"], a["wos"], a["wol"], a["rms"], a["scale"], a["eps"], a["dy"], a["dx"],
+                                  a["dq"], a["dk"], a["dv"], a["dtk"], a["dtv"], a["dwgs"], a["dwgl"], a["dwos"],
+                                  a["dwol"], a["drms"], a["ws"], a["wsb"], None, None)
+        return r, lib.hyb_last_error().decode()
+
+    assert call(dy=None)[0] == api.HYB_ERR_INVALID_ARGUMENT
+    assert call(dq=None)[0] == api.HYB_ERR_INVALID_ARGUMENT
+    assert call(dtk=None)[0] == api.HYB_ERR_INVALID_ARGUMENT                 # text present, dtext_k needed
+    assert call(dx=a0["dx"] + 8)[0] == api.HYB_ERR_INVALID_ARGUMENT           # misaligned
+    assert call(dwgs=a0["dwgs"] + 4)[0] == api.HYB_ERR_INVALID_ARGUMENT       # misaligned weight gradient
+    assert call(ws=a0["ws"] + 16)[0] == api.HYB_ERR_INVALID_ARGUMENT          # workspace alignment
+    assert call(eps=float("nan"))[0] == api.HYB_ERR_INVALID_ARGUMENT
+    r, msg = call(dk=a0["dq"] + 4096)                                         # dk overlaps dq
+    assert r == api.HYB_ERR_INVALID_ARGUMENT and "overlaps" in msg
+    r, msg = call(dv=a0["q"].ptr + 1024)                                      # output over an input
+    assert r == api.HYB_ERR_INVALID_ARGUMENT and "overlaps input" in msg
+    r, msg = call(wsb=1000)
+    assert r == api.HYB_ERR_WORKSPACE_TOO_SMALL and "needs" in msg
+    # frozen weights: null gradient pointers are accepted (the call then reaches the
+    # workspace check with the fake sizes)
+    r, msg = call(dwgs=None, dwos=None, drms=None, wsb=1000)
+    assert r == api.HYB_ERR_WORKSPACE_TOO_SMALL
+    bad = api.Layout(1, 15, 64, 16, 2, 32).c()
+    assert call(lay_c=bad)[0] == api.HYB_ERR_UNSUPPORTED                      # head_dim 32
+    big = api.Layout(1, 2, 64, 0, 160, 128).c()
+    assert call(lay_c=big)[0] == api.HYB_ERR_UNSUPPORTED                      # hidden 20480
+    n = api.backward_workspace_size(lay)
+    assert n > api.workspace_size(lay, "bf16")
