@@ -23,13 +23,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from hybrid_softmax_linear_block_amd import api  # noqa: E402
-from hybrid_softmax_linear_block_amd.inputs import (WORKLOADS, make_inputs, make_projection_weights,  # noqa: E402
-                                                    sample_tokens)
+from hybrid_softmax_linear_block_amd.inputs import (WORKLOADS, make_grad_output, make_inputs,  # noqa: E402
+                                                    make_projection_weights, sample_tokens)
 
 WORKLOADS_ID = {w.name: i for i, w in WORKLOADS.items()}
 
 METRIC = "hybrid-attn layer Mtokens/s + softmax-branch TFLOP/s (768p-shaped, bf16)"
 METRIC_BLOCK = "hybrid-attn layer with its Q/K/V projection Mtokens/s (768p-shaped, bf16)"
+METRIC_BWD = "hybrid-attn layer backward (forward recompute + all gradients) Mtokens/s (768p-shaped, bf16)"
 PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense MFMA TFLOP/s, MI355X published
 PEAK_HBM_GBS = 8000.0  # HBM3E, MI355X published
 HBM_PEAK_GBS = 8000.0
@@ -84,6 +85,20 @@ def stage_work(w, soft, block=False):
         # x [B*N][hid] @ [hid][3 hid]: 2 * B*N * hid * 3 hid
         work["qkv"] = ("mfma", 2.0 * B * N * hid * 3 * hid)
     return work
+
+
+def backward_work(w):
+    """Algorithmic work of the backward stages: FLOP of the MFMA products
+    (softmax: S, dP, dQ in the query-centric kernel and S, dP, dV, dK in the
+    key-centric one, 2 D each per visible pair; epilogue: dA' and dx GEMMs;
+    weight gradients: the two token-contraction GEMMs) and the forward
+    recompute (the forward without its output GEMM)."""
+    wc = work_counts(w)
+    B, N, hid = w.batch, w.n_video, w.hidden
+    gemm = 2.0 * B * N * hid * 2 * hid
+    return {"forward": ("mfma", wc["softmax_flop"] + wc["linear_flop"] + gemm),
+            "epilogue": ("mfma", 2 * gemm), "wgrad": ("mfma", 2 * gemm),
+            "softmax": ("mfma", wc["softmax_flop"] * 14.0 / 4.0)}
 
 
 def stage_roofline(w, soft, stage_ms, block=False):
@@ -223,6 +238,66 @@ def device_info(torch):
             "peak_basis": "published MI355X dense peaks (256 CUs, 2.4 GHz)"}
 
 
+def bench_backward(args, w, lay, dev, torch):
+    """Time hyb_attn_backward (forward recompute + every gradient, all weight
+    gradients requested) and print one JSON line."""
+    if w.act != "bf16" or w.soft != "bf16":
+        print("--backward runs the bf16 path", file=sys.stderr)
+        sys.exit(2)
+    dy = torch.from_numpy(make_grad_output(w)).to("cuda").to(torch.bfloat16)
+    ws = torch.empty(api.backward_workspace_size(lay), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    grads = api.backward(lay, dev["x"], dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"], dev["w_gs"],
+                         dev["w_gl"], dev["w_os"], dev["w_ol"], dev["rms_w"], dy, workspace=ws, stream=stream)
+
+    def step(timer=None):
+        api.backward(lay, dev["x"], dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"], dev["w_gs"],
+                     dev["w_gl"], dev["w_os"], dev["w_ol"], dev["rms_w"], dy, grads=grads, workspace=ws,
+                     stream=stream, debug={"stage_events": timer.address} if timer else None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers = [api.StageTimer(api.BWD_STAGES, "forward", "linear") for _ in range(args.steps)]
+    print("bench: timing %d backward steps" % args.steps, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(timers[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = {k: [] for k in api.BWD_STAGES}
+    for t in timers:
+        for k, v in t.elapsed_ms().items():
+            stage[k].append(v)
+        t.close()
+    stage_ms = {k: float(np.mean(v)) for k, v in stage.items()}
+    ms = wall * 1e3 / args.steps
+    work = backward_work(w)
+    roof = {}
+    for k, (bound, flop) in work.items():
+        t = stage_ms.get(k, 0.0)
+        if t > 0:
+            ach = flop / (t * 1e-3) / 1e12
+            roof[k] = {"bound": bound, "algorithmic": flop, "unit": "TFLOP/s", "achieved": round(ach, 2),
+                       "peak": PEAK["bf16"], "frac": round(ach / PEAK["bf16"], 4)}
+    out = {
+        "metric": METRIC_BWD, "value": round(w.batch * w.n_video / (ms * 1e-3) / 1e6, 4), "unit": "Mtokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.act, "data": "synthetic",
+        "config": {"workload": describe(w), "batch": w.batch, "video_tokens": w.n_video,
+                   "text_tokens": w.text_tokens, "heads": w.heads, "head_dim": w.head_dim,
+                   "parallelism": "none (1 GPU)", "weight_gradients": "all"},
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "stage_roofline": roof,
+        "device": device_info(torch),
+        "roofline": dict(roof.get("softmax", {}), kernel="softmax-branch backward (k_attn_bwd_dq + k_attn_bwd_dkv)",
+                         traffic=None),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,6 +307,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block", action="store_true",
                     help="time the layer with its Q/K/V projection (x -> q, k, v -> y) instead of the layer")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (forward recompute + every gradient) instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--write-traffic", metavar="PMC_DIR",
@@ -266,6 +343,9 @@ def main():
     dev = {k: torch.from_numpy(v).to("cuda").to(dt) for k, v in inp.items()}
     lay = layout_of(w)
     soft = "fp8" if w.soft == "fp8" else None
+    if args.backward:
+        bench_backward(args, w, lay, dev, torch)
+        return
     if args.block:
         if w.act != "bf16":
             print("--block runs the bf16 path", file=sys.stderr)

@@ -560,7 +560,7 @@ BwdPlan make_bwd_plan(const hyb::Dims& d) {
   const size_t ML = (size_t)d.B * d.L;
   p.mpad = (long long)((M + 64 * kWgradSplit - 1) / (64 * kWgradSplit) * (64 * kWgradSplit));
   const long long rb = ((long long)M + 3) / 4;
-  p.rms_blocks = (int)(rb < 1024 ? rb : 1024);
+  p.rms_blocks = (int)(rb < 512 ? rb : 512);
   int split, ts, tsplit;
   state_split(d, &split, &ts, &tsplit);
   p.lin_split = split;

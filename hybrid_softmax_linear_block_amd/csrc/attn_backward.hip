@@ -170,7 +170,7 @@ void k_attn_bwd_dq(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 
 // forward's longest-first order.  32 keys per wave, NW waves; query tiles of
 // 32 rows (Q and dO, double buffered in LDS).
 template <int D, int NW>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 void k_attn_bwd_dkv(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv, const bf16_t* __restrict__ dos,
                     const float* __restrict__ lse, const float* __restrict__ dvr, float sl2, float tau,
                     int text_items, float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dtk,
@@ -179,6 +179,8 @@ void k_attn_bwd_dkv(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4
   using Ldr = TileLoader<D, NW, 1>;  // one block of 32 query rows per tile
   __shared__ __attribute__((aligned(16))) bf16_t Qs[2][Ldr::TILE];
   __shared__ __attribute__((aligned(16))) bf16_t Ds[2][Ldr::TILE];
+  __shared__ __attribute__((aligned(16))) float Ls[2][2 * QT];  // per tile: the rows' lse2, then their D
+  __shared__ __attribute__((aligned(16))) bf16_t Vk[KT * D];     // this workgroup's value rows (B operand of dP)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -225,17 +227,22 @@ void k_attn_bwd_dkv(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4
   const bool key_ok = key < nkeys;
   const int keyc = key_ok ? key : nkeys - 1;
 
-  // K^T and V^T fragments of this lane's key (B operands of S and dP)
-  bf16x8 kf[KS], vf[KS];
+  // K^T fragments of this lane's key (B operand of S) in registers; the
+  // workgroup's V rows (B operand of dP) in LDS, which keeps the kernel at two
+  // waves per SIMD
+  bf16x8 kf[KS];
   {
     const bf16_t* kp = text ? (const bf16_t*)tk.p + tok_off(tk, b, keyc, h)
                             : (const bf16_t*)k.p + tok_off(k, b, (long long)g * d.n + keyc, h);
-    const bf16_t* vp = text ? (const bf16_t*)tv.p + tok_off(tv, b, keyc, h)
-                            : (const bf16_t*)v.p + tok_off(v, b, (long long)g * d.n + keyc, h);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      kf[s] = __builtin_bit_cast(bf16x8, ldg16(kp + 8 * half + 16 * s));
-      vf[s] = __builtin_bit_cast(bf16x8, ldg16(vp + 8 * half + 16 * s));
+    for (int s = 0; s < KS; ++s) kf[s] = __builtin_bit_cast(bf16x8, ldg16(kp + 8 * half + 16 * s));
+    constexpr int G = D / 8;
+    for (int ci = tid; ci < KT * G; ci += 64 * NW) {
+      const int r = ci / G, c = (ci % G) * 8;
+      const int kr = min(ktile * KT + r, nkeys - 1);
+      const bf16_t* vp = text ? (const bf16_t*)tv.p + tok_off(tv, b, kr, h)
+                              : (const bf16_t*)v.p + tok_off(v, b, (long long)g * d.n + kr, h);
+      *(uint4*)&Vk[Swz<D>::off(r, c)] = ldg16(vp + c);
     }
   }
 
@@ -263,12 +270,23 @@ void k_attn_bwd_dkv(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4
   const float* lrow = lse + ((long long)b * d.H + h) * d.N;
   const float* drow = dvr + ((long long)b * d.H + h) * d.N;
 
+  // Q and dO rows by direct-to-LDS loads; the rows' lse2 and D (one value per
+  // lane of wave 0, rows past the tile repeat its last row) go through a
+  // register and are written to LDS just before the tile's barrier
+  float lsv = 0.f;
   auto issue = [&](int step, int buf) {
     const int f = frame_at(step / tpf), t0 = (step % tpf) * QT;
     const int valid = min(QT, d.n - t0);
     const long long tok = (long long)f * d.n + t0;
     ldr.load_k(qbase + tok * (q.st * 2), valid, wave, qs_lds + buf * kTileBytes);
     ldr.load_v(dbase + tok * ((long long)d.hid * 2), valid, wave, ds_lds + buf * kTileBytes);
+    if (wave == 0) {
+      const int r = min(l32, valid - 1);
+      lsv = half == 0 ? lrow[tok + r] : drow[tok + r];
+    }
+  };
+  auto publish = [&](int buf) {  // after this wave's loads landed, before the barrier
+    if (wave == 0) Ls[buf][lane] = lsv;
   };
 
   floatx16 dka[DB], dva[DB];
@@ -281,46 +299,51 @@ void k_attn_bwd_dkv(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4
 
   if (nsteps > 0) issue(0, 0);
   wait_vmcnt<0>();
+  publish(0);
   tile_barrier();
   for (int step = 0; step < nsteps; ++step) {
     const int buf = step & 1;
     if (step + 1 < nsteps) issue(step + 1, buf ^ 1);
-    const int f = frame_at(step / tpf), t0 = (step % tpf) * QT;
+    const int t0 = (step % tpf) * QT;
     const int valid = min(QT, d.n - t0);
-    const long long tok = (long long)f * d.n + t0;
-    // this lane's 16 query rows: 8 (j / 4) + 4 half + j % 4; the arrays are
-    // padded past the last token, rows >= valid are dropped below
-    float lv[16], dvv[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const long long r = tok + 8 * (j >> 2) + 4 * half + (j & 3);
-      lv[j] = lrow[r];
-      dvv[j] = drow[r];
-    }
     floatx16 s = zero16(), dp = zero16();
+    // S and dP chains interleaved; two k-steps of operand reads in flight
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
+      if (st % 2 == 0) __builtin_amdgcn_sched_barrier(0);
       const bf16x8 a = *(const bf16x8*)&Qs[buf][Swz<D>::off(l32, 16 * st + 8 * half)];
+      const bf16x8 b = *(const bf16x8*)&Ds[buf][Swz<D>::off(l32, 16 * st + 8 * half)];
+      const bf16x8 vb = *(const bf16x8*)&Vk[Swz<D>::off(wave * 32 + l32, 16 * st + 8 * half)];
       s = mfma32(a, kf[st], s);
+      dp = mfma32(b, vb, dp);
     }
-#pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      const bf16x8 a = *(const bf16x8*)&Ds[buf][Swz<D>::off(l32, 16 * st + 8 * half)];
-      dp = mfma32(a, vf[st], dp);
-    }
+    // this lane's 16 query rows: 8 (j / 4) + 4 half + j % 4; rows >= valid
+    // contribute nothing
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8 pf[2], dsf[2];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int row = 8 * (j >> 2) + 4 * half + (j & 3);
-      const bool ok = row < valid;
-      const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[j], sl2, -lv[j])) : 0.f;
-      const float ds = ok ? p * (dp[j] - dvv[j]) : 0.f;
-      pf[j >> 3][j & 7] = static_cast<__bf16>(p);
-      dsf[j >> 3][j & 7] = static_cast<__bf16>(ds);
+    for (int jg = 0; jg < 4; ++jg) {
+      const float4 l4 = *(const float4*)&Ls[buf][8 * jg + 4 * half];
+      const float4 d4 = *(const float4*)&Ls[buf][QT + 8 * jg + 4 * half];
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 4 * jg + r;
+        const bool ok = 8 * jg + 4 * half + r < valid;
+        const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[j], sl2, -lv[r])) : 0.f;
+        const float ds = ok ? p * (dp[j] - dvv[r]) : 0.f;
+        pf[j >> 3][j & 7] = static_cast<__bf16>(p);
+        dsf[j >> 3][j & 7] = static_cast<__bf16>(ds);
+      }
     }
+    // phase boundaries keep each phase's operand reads from being hoisted
+    // into the previous one (register pressure at two waves per SIMD)
+    __builtin_amdgcn_sched_barrier(0);
     pv_tile<D, 1>(dva, Ds[buf], pf, half, j16, dsub);
+    __builtin_amdgcn_sched_barrier(0);
     pv_tile<D, 1>(dka, Qs[buf], dsf, half, j16, dsub);
     wait_vmcnt<0>();
+    if (step + 1 < nsteps) publish(buf ^ 1);
     tile_barrier();
   }
   if (!key_ok) return;

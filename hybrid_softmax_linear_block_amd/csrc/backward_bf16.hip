@@ -166,14 +166,19 @@ __global__ __launch_bounds__(256) void k_rms_back(const bf16_t* __restrict__ dr,
   }
 }
 
-// out[c] = sum_r part[r][c]
+// out[c] = sum_r part[r][c]: 64 columns per workgroup, its four waves sum
+// interleaved rows, then one LDS combine (fixed order).
 __global__ __launch_bounds__(256) void k_colsum(const float* __restrict__ part, int rows, int cols,
                                                 float* __restrict__ out) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= cols) return;
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
   float v = 0.f;
-  for (int r = 0; r < rows; ++r) v += part[(long long)r * cols + c];
-  out[c] = v;
+  if (c < cols)
+    for (int r = wave; r < rows; r += 4) v += part[(long long)r * cols + c];
+  red[wave][lane] = v;
+  __syncthreads();
+  if (wave == 0 && c < cols) out[c] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
 }
 
 __global__ __launch_bounds__(256) void k_bf16_to_f32(const bf16_t* __restrict__ src, float* __restrict__ dst,
@@ -241,7 +246,7 @@ hipError_t run_bwd_bf16(const Dims& d, const Bf16Args& f, const BwdArgs& a, hipS
                        a.tcoef, M, hid, a.dol, a.rms_part);
     HYB_TRY(hipGetLastError());
     if (a.drmsw) {
-      hipLaunchKernelGGL(k_colsum, dim3((unsigned)((hid + 255) / 256)), dim3(256), 0, s, a.rms_part, a.rms_blocks,
+      hipLaunchKernelGGL(k_colsum, dim3((unsigned)((hid + 63) / 64)), dim3(256), 0, s, a.rms_part, a.rms_blocks,
                          hid, a.drmsw);
       HYB_TRY(hipGetLastError());
     }

@@ -8,8 +8,9 @@ sum |gpu - ref| / sum |ref|.  The HIP path rounds some operands to bf16
 bf16; P and dS enter the softmax products in bf16; every output is bf16.
 One such rounding gives a mean relative error of about 1.4e-3 (measured on
 dL/dO_s, which passes through exactly one).  The computed operands of the
-linear branch (the states, phi(q), phi(k), dnum) are split into bf16 hi + lo
-and add nothing at this level.  The longest paths (dq, dk, dtext_k: dO_s or
+linear branch (the states, phi(q), phi(k), and dnum where it multiplies the
+states) are split into bf16 hi + lo and add nothing at this level; the copy
+of dnum summed into the state gradients is bf16, averaged over a frame.  The longest paths (dq, dk, dtext_k: dO_s or
 dR, then dS, then the output) pass through three roundings, so their mean
 error is at most about 3 x 1.4e-3 = 4.2e-3: bound 5e-3.  The max bound is the
 forward's, 1e-2.  Measured: mean 1.4e-3 to 3.2e-3, max at most 5.1e-3.
