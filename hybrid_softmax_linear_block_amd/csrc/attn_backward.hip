@@ -23,6 +23,8 @@
 //                   S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS.
 // Both reuse the forward's MFMA tile products; every operand order is the one
 // the previous MFMA's register layout gives (no transposes in registers).
+#include <type_traits>
+
 #include "attn_tiles.h"
 #include "work_items.h"
 
@@ -270,8 +272,8 @@ void k_attn_bwd_dkv(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4
   const float* lrow = lse + ((long long)b * d.H + h) * d.N;
   const float* drow = dvr + ((long long)b * d.H + h) * d.N;
 
-  // Q and dO rows by direct-to-LDS loads; the rows' lse2 and D (one value per
-  // lane of wave 0, rows past the tile repeat its last row) go through a
+  // Q and dO rows by direct-to-LDS loads (rows past the tile repeat its last
+  // row); the rows' lse2 and D (one value per lane of wave 0) go through a
   // register and are written to LDS just before the tile's barrier
   float lsv = 0.f;
   auto issue = [&](int step, int buf) {
@@ -280,9 +282,10 @@ void k_attn_bwd_dkv(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4
     const long long tok = (long long)f * d.n + t0;
     ldr.load_k(qbase + tok * (q.st * 2), valid, wave, qs_lds + buf * kTileBytes);
     ldr.load_v(dbase + tok * ((long long)d.hid * 2), valid, wave, ds_lds + buf * kTileBytes);
-    if (wave == 0) {
-      const int r = min(l32, valid - 1);
-      lsv = half == 0 ? lrow[tok + r] : drow[tok + r];
+    if (wave == 0) {  // rows past the tile: lse2 = +inf and D = 0, so P = dS = 0 there
+      const bool ok = l32 < valid;
+      const float vl = half == 0 ? lrow[tok + (ok ? l32 : 0)] : drow[tok + (ok ? l32 : 0)];
+      lsv = ok ? vl : (half == 0 ? INFINITY : 0.f);
     }
   };
   auto publish = [&](int buf) {  // after this wave's loads landed, before the barrier
@@ -304,8 +307,6 @@ void k_attn_bwd_dkv(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4
   for (int step = 0; step < nsteps; ++step) {
     const int buf = step & 1;
     if (step + 1 < nsteps) issue(step + 1, buf ^ 1);
-    const int t0 = (step % tpf) * QT;
-    const int valid = min(QT, d.n - t0);
     floatx16 s = zero16(), dp = zero16();
     // S and dP chains interleaved; two k-steps of operand reads in flight
 #pragma unroll
@@ -317,8 +318,7 @@ void k_attn_bwd_dkv(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4
       s = mfma32(a, kf[st], s);
       dp = mfma32(b, vb, dp);
     }
-    // this lane's 16 query rows: 8 (j / 4) + 4 half + j % 4; rows >= valid
-    // contribute nothing
+    // this lane's 16 query rows: 8 (j / 4) + 4 half + j % 4
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 pf[2], dsf[2];
 #pragma unroll
@@ -329,11 +329,9 @@ void k_attn_bwd_dkv(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 4 * jg + r;
-        const bool ok = 8 * jg + 4 * half + r < valid;
-        const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[j], sl2, -lv[r])) : 0.f;
-        const float ds = ok ? p * (dp[j] - dvv[r]) : 0.f;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[j], sl2, -lv[r]));
         pf[j >> 3][j & 7] = static_cast<__bf16>(p);
-        dsf[j >> 3][j & 7] = static_cast<__bf16>(ds);
+        dsf[j >> 3][j & 7] = static_cast<__bf16>(p * (dp[j] - dvv[r]));
       }
     }
     // phase boundaries keep each phase's operand reads from being hoisted
