@@ -133,6 +133,20 @@ def make_projection_weights(w: Workload, seed=None):
     return out
 
 
+def make_ffn_weights(w: Workload, seed=None, expansion=4):
+    """Seeded feed-forward weights of the block: w_n [hid] = 1 + 0.1 N(0, 1)
+    (RMSNorm weight), w_1 [hid, F], w_2 [F, hid] ~ N(0, weight_std^2) with
+    F = expansion * hid, exact in ``w.act``; drawn from PCG64(seed + 5000)."""
+    seed = w.seed if seed is None else seed
+    g = np.random.Generator(np.random.PCG64(seed + 5000))
+    hid = w.hidden
+    F = expansion * hid
+    w_n = np.float32(1.0) + np.float32(0.1) * g.standard_normal(size=hid, dtype=np.float32)
+    w_1 = g.standard_normal(size=(hid, F), dtype=np.float32) * np.float32(w.weight_std)
+    w_2 = g.standard_normal(size=(F, hid), dtype=np.float32) * np.float32(w.weight_std)
+    return {"w_n": _store(w_n, w.act), "w_1": _store(w_1, w.act), "w_2": _store(w_2, w.act)}
+
+
 def make_grad_output(w: Workload, seed=None):
     """Seeded gradient of the layer output, dy [B, N, hid] ~ N(0, 1), exact in
     ``w.act``; drawn from PCG64(seed + 4000)."""

@@ -37,6 +37,11 @@ Parity status per function (what pins it, in ``tests/test_oracle_*.py``):
                                       and for the whole layer, on three frame
                                       layouts; planted mistakes are caught.
   backward.softmax_lse                pinned: closed forms (q = 0, constant keys).
+  dit.gelu_tanh / rmsnorm / ffn /     pinned: torch's tanh GELU and its limits,
+  dit_block                           RMSNorm hand example and scale
+                                      invariance, zero / identity / one-hot
+                                      feed-forward weights, composition with
+                                      the layer oracle.
   Anchor frames as queries (they attend to every frame): parity unpinned --
   the article says only that anchors interact with the other frames.
 """
@@ -45,3 +50,4 @@ from .hybrid import (phi, softmax_branch, linear_states, linear_branch,  # noqa:
                      epilogue, hybrid_forward)
 from . import projection  # noqa: F401
 from . import backward  # noqa: F401
+from . import dit  # noqa: F401
