@@ -23,13 +23,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from hybrid_softmax_linear_block_amd import api  # noqa: E402
-from hybrid_softmax_linear_block_amd.inputs import (WORKLOADS, make_grad_output, make_inputs,  # noqa: E402
-                                                    make_projection_weights, sample_tokens)
+from hybrid_softmax_linear_block_amd.inputs import (WORKLOADS, make_ffn_weights, make_grad_output,  # noqa: E402
+                                                    make_inputs, make_projection_weights, sample_tokens)
 
 WORKLOADS_ID = {w.name: i for i, w in WORKLOADS.items()}
 
 METRIC = "hybrid-attn layer Mtokens/s + softmax-branch TFLOP/s (768p-shaped, bf16)"
 METRIC_BLOCK = "hybrid-attn layer with its Q/K/V projection Mtokens/s (768p-shaped, bf16)"
+METRIC_DIT = "DiT block (Q/K/V projection + hybrid layer + feed-forward) Mtokens/s (768p-shaped, bf16)"
 METRIC_BWD = "hybrid-attn layer backward (forward recompute + all gradients) Mtokens/s (768p-shaped, bf16)"
 PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense MFMA TFLOP/s, MI355X published
 PEAK_HBM_GBS = 8000.0  # HBM3E, MI355X published
@@ -60,7 +61,7 @@ def work_counts(w):
             "layer_flop": soft + states + readout + gemm}
 
 
-def stage_work(w, soft, block=False):
+def stage_work(w, soft, block=False, ffn_hidden=0):
     """Algorithmic work per stage of the bf16 path: FLOP for the MFMA
     kernels, the HBM bytes each kernel must move for the others (inputs read
     once, outputs written once, intermediates in the formats the path uses)."""
@@ -84,6 +85,9 @@ def stage_work(w, soft, block=False):
     if block:
         # x [B*N][hid] @ [hid][3 hid]: 2 * B*N * hid * 3 hid
         work["qkv"] = ("mfma", 2.0 * B * N * hid * 3 * hid)
+    if ffn_hidden:
+        # two GEMMs, [B*N][hid] @ [hid][F] and [B*N][F] @ [F][hid]
+        work["ffn"] = ("mfma", 2 * 2.0 * B * N * hid * ffn_hidden)
     return work
 
 
@@ -101,9 +105,9 @@ def backward_work(w):
             "softmax": ("mfma", wc["softmax_flop"] * 14.0 / 4.0)}
 
 
-def stage_roofline(w, soft, stage_ms, block=False):
+def stage_roofline(w, soft, stage_ms, block=False, ffn_hidden=0):
     out = {}
-    for k, (bound, amount) in stage_work(w, soft, block).items():
+    for k, (bound, amount) in stage_work(w, soft, block, ffn_hidden).items():
         t = stage_ms.get(k, 0.0)
         if t <= 0:
             continue
@@ -307,6 +311,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--block", action="store_true",
                     help="time the layer with its Q/K/V projection (x -> q, k, v -> y) instead of the layer")
+    ap.add_argument("--dit", action="store_true",
+                    help="time one DiT block: projection, layer and the feed-forward (4 x hid)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (forward recompute + every gradient) instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -346,12 +352,18 @@ def main():
     if args.backward:
         bench_backward(args, w, lay, dev, torch)
         return
+    ffn_hidden = 4 * w.hidden if args.dit else 0
+    if args.dit:
+        args.block = True
     if args.block:
         if w.act != "bf16":
-            print("--block runs the bf16 path", file=sys.stderr)
+            print("--block and --dit run the bf16 path", file=sys.stderr)
             sys.exit(2)
         pw = {k: torch.from_numpy(v).to("cuda").to(dt) for k, v in make_projection_weights(w).items()}
         ws_bytes = api.block_workspace_size(lay, soft)
+        if args.dit:
+            fw = {k: torch.from_numpy(v).to("cuda").to(dt) for k, v in make_ffn_weights(w).items()}
+            ws_bytes = api.dit_block_workspace_size(lay, ffn_hidden, soft)
     else:
         ws_bytes = api.workspace_size(lay, "f32" if w.act == "f32" else "bf16", soft)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
@@ -360,7 +372,11 @@ def main():
 
     def step(timer=None):
         dbg = {"stage_events": timer.address} if timer else None
-        if args.block:
+        if args.dit:
+            api.dit_block_forward(lay, dev["x"], pw["w_q"], pw["w_k"], pw["w_v"], dev["text_k"], dev["text_v"],
+                                  dev["w_gs"], dev["w_gl"], dev["w_os"], dev["w_ol"], dev["rms_w"], fw["w_n"],
+                                  fw["w_1"], fw["w_2"], soft=soft, z=y, workspace=ws, stream=stream, debug=dbg)
+        elif args.block:
             api.block_forward(lay, dev["x"], pw["w_q"], pw["w_k"], pw["w_v"], dev["text_k"], dev["text_v"],
                               dev["w_gs"], dev["w_gl"], dev["w_os"], dev["w_ol"], dev["rms_w"], soft=soft, y=y,
                               workspace=ws, stream=stream, debug=dbg)
@@ -372,7 +388,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    timers = [api.StageTimer() for _ in range(args.steps)]
+    timers = [api.StageTimer(last="ffn" if args.dit else "out") for _ in range(args.steps)]
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -392,7 +408,8 @@ def main():
     def pct(v):
         p10, p50, p90 = np.percentile(np.asarray(v), [10, 50, 90])
         return {"p10": round(float(p10), 4), "p50": round(float(p50), 4), "p90": round(float(p90), 4)}
-    stage_ms = {k: float(np.mean(v)) for k, v in stage.items() if args.block or k != "qkv"}
+    stage_ms = {k: float(np.mean(v)) for k, v in stage.items()
+                if (args.block or k != "qkv") and (args.dit or k != "ffn")}
     ms = wall * 1e3 / args.steps
     wc = work_counts(w)
     soft_key = "softmax_fp8" if soft else "softmax"
@@ -400,9 +417,10 @@ def main():
     soft_tflops = wc["softmax_flop"] / (soft_ms * 1e-3) / 1e12
     peak = PEAK["fp8" if soft else w.act]
     value = w.batch * w.n_video / (ms * 1e-3) / 1e6
-    layer_flop = wc["layer_flop"] + (stage_work(w, soft, True)["qkv"][1] if args.block else 0.0)
+    sw = stage_work(w, soft, True, ffn_hidden)
+    layer_flop = wc["layer_flop"] + (sw["qkv"][1] if args.block else 0.0) + (sw["ffn"][1] if args.dit else 0.0)
     out = {
-        "metric": METRIC_BLOCK if args.block else METRIC, "value": round(value, 4), "unit": "Mtokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC_DIT if args.dit else (METRIC_BLOCK if args.block else METRIC), "value": round(value, 4), "unit": "Mtokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.act, "data": "synthetic",
         "config": {"workload": describe(w), "batch": w.batch, "video_tokens": w.n_video,
@@ -412,7 +430,7 @@ def main():
         "layer_tflops": round(layer_flop / (ms * 1e-3) / 1e12, 2),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "gpu_ms_percentiles": {"forward": pct(span), "softmax": pct(stage["softmax"])},
-        "stage_roofline": stage_roofline(w, soft, stage_ms, args.block) if w.act != "f32" else None,
+        "stage_roofline": stage_roofline(w, soft, stage_ms, args.block, ffn_hidden) if w.act != "f32" else None,
         "device": device_info(torch),
         "roofline": {"kernel": "k_attn_bf16_sp (softmax branch)" if not soft else "softmax branch fp8",
                      "bound": "mfma", "achieved": round(soft_tflops, 2), "peak": peak, "unit": "TFLOP/s",

@@ -39,7 +39,7 @@ class _Debug(ctypes.Structure):
                                                 "stage_events")]
 
 
-STAGES = ("weights", "quant", "softmax", "states", "scan", "readout", "gate", "out", "qkv")
+STAGES = ("weights", "quant", "softmax", "states", "scan", "readout", "gate", "out", "qkv", "ffn")
 BWD_STAGES = ("forward", "epilogue", "wgrad", "rms", "softmax", "linear")
 
 
@@ -108,6 +108,14 @@ def load(path=None):
     lib.hyb_block_forward.argtypes = (
         [ctypes.POINTER(_Layout), ctypes.c_int] + [ctypes.c_void_p] * 4 + [_Tensor] * 2 + [ctypes.c_void_p] * 5
         + [ctypes.c_float, ctypes.c_float]
+        + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(_Debug)])
+    lib.hyb_dit_block_workspace_size.restype = ctypes.c_int
+    lib.hyb_dit_block_workspace_size.argtypes = [ctypes.POINTER(_Layout), ctypes.c_int, ctypes.c_int32,
+                                                 ctypes.POINTER(ctypes.c_size_t)]
+    lib.hyb_dit_block_forward.restype = ctypes.c_int
+    lib.hyb_dit_block_forward.argtypes = (
+        [ctypes.POINTER(_Layout), ctypes.c_int] + [ctypes.c_void_p] * 4 + [_Tensor] * 2 + [ctypes.c_void_p] * 8
+        + [ctypes.c_int32, ctypes.c_float, ctypes.c_float]
         + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(_Debug)])
     lib.hyb_backward_workspace_size.restype = ctypes.c_int
     lib.hyb_backward_workspace_size.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(ctypes.c_size_t)]
@@ -407,3 +415,47 @@ def backward(lay: Layout, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin, w
         out["dq"].data_ptr(), out["dk"].data_ptr(), out["dv"].data_ptr(), tptr[0], tptr[1], *wptr,
         workspace.data_ptr(), workspace.numel(), stream, ctypes.byref(dbg) if dbg is not None else None))
     return out
+
+
+def dit_block_workspace_size(lay: Layout, ffn_hidden, soft=None):
+    lib = load()
+    n = ctypes.c_size_t(0)
+    c = lay.c()
+    _check(lib.hyb_dit_block_workspace_size(ctypes.byref(c), DTYPES[soft or "bf16"], int(ffn_hidden),
+                                            ctypes.byref(n)))
+    return n.value
+
+
+def dit_block_forward(lay: Layout, x, w_q, w_k, w_v, text_k, text_v, w_gate_soft, w_gate_lin, w_out_soft,
+                      w_out_lin, rms_weight, ffn_norm_weight, w_ff1, w_ff2, soft=None, softmax_scale=0.0,
+                      eps=1e-6, z=None, workspace=None, debug=None, stream=None):
+    """One block: z = y + GELU_tanh(RMSNorm(y) W_1) W_2 with y the layer with
+    its Q/K/V projection (bf16).  Arguments as in ``block_forward`` plus the
+    feed-forward weights ffn_norm_weight [hid], w_ff1 [hid, F], w_ff2 [F, hid]."""
+    import torch
+    lib = load()
+    for t in (x, w_q, w_k, w_v, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin, rms_weight, ffn_norm_weight,
+              w_ff1, w_ff2):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("x, weights and norm weights must be contiguous bfloat16 device tensors")
+    F = w_ff1.shape[1]
+    if tuple(w_ff1.shape) != (lay.hidden, F) or tuple(w_ff2.shape) != (F, lay.hidden):
+        raise ValueError("w_ff1 must be [hid, F] and w_ff2 [F, hid]")
+    if z is None:
+        z = torch.empty_like(x)
+    if workspace is None:
+        workspace = torch.empty(dit_block_workspace_size(lay, F, soft), dtype=torch.uint8, device=x.device)
+    dbg = None
+    if debug:
+        dbg = _Debug(*([_ptr(debug.get(n)) for n in ("o_soft", "o_lin", "delta_f32", "gates", "scales")]
+                       + [debug.get("stage_events")]))
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    c = lay.c()
+    _check(lib.hyb_dit_block_forward(
+        ctypes.byref(c), DTYPES[soft or "bf16"], x.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), w_v.data_ptr(),
+        _tensor4(text_k), _tensor4(text_v), w_gate_soft.data_ptr(), w_gate_lin.data_ptr(), w_out_soft.data_ptr(),
+        w_out_lin.data_ptr(), rms_weight.data_ptr(), ffn_norm_weight.data_ptr(), w_ff1.data_ptr(),
+        w_ff2.data_ptr(), int(F), float(softmax_scale), float(eps), z.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), stream, ctypes.byref(dbg) if dbg is not None else None))
+    return z

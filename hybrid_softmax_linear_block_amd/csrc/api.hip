@@ -356,6 +356,11 @@ hyb_status attn_forward_impl(const hyb_layout* layout, hyb_dtype act, hyb_dtype 
     if (he == hipSuccess && dbg && dbg->o_lin)
       he = hipMemcpyAsync(dbg->o_lin, ws + plan.off[W_OL], bytes, hipMemcpyDeviceToDevice, s);
   }
+  if (he == hipSuccess && dbg && dbg->stage_events) {  // no feed-forward here: empty interval
+    hipEvent_t* ev = (hipEvent_t*)dbg->stage_events;
+    he = hipEventRecord(ev[2 * HYB_STAGE_FFN], s);
+    if (he == hipSuccess) he = hipEventRecord(ev[2 * HYB_STAGE_FFN + 1], s);
+  }
   if (he != hipSuccess) return fail(HYB_ERR_HIP, "HIP error: %s", hipGetErrorString(he));
   return HYB_OK;
 }
@@ -803,6 +808,106 @@ hyb_status hyb_attn_backward(const hyb_layout* layout, const void* x, hyb_tensor
     he = hipMemcpyAsync(dbg->d_ol, a.dol, (size_t)nel * 4, hipMemcpyDeviceToDevice, s);
   if (he == hipSuccess && dbg && dbg->lse2)
     he = hipMemcpyAsync(dbg->lse2, a.lse, (size_t)d.B * d.H * d.N * 4, hipMemcpyDeviceToDevice, s);
+  if (he != hipSuccess) return fail(HYB_ERR_HIP, "HIP error: %s", hipGetErrorString(he));
+  return HYB_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// DiT block: projection + layer + feed-forward.
+namespace {
+
+struct DitPlan {
+  BlockPlan block;
+  size_t y, h, u, w1t, w2t, total;
+};
+
+DitPlan make_dit_plan(const hyb::Dims& d, hyb_dtype soft, int F) {
+  DitPlan p;
+  p.block = make_block_plan(d, soft);
+  const size_t M = (size_t)d.B * d.N, hid = d.hid;
+  size_t o = p.block.total;
+  p.y = o; o = align_up(o + M * hid * 2, 256);
+  p.h = o; o = align_up(o + M * hid * 2, 256);
+  p.u = o; o = align_up(o + M * (size_t)F * 2, 256);
+  p.w1t = o; o = align_up(o + (size_t)F * hid * 2, 256);
+  p.w2t = o; o = align_up(o + (size_t)F * hid * 2, 256);
+  p.total = o;
+  return p;
+}
+
+hyb_status check_dit(const hyb_layout* layout, hyb_dtype soft, int32_t F) {
+  hyb_status st = check_projection(layout);
+  if (st != HYB_OK) return st;
+  st = check_dtypes(layout, HYB_BF16, soft);
+  if (st != HYB_OK) return st;
+  if (F <= 0 || F % 64) return fail(HYB_ERR_INVALID_ARGUMENT, "ffn_hidden must be a positive multiple of 64 (got %d)", F);
+  return HYB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hyb_status hyb_dit_block_workspace_size(const hyb_layout* layout, hyb_dtype soft, int32_t ffn_hidden,
+                                        size_t* bytes) {
+  g_err[0] = 0;
+  hyb_status st = check_dit(layout, soft, ffn_hidden);
+  if (st != HYB_OK) return st;
+  if (!bytes) return fail(HYB_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = make_dit_plan(make_dims(layout), soft, ffn_hidden).total;
+  return HYB_OK;
+}
+
+hyb_status hyb_dit_block_forward(const hyb_layout* layout, hyb_dtype soft, const void* x, const void* w_q,
+                                 const void* w_k, const void* w_v, hyb_tensor text_k, hyb_tensor text_v,
+                                 const void* w_gate_soft, const void* w_gate_lin, const void* w_out_soft,
+                                 const void* w_out_lin, const void* rms_weight, const void* ffn_norm_weight,
+                                 const void* w_ff1, const void* w_ff2, int32_t ffn_hidden, float softmax_scale,
+                                 float eps, void* z, void* workspace, size_t workspace_bytes, void* stream,
+                                 const hyb_debug* dbg) {
+  g_err[0] = 0;
+  hyb_status st = check_dit(layout, soft, ffn_hidden);
+  if (st != HYB_OK) return st;
+  const void* ptrs[] = {ffn_norm_weight, w_ff1, w_ff2, z, workspace};
+  const char* names[] = {"ffn_norm_weight", "w_ff1", "w_ff2", "z", "workspace"};
+  for (int i = 0; i < 5; ++i) {
+    if (!ptrs[i]) return fail(HYB_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+    if (!aligned(ptrs[i], i == 4 ? 256 : 16))
+      return fail(HYB_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", names[i], i == 4 ? 256 : 16);
+  }
+  const hyb::Dims d = make_dims(layout);
+  const DitPlan p = make_dit_plan(d, soft, ffn_hidden);
+  if (workspace_bytes < p.total)
+    return fail(HYB_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, p.total);
+  char* ws = (char*)workspace;
+  // projection + layer into the workspace's y (validates the remaining arguments)
+  st = hyb_block_forward(layout, soft, x, w_q, w_k, w_v, text_k, text_v, w_gate_soft, w_gate_lin, w_out_soft,
+                         w_out_lin, rms_weight, softmax_scale, eps, ws + p.y, workspace, p.block.total, stream, dbg);
+  if (st != HYB_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t* ev = dbg ? (hipEvent_t*)dbg->stage_events : nullptr;
+  hipError_t he = hipSuccess;
+  if (ev) he = hipEventRecord(ev[2 * HYB_STAGE_FFN], s);
+  if (he == hipSuccess) {
+    hyb::FfnArgs a;
+    a.M = (long long)d.B * d.N;
+    a.hid = d.hid;
+    a.F = ffn_hidden;
+    a.eps = eps;
+    a.y = (const hyb::bf16_t*)(ws + p.y);
+    a.wn = (const hyb::bf16_t*)ffn_norm_weight;
+    a.w1 = (const hyb::bf16_t*)w_ff1;
+    a.w2 = (const hyb::bf16_t*)w_ff2;
+    a.h = (hyb::bf16_t*)(ws + p.h);
+    a.u = (hyb::bf16_t*)(ws + p.u);
+    a.w1t = (hyb::bf16_t*)(ws + p.w1t);
+    a.w2t = (hyb::bf16_t*)(ws + p.w2t);
+    a.z = (hyb::bf16_t*)z;
+    he = hyb::run_ffn_bf16(a, s);
+  }
+  if (he == hipSuccess && ev) he = hipEventRecord(ev[2 * HYB_STAGE_FFN + 1], s);
   if (he != hipSuccess) return fail(HYB_ERR_HIP, "HIP error: %s", hipGetErrorString(he));
   return HYB_OK;
 }

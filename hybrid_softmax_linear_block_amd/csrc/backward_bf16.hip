@@ -65,8 +65,8 @@ __global__ __launch_bounds__(256) void k_transpose_tok(const uint16_t* __restric
   }
 }
 
-static hipError_t transpose_tok(const uint16_t* src, bool f16, long long M, int C, long long mpad, bf16_t* dst,
-                                hipStream_t s) {
+hipError_t transpose_tok(const uint16_t* src, bool f16, long long M, int C, long long mpad, bf16_t* dst,
+                         hipStream_t s) {
   const long long blocks = (mpad / 64) * ((C + 63) / 64);
   if (blocks > 0x7fffffffLL || mpad % 64) return hipErrorInvalidValue;
   if (f16)

@@ -19,7 +19,7 @@
 
 namespace hyb {
 
-enum { EPI_GATE = 0, EPI_OUT = 1, EPI_QKV = 2, EPI_DA = 3, EPI_RES = 4, EPI_WGRAD = 5 };
+enum { EPI_GATE = 0, EPI_OUT = 1, EPI_QKV = 2, EPI_DA = 3, EPI_RES = 4, EPI_WGRAD = 5, EPI_GELU = 6 };
 
 struct GemmArgs {
   const uint16_t* A;   // [M][ldk] token rows (bf16 or fp16 bits)
@@ -51,7 +51,17 @@ struct GemmArgs {
   bf16_t *dos, *dz, *dr;  // [M][hid], [M][2 hid], [M][hid] bf16
   // weight gradients (EPI_WGRAD): fp32 partial sums [ksplit][M][N]
   float* part;
+  // feed-forward (EPI_GELU): out[M][N] = bf16(GELU_tanh(acc))
+  bf16_t* out;
 };
+
+// GELU, tanh form: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))), with
+// tanh(a) = 1 - 2 / (exp(2a) + 1) (saturates correctly for large |a|).
+__device__ __forceinline__ float gelu_tanh_f(float u) {
+  const float a = 0.7978845608028654f * fmaf(0.044715f * u, u * u, u);
+  const float t = 1.f - 2.f / (__expf(2.f * a) + 1.f);
+  return 0.5f * u * (1.f + t);
+}
 
 // WG = WM x WN waves; each wave computes WTM x WFN blocks of 32 x 32 (tokens x
 // features).  BK-deep k-tiles live in an ST-stage LDS ring filled by
@@ -201,6 +211,23 @@ void k_gemm_bf16(GemmArgs g) {
           const int n = n0 + wn * WFN * 32 + 32 * f + 8 * jg + 4 * half;
           *(float4*)(outp + m * g.N + n) =
               make_float4(acc[f][i][4 * jg], acc[f][i][4 * jg + 1], acc[f][i][4 * jg + 2], acc[f][i][4 * jg + 3]);
+        }
+    }
+    return;
+  }
+  if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+    for (int i = 0; i < WTM; ++i) {
+      const long long m = m0 + wm * WTM * 32 + i * 32 + l32;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int f = 0; f < WFN; ++f)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const int n = n0 + wn * WFN * 32 + 32 * f + 8 * jg + 4 * half;
+          *(uint2*)(g.out + m * g.N + n) =
+              make_uint2(pack_bf16x2(gelu_tanh_f(acc[f][i][4 * jg]), gelu_tanh_f(acc[f][i][4 * jg + 1])),
+                         pack_bf16x2(gelu_tanh_f(acc[f][i][4 * jg + 2]), gelu_tanh_f(acc[f][i][4 * jg + 3])));
         }
     }
     return;
@@ -356,7 +383,7 @@ void k_gemm_bf16(GemmArgs g) {
 #pragma unroll
       for (int f = 0; f < WFN; ++f)
 #pragma unroll
-        for (int jg = 0; jg < 4; ++jg) xv[f][jg] = *(const uint2*)(g.x + m * g.hid + nw + 32 * f + 8 * jg);
+        for (int jg = 0; jg < 4; ++jg) xv[f][jg] = *(const uint2*)(g.x + m * g.N + nw + 32 * f + 8 * jg);
 #pragma unroll
       for (int f = 0; f < WFN; ++f)
 #pragma unroll
@@ -367,8 +394,8 @@ void k_gemm_bf16(GemmArgs g) {
           uint2 st;
           st.x = pack_bf16x2(__uint_as_float(xv[f][jg].x << 16) + c0, __uint_as_float(xv[f][jg].x & 0xffff0000u) + c1);
           st.y = pack_bf16x2(__uint_as_float(xv[f][jg].y << 16) + c2, __uint_as_float(xv[f][jg].y & 0xffff0000u) + c3);
-          *(uint2*)(g.y + m * g.hid + n) = st;
-          if (g.delta_dbg) *(float4*)(g.delta_dbg + m * g.hid + n) = make_float4(c0, c1, c2, c3);
+          *(uint2*)(g.y + m * g.N + n) = st;
+          if (g.delta_dbg) *(float4*)(g.delta_dbg + m * g.N + n) = make_float4(c0, c1, c2, c3);
         }
     }
   }
@@ -579,6 +606,41 @@ hipError_t launch_wgrad_gemm(const bf16_t* aT, const bf16_t* bT, int Mop, int No
   if (Nop % 256 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_WGRAD, 4>(g, s);
   if (Nop % 128 == 0) return launch_gemm<2, 2, 4, 2, 32, 3, 2, EPI_WGRAD>(g, s);
   return launch_gemm<2, 2, 4, 1, 32, 3, 2, EPI_WGRAD>(g, s);
+}
+
+// ---- feed-forward of the block ------------------------------------------------
+
+// out[M][F] = GELU_tanh(h W_1): h [M][hid], w1t [F][hid] (W_1 transposed), bf16.
+hipError_t launch_gelu_gemm(long long M, int hid, int F, const bf16_t* h, const bf16_t* w1t, bf16_t* out,
+                            hipStream_t s) {
+  GemmArgs g = {};
+  g.M = M;
+  g.N = F;
+  g.K = hid;
+  g.hid = hid;
+  g.A = h;
+  g.Bt = w1t;
+  g.out = out;
+  if (F % 256 == 0 && hid % 64 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_GELU, 4>(g, s);
+  if (F % 128 == 0 && hid % 32 == 0) return launch_gemm<2, 2, 4, 2, 32, 3, 2, EPI_GELU>(g, s);
+  return launch_gemm<2, 2, 4, 1, 32, 3, 2, EPI_GELU>(g, s);
+}
+
+// out[M][N] = resid + A Bt^T: A [M][K], bt [N][K], resid / out [M][N], bf16.
+hipError_t launch_resid_gemm(long long M, int N, int K, const bf16_t* a, const bf16_t* bt, const bf16_t* resid,
+                             bf16_t* out, hipStream_t s) {
+  GemmArgs g = {};
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.hid = N;
+  g.A = a;
+  g.Bt = bt;
+  g.x = resid;
+  g.y = out;
+  if (N % 256 == 0 && K % 64 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_RES, 2>(g, s);
+  if (N % 128 == 0 && K % 32 == 0) return launch_gemm<2, 2, 4, 2, 32, 3, 2, EPI_RES>(g, s);
+  return launch_gemm<2, 2, 4, 1, 32, 3, 2, EPI_RES>(g, s);
 }
 
 }  // namespace hyb

@@ -100,6 +100,19 @@ struct BwdArgs {
 hipError_t run_bwd_bf16(const Dims& d, const Bf16Args& fwd, const BwdArgs& a, hipStream_t s);
 hipError_t launch_bf16_to_f32(const bf16_t* src, float* dst, long long n, hipStream_t s);
 
+// ---- feed-forward of the block (dit_block.hip) ----
+// z = y + GELU_tanh(RMSNorm(y) W_1) W_2 for y [M][hid] bf16; weights [in][out]
+// bf16 (w_1 [hid][F], w_2 [F][hid]), w_n [hid]; scratch: h [M][hid],
+// u [M][F], w1t [F][hid], w2t [hid][F] (bf16).
+struct FfnArgs {
+  long long M;
+  int hid, F;
+  float eps;
+  const bf16_t *y, *wn, *w1, *w2;
+  bf16_t *h, *u, *w1t, *w2t, *z;
+};
+hipError_t run_ffn_bf16(const FfnArgs& a, hipStream_t s);
+
 // Workspace sizes (bytes) of each buffer in the plans above.
 struct WsPlan {
   size_t off[24];

@@ -27,5 +27,13 @@ hipError_t launch_states_weighted(const Dims& d, Tensor4 q, const bf16_t* dnum, 
                                   float* part, hipStream_t s);
 hipError_t launch_softmax_backward(const Dims& d, const BwdArgs& a, hipStream_t s);
 hipError_t launch_linear_backward(const Dims& d, const BwdArgs& a, hipStream_t s);
+// src [M][C] (bf16, or fp16 when f16) -> dst [C][mpad] bf16, zero past M; mpad % 64 == 0
+hipError_t transpose_tok(const uint16_t* src, bool f16, long long M, int C, long long mpad, bf16_t* dst,
+                         hipStream_t s);
+// feed-forward of the block
+hipError_t launch_gelu_gemm(long long M, int hid, int F, const bf16_t* h, const bf16_t* w1t, bf16_t* out,
+                            hipStream_t s);
+hipError_t launch_resid_gemm(long long M, int N, int K, const bf16_t* a, const bf16_t* bt, const bf16_t* resid,
+                             bf16_t* out, hipStream_t s);
 
 }  // namespace hyb

@@ -96,7 +96,8 @@ enum {
   HYB_STAGE_GATE = 6,      /* gate GEMM + RMSNorm/gating epilogue */
   HYB_STAGE_OUT = 7,       /* output GEMM + residual */
   HYB_STAGE_QKV = 8,       /* Q/K/V projection (hyb_block_forward only; recorded first) */
-  HYB_STAGE_COUNT = 9
+  HYB_STAGE_FFN = 9,       /* feed-forward of the block (hyb_dit_block_forward only; recorded last) */
+  HYB_STAGE_COUNT = 10
 };
 
 /* Optional float32 copies of intermediate results (each pointer may be NULL):
@@ -256,6 +257,33 @@ hyb_status hyb_attn_backward(const hyb_layout* layout, const void* x, hyb_tensor
                              void* dtext_k, void* dtext_v, float* dw_gate_soft, float* dw_gate_lin,
                              float* dw_out_soft, float* dw_out_lin, float* drms_weight, void* workspace,
                              size_t workspace_bytes, void* stream, const hyb_bwd_debug* dbg);
+
+/*
+ * One DiT block around the layer -- article section "分阶段适配预训练模型": a
+ * block of the denoiser has Q/K/V/O projections and a feed-forward network.
+ * The article describes no more of the block; this library's reading:
+ *   y = hyb_block_forward(x)                      (projection + layer, bf16)
+ *   z = y + GELU_tanh(RMSNorm(y) W_1) W_2         (RMSNorm over hid with
+ *                                                  ffn_norm_weight and eps;
+ *                                                  no biases)
+ *   ffn_norm_weight [hid]; w_ff1 [hid][ffn_hidden]; w_ff2 [ffn_hidden][hid]
+ *   (bf16, [in][out]); ffn_hidden a positive multiple of 64 (4 * hid in the
+ *   usual block).  z [B, N, hid] bf16 may alias x.  Other arguments as in
+ *   hyb_block_forward(); the workspace (hyb_dit_block_workspace_size())
+ *   also holds y, the normalised y, the GELU output and the transposed
+ *   feed-forward weights; dbg's stage_events include HYB_STAGE_FFN.
+ * Timestep modulation and cross-attention are not in the article and are not
+ * part of the block.
+ */
+hyb_status hyb_dit_block_workspace_size(const hyb_layout* layout, hyb_dtype soft, int32_t ffn_hidden,
+                                        size_t* bytes);
+hyb_status hyb_dit_block_forward(const hyb_layout* layout, hyb_dtype soft, const void* x, const void* w_q,
+                                 const void* w_k, const void* w_v, hyb_tensor text_k, hyb_tensor text_v,
+                                 const void* w_gate_soft, const void* w_gate_lin, const void* w_out_soft,
+                                 const void* w_out_lin, const void* rms_weight, const void* ffn_norm_weight,
+                                 const void* w_ff1, const void* w_ff2, int32_t ffn_hidden, float softmax_scale,
+                                 float eps, void* z, void* workspace, size_t workspace_bytes, void* stream,
+                                 const hyb_debug* dbg);
 
 /* Static description of a status code. */
 const char* hyb_status_string(hyb_status status);

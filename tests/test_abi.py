@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol():
     assert names == sorted(["hyb_attn_forward", "hyb_last_error", "hyb_layout_tables",
                             "hyb_status_string", "hyb_workspace_size", "hyb_qkv_workspace_size",
                             "hyb_qkv_project", "hyb_block_workspace_size", "hyb_block_forward",
-                            "hyb_backward_workspace_size", "hyb_attn_backward"])
+                            "hyb_backward_workspace_size", "hyb_attn_backward",
+                            "hyb_dit_block_workspace_size", "hyb_dit_block_forward"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -236,3 +237,34 @@ def test_backward_validation_errors():
     assert call(lay_c=big)[0] == api.HYB_ERR_UNSUPPORTED                      # hidden 20480
     n = api.backward_workspace_size(lay)
     assert n > api.workspace_size(lay, "bf16")
+
+
+def test_dit_block_validation_errors():
+    lib = api.load()
+    lay = api.Layout(1, 15, 1024, 128, 8, 64)
+    c = lay.c()
+    base = 1 << 40
+    T4 = api._Tensor
+    st = (128 * 512, 512, 64)
+
+    def call(**over):
+        a = dict(soft=1, x=base, wq=base + (1 << 34), wk=base + (2 << 34), wv=base + (3 << 34),
+                 tk=T4(base + (4 << 34), *st), tv=T4(base + (5 << 34), *st), wgs=base + (6 << 34),
+                 wgl=base + (7 << 34), wos=base + (8 << 34), wol=base + (9 << 34), rms=base + (10 << 34),
+                 wn=base + (11 << 34), w1=base + (12 << 34), w2=base + (13 << 34), F=2048, scale=0.0, eps=1e-6,
+                 z=base + (14 << 34), ws=base + (15 << 34), wsb=1 << 40)
+        a.update(over)
+        return lib.hyb_dit_block_forward(ctypes.byref(c), a["soft"], a["x"], a["wq"], a["wk"], a["wv"], a["tk"],
+                                         a["tv"], a["wgs"], a["wgl"], a["wos"], a["wol"], a["rms"], a["wn"],
+                                         a["w1"], a["w2"], a["F"], a["scale"], a["eps"], a["z"], a["ws"],
+                                         a["wsb"], None, None)
+
+    assert call(w1=None) == api.HYB_ERR_INVALID_ARGUMENT
+    assert call(wn=base + 2) == api.HYB_ERR_INVALID_ARGUMENT              # misaligned
+    assert call(F=100) == api.HYB_ERR_INVALID_ARGUMENT                    # not a multiple of 64
+    assert call(F=0) == api.HYB_ERR_INVALID_ARGUMENT
+    assert call(wsb=1000) == api.HYB_ERR_WORKSPACE_TOO_SMALL
+    assert call(wq=None) == api.HYB_ERR_INVALID_ARGUMENT                  # checked by the block call, pre-launch
+    n = api.dit_block_workspace_size(lay, 2048)
+    M, hid = 15 * 1024, 512
+    assert n >= api.block_workspace_size(lay) + 2 * M * hid * 2 + M * 2048 * 2 + 2 * 2048 * hid * 2
