@@ -35,7 +35,16 @@ METRIC_BWD = "hybrid-attn layer backward (forward recompute + all gradients) Mto
 PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense MFMA TFLOP/s, MI355X published
 PEAK_HBM_GBS = 8000.0  # HBM3E, MI355X published
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = {"softmax": "attn_softmax.hip", "softmax_fp8": "fp8_softmax.hip"}
+# source files whose text determines each measured kernel (hashed together)
+KERNEL_SOURCES = {"softmax": ("attn_softmax.hip", "attn_tiles.h", "mfma_common.h", "work_items.h"),
+                  "softmax_fp8": ("fp8_softmax.hip", "mfma_common.h", "work_items.h")}
+
+
+def sources_sha256(kernel_key):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel_key]:
+        h.update(open(os.path.join(ROOT, "hybrid_softmax_linear_block_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
 
 
 def layout_of(w):
@@ -139,8 +148,7 @@ def traffic_for(kernel_key, workload):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, "hybrid_softmax_linear_block_amd", "csrc", KERNEL_SOURCES[kernel_key])
-    if rec.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    if rec.get("source_sha256") != sources_sha256(kernel_key):
         return None
     return rec.get("bytes_per_launch")
 
@@ -172,11 +180,11 @@ def write_traffic(pmc_dir, w):
     w_scale = copy_kib * ncw / cw if cw else None
     rd = fetch / nf * 1024 * f_scale
     wr = write / nw * 1024 * w_scale
-    src = os.path.join(ROOT, "hybrid_softmax_linear_block_amd", "csrc", KERNEL_SOURCES["softmax"])
     rec = {"kernel": "k_attn_bf16_sp", "workload": w.name, "bytes_per_launch": rd + wr,
            "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
            "fetch_scale": f_scale, "write_scale": w_scale,
-           "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+           "sources": list(KERNEL_SOURCES["softmax"]),
+           "source_sha256": sources_sha256("softmax"),
            "commands": ["rocprofv3 --pmc FETCH_SIZE --kernel-include-regex k_attn_bf16 --output-format csv "
                         "-d PMC_DIR/fetch -o fetch -- python3 bench.py --workload %d --steps 1 --warmup 0 "
                         "--no-cpu-baseline" % WORKLOADS_ID[w.name],
