@@ -242,3 +242,51 @@ def hybrid_backward(inp, lay, dy, scale=None, eps=1e-6):
                 "d_os": d_os, "d_ol": d_ol,
                 "lse": softmax_lse(inp["q"], inp["k"], inp["text_k"], lay, scale=scale)})
     return out
+
+
+def dq_dx_at(inp, lay, dy, tokens, states=None, scale=None, eps=1e-6):
+    """dq and dx at a sample of video tokens only (each is a function of its
+    own row given the layer's frame states): the epilogue backward of those
+    rows, then the softmax rows' dQ over their key sets and the linear
+    readout's dq.  Returns (dq [B, len, H, D], dx [B, len, hid])."""
+    from .hybrid import linear_branch, softmax_branch
+    q, k, v, tk, tv = inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"]
+    B, N, H, D = q.shape
+    n = lay.tokens_per_frame
+    tau = 1.0 / math.sqrt(D) if not scale else float(scale)
+    rows = np.asarray(tokens, np.int64)
+    st = states if states is not None else linear_states(k, v, tk, tv, lay)
+    o_s = softmax_branch(q, k, v, tk, tv, lay, scale=scale, tokens=rows)
+    o_l = linear_branch(q, st, lay, eps=eps, tokens=rows)
+    ep = epilogue_backward(np.asarray(inp["x"])[:, rows], o_s, o_l, inp["w_gs"], inp["w_gl"], inp["w_os"],
+                           inp["w_ol"], inp["rms_w"], np.asarray(dy)[:, rows], eps=eps)
+    d_os = ep["d_os"].reshape(B, rows.size, H, D)
+    d_ol = ep["d_ol"].reshape(B, rows.size, H, D)
+    sets = frame_sets(lay.frames, lay.chunk_frames, lay.chunk_radius, lay.anchor_first, lay.anchor_last)
+    Sf, zf, Sb, zb = directional_states(st, lay)
+    dq = np.zeros((B, rows.size, H, D))
+    for f in range(lay.frames):
+        sel = np.nonzero(rows // n == f)[0]
+        if sel.size == 0:
+            continue
+        kt = _key_tokens(lay, sets[f][0])
+        for b in range(B):
+            for h in range(H):
+                K = np.concatenate([np.asarray(k[b, kt, h], np.float64), np.asarray(tk[b, :, h], np.float64)])
+                V = np.concatenate([np.asarray(v[b, kt, h], np.float64), np.asarray(tv[b, :, h], np.float64)])
+                C = Sf[b, h, f] + Sb[b, h, f]
+                c = zf[b, h, f] + zb[b, h, f]
+                for i in sel:
+                    qi = np.asarray(q[b, rows[i], h], np.float64)
+                    sc = tau * (K @ qi)
+                    p = np.exp(sc - sc.max())
+                    p /= p.sum()
+                    dO = d_os[b, i, h]
+                    ds = p * (V @ dO - np.dot(dO, o_s[b, i, h]))
+                    pq = phi(qi)
+                    den = pq @ c + eps
+                    O = (pq @ C) / den
+                    g = d_ol[b, i, h]
+                    dpq = C @ (g / den) - c * (np.dot(g, O) / den)
+                    dq[b, i, h] = tau * (ds @ K) + dpq * dphi(qi)
+    return dq, ep["dx"]

@@ -107,3 +107,45 @@ def test_frozen_weights_are_not_written_and_rest_unchanged():
         assert np.array_equal(full[k], part[k]), k
     assert "dw_gate_soft" not in part and "dw_out_soft" not in part
     torch.cuda.synchronize()
+
+
+def test_backward_head_major_strides_bit_identical():
+    """q, k, v, text_k, text_v as head-major [B, H, tokens, D] storage viewed
+    as [B, tokens, H, D]: the same gradients bit for bit."""
+    import torch
+    w = CASES[1]
+    inp = make_inputs(w)
+    dy = make_grad_output(w)
+    base = run_backward(w, inp, dy)
+    d = {k: _dev(v) for k, v in inp.items()}
+    for name in ("q", "k", "v", "text_k", "text_v"):
+        d[name] = d[name].permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)   # strided view
+    g = api.backward(gu.api_layout(w), d["x"], d["q"], d["k"], d["v"], d["text_k"], d["text_v"], d["w_gs"],
+                     d["w_gl"], d["w_os"], d["w_ol"], d["rms_w"], _dev(dy))
+    torch.cuda.synchronize()
+    for k_, v_ in g.items():
+        assert np.array_equal(v_.float().cpu().numpy().astype(np.float64), base[k_]), k_
+
+
+def test_backward_768p_sampled():
+    """768p shape, the bench's launch configuration: dq and dx on sampled
+    tokens against the oracle evaluated one token at a time (full states)."""
+    import torch
+    from hybrid_softmax_linear_block_amd.inputs import sample_tokens
+    w = WORKLOADS[3]
+    inp = make_inputs(w)
+    dy = make_grad_output(w)
+    d = {k: _dev(v) for k, v in inp.items()}
+    g = api.backward(gu.api_layout(w), d["x"], d["q"], d["k"], d["v"], d["text_k"], d["text_v"], d["w_gs"],
+                     d["w_gl"], d["w_os"], d["w_ol"], d["rms_w"], _dev(dy), weight_grads=())
+    torch.cuda.synchronize()
+    tok = sample_tokens(w, per_frame=6)
+    t = torch.from_numpy(tok).to("cuda")
+    dq = g["dq"][:, t].float().cpu().numpy().astype(np.float64)
+    dx = g["dx"][:, t].float().cpu().numpy().astype(np.float64)
+    del g
+    rq, rx = obw.dq_dx_at(inp, gu.oracle_layout(w), dy, tok)
+    for name, got, ref in (("dq", dq, rq), ("dx", dx, rx)):
+        e = gu.errors(got, ref)
+        print("768p", name, "max %.2e mean %.2e" % e, flush=True)
+        assert e[0] <= TOL_GRAD[0] and e[1] <= TOL_GRAD[1], (name, e)

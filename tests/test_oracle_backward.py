@@ -197,3 +197,15 @@ def test_planted_mistakes_are_caught(mut):
         if caught:
             break
     assert caught, mut
+
+
+def test_dq_dx_at_sampled_tokens_equal_full_backward():
+    """The per-token form used at full size equals the full backward on the
+    sampled rows (it restates the same reverse steps one row at a time)."""
+    lay = LAYOUTS[1]
+    inp, dy = make(lay, 500)
+    full = BW.hybrid_backward(inp, lay, dy)
+    tok = np.array([0, 3, 7, 10, lay.n_video - 1])
+    dq, dx = BW.dq_dx_at(inp, lay, dy, tok)
+    assert np.allclose(dq, full["dq"][:, tok], rtol=1e-10, atol=1e-12)
+    assert np.allclose(dx, full["dx"][:, tok], rtol=1e-10, atol=1e-12)
