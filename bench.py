@@ -31,6 +31,7 @@ WORKLOADS_ID = {w.name: i for i, w in WORKLOADS.items()}
 METRIC = "hybrid-attn layer Mtokens/s + softmax-branch TFLOP/s (768p-shaped, bf16)"
 METRIC_BLOCK = "hybrid-attn layer with its Q/K/V projection Mtokens/s (768p-shaped, bf16)"
 METRIC_DIT = "DiT block (Q/K/V projection + hybrid layer + feed-forward) Mtokens/s (768p-shaped, bf16)"
+METRIC_TRAIN = "hybrid-attn layer training step (forward keeping its values + backward) Mtokens/s (768p-shaped, bf16)"
 METRIC_BWD = "hybrid-attn layer backward (forward recompute + all gradients) Mtokens/s (768p-shaped, bf16)"
 PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense MFMA TFLOP/s, MI355X published
 PEAK_HBM_GBS = 8000.0  # HBM3E, MI355X published
@@ -259,23 +260,35 @@ def bench_backward(args, w, lay, dev, torch):
     dy = torch.from_numpy(make_grad_output(w)).to("cuda").to(torch.bfloat16)
     ws = torch.empty(api.backward_workspace_size(lay), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
-    grads = api.backward(lay, dev["x"], dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"], dev["w_gs"],
-                         dev["w_gl"], dev["w_os"], dev["w_ol"], dev["rms_w"], dy, workspace=ws, stream=stream)
+    lay_args = (lay, dev["x"], dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"], dev["w_gs"], dev["w_gl"],
+                dev["w_os"], dev["w_ol"], dev["rms_w"])
+    saved = y = fws = None
+    fwd_timers = []
+    if args.train:
+        saved = torch.empty(api.saved_size(lay), dtype=torch.uint8, device="cuda")
+        fws = torch.empty(api.workspace_size(lay, "bf16"), dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(dev["x"])
+    grads = api.backward(*lay_args, dy, workspace=ws, stream=stream)
 
-    def step(timer=None):
-        api.backward(lay, dev["x"], dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"], dev["w_gs"],
-                     dev["w_gl"], dev["w_os"], dev["w_ol"], dev["rms_w"], dy, grads=grads, workspace=ws,
-                     stream=stream, debug={"stage_events": timer.address} if timer else None)
+    def step(timer=None, ftimer=None):
+        if args.train:
+            api.forward_train(*lay_args, y=y, saved=saved, workspace=fws, stream=stream,
+                              debug={"stage_events": ftimer.address} if ftimer else None)
+        api.backward(*lay_args, dy, grads=grads, workspace=ws, stream=stream, saved=saved,
+                     debug={"stage_events": timer.address} if timer else None)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     timers = [api.StageTimer(api.BWD_STAGES, "forward", "linear") for _ in range(args.steps)]
-    print("bench: timing %d backward steps" % args.steps, file=sys.stderr, flush=True)
+    if args.train:
+        fwd_timers = [api.StageTimer() for _ in range(args.steps)]
+    print("bench: timing %d %s steps" % (args.steps, "training" if args.train else "backward"), file=sys.stderr,
+          flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(timers[i])
+        step(timers[i], fwd_timers[i] if args.train else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     stage = {k: [] for k in api.BWD_STAGES}
@@ -284,17 +297,26 @@ def bench_backward(args, w, lay, dev, torch):
             stage[k].append(v)
         t.close()
     stage_ms = {k: float(np.mean(v)) for k, v in stage.items()}
+    if args.train:
+        fstage = {k: [] for k in api.STAGES}
+        for t in fwd_timers:
+            for k, v in t.elapsed_ms().items():
+                fstage[k].append(v)
+            t.close()
+        stage_ms = dict({"fwd_" + k: float(np.mean(v)) for k, v in fstage.items() if k not in ("qkv", "ffn")},
+                        **{"bwd_" + k: v for k, v in stage_ms.items()})
     ms = wall * 1e3 / args.steps
     work = backward_work(w)
     roof = {}
     for k, (bound, flop) in work.items():
-        t = stage_ms.get(k, 0.0)
-        if t > 0:
+        t = stage_ms.get(("bwd_" if args.train else "") + k, 0.0)
+        if t > 0.05:
             ach = flop / (t * 1e-3) / 1e12
             roof[k] = {"bound": bound, "algorithmic": flop, "unit": "TFLOP/s", "achieved": round(ach, 2),
                        "peak": PEAK["bf16"], "frac": round(ach / PEAK["bf16"], 4)}
     out = {
-        "metric": METRIC_BWD, "value": round(w.batch * w.n_video / (ms * 1e-3) / 1e6, 4), "unit": "Mtokens/s",
+        "metric": METRIC_TRAIN if args.train else METRIC_BWD,
+        "value": round(w.batch * w.n_video / (ms * 1e-3) / 1e6, 4), "unit": "Mtokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.act, "data": "synthetic",
         "config": {"workload": describe(w), "batch": w.batch, "video_tokens": w.n_video,
@@ -323,6 +345,8 @@ def main():
                     help="time one DiT block: projection, layer and the feed-forward (4 x hid)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (forward recompute + every gradient) instead of the forward")
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step: forward keeping its values, then the backward reading them")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--write-traffic", metavar="PMC_DIR",
@@ -357,7 +381,7 @@ def main():
     dev = {k: torch.from_numpy(v).to("cuda").to(dt) for k, v in inp.items()}
     lay = layout_of(w)
     soft = "fp8" if w.soft == "fp8" else None
-    if args.backward:
+    if args.backward or args.train:
         bench_backward(args, w, lay, dev, torch)
         return
     ffn_hidden = 4 * w.hidden if args.dit else 0

@@ -123,7 +123,15 @@ def load(path=None):
     lib.hyb_attn_backward.argtypes = (
         [ctypes.POINTER(_Layout), ctypes.c_void_p] + [_Tensor] * 5 + [ctypes.c_void_p] * 5
         + [ctypes.c_float, ctypes.c_float] + [ctypes.c_void_p] * 7 + [ctypes.c_void_p] * 5
+        + [ctypes.c_void_p, ctypes.c_size_t]
         + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(_BwdDebug)])
+    lib.hyb_saved_size.restype = ctypes.c_int
+    lib.hyb_saved_size.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(ctypes.c_size_t)]
+    lib.hyb_attn_forward_train.restype = ctypes.c_int
+    lib.hyb_attn_forward_train.argtypes = (
+        [ctypes.POINTER(_Layout), ctypes.c_void_p] + [_Tensor] * 5 + [ctypes.c_void_p] * 5
+        + [ctypes.c_float, ctypes.c_float] + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
+        + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(_Debug)])
     lib.hyb_status_string.restype = ctypes.c_char_p
     lib.hyb_status_string.argtypes = [ctypes.c_int]
     lib.hyb_last_error.restype = ctypes.c_char_p
@@ -364,9 +372,49 @@ def backward_workspace_size(lay: Layout):
 WEIGHT_GRADS = ("w_gate_soft", "w_gate_lin", "w_out_soft", "w_out_lin", "rms_weight")
 
 
+def saved_size(lay: Layout):
+    lib = load()
+    n = ctypes.c_size_t(0)
+    c = lay.c()
+    _check(lib.hyb_saved_size(ctypes.byref(c), ctypes.byref(n)))
+    return n.value
+
+
+def forward_train(lay: Layout, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin,
+                  rms_weight, softmax_scale=0.0, eps=1e-6, y=None, saved=None, workspace=None, debug=None,
+                  stream=None):
+    """Training forward (bf16): returns (y, saved) where ``saved`` is the
+    uint8 device buffer of forward values that ``backward(..., saved=saved)``
+    reads instead of recomputing the forward."""
+    import torch
+    lib = load()
+    for t in (x, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin, rms_weight):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("x, weights and rms_weight must be contiguous bfloat16 device tensors")
+    if y is None:
+        y = torch.empty_like(x)
+    if saved is None:
+        saved = torch.empty(saved_size(lay), dtype=torch.uint8, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(workspace_size(lay, "bf16"), dtype=torch.uint8, device=x.device)
+    dbg = None
+    if debug:
+        dbg = _Debug(*([_ptr(debug.get(n)) for n in ("o_soft", "o_lin", "delta_f32", "gates", "scales")]
+                       + [debug.get("stage_events")]))
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    c = lay.c()
+    _check(lib.hyb_attn_forward_train(
+        ctypes.byref(c), x.data_ptr(), _tensor4(q), _tensor4(k), _tensor4(v), _tensor4(text_k), _tensor4(text_v),
+        w_gate_soft.data_ptr(), w_gate_lin.data_ptr(), w_out_soft.data_ptr(), w_out_lin.data_ptr(),
+        rms_weight.data_ptr(), float(softmax_scale), float(eps), y.data_ptr(), saved.data_ptr(), saved.numel(),
+        workspace.data_ptr(), workspace.numel(), stream, ctypes.byref(dbg) if dbg is not None else None))
+    return y, saved
+
+
 def backward(lay: Layout, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin,
              rms_weight, dy, softmax_scale=0.0, eps=1e-6, weight_grads=WEIGHT_GRADS, grads=None,
-             workspace=None, debug=None, stream=None):
+             workspace=None, debug=None, stream=None, saved=None):
     """Gradients of sum(dy * y) for the layer (bf16 activations), by libhybattn.
 
     Returns a dict: dx, dq, dk, dv, dtext_k, dtext_v (bf16, contiguous
@@ -375,7 +423,8 @@ def backward(lay: Layout, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin, w
     ``grads`` may pre-supply any of those output tensors.  ``debug`` may map
     "d_os", "d_ol" (float32 [B, N, H, D]), "lse2" (float32 [B, H, N]) and
     "stage_events" (address of 2 * len(BWD_STAGES) hipEvent_t, see
-    ``StageTimer``)."""
+    ``StageTimer``).  ``saved``: the buffer of ``forward_train`` on the same
+    inputs (then no forward recompute runs)."""
     import torch
     lib = load()
     for t in (x, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin, rms_weight, dy):
@@ -413,6 +462,7 @@ def backward(lay: Layout, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin, w
         w_gate_soft.data_ptr(), w_gate_lin.data_ptr(), w_out_soft.data_ptr(), w_out_lin.data_ptr(),
         rms_weight.data_ptr(), float(softmax_scale), float(eps), dy.data_ptr(), out["dx"].data_ptr(),
         out["dq"].data_ptr(), out["dk"].data_ptr(), out["dv"].data_ptr(), tptr[0], tptr[1], *wptr,
+        saved.data_ptr() if saved is not None else None, saved.numel() if saved is not None else 0,
         workspace.data_ptr(), workspace.numel(), stream, ctypes.byref(dbg) if dbg is not None else None))
     return out
 

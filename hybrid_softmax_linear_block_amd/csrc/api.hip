@@ -224,12 +224,20 @@ namespace {
 // The layer.  after_projection: called by hyb_block_forward, whose projection
 // already ran (its stage events are recorded) and, with fp8, already wrote the
 // absmax of q, k, v into the workspace.
+// Forward values a training forward keeps for its backward (pointers into
+// the caller's saved buffer); see hyb_attn_forward_train.
+struct SavedPtrs {
+  uint16_t *os, *ol, *ap, *gates16;
+  float *rinv, *lse, *comb_z;
+  hyb::bf16_t *comb_hi, *comb_lo;
+};
+
 hyb_status attn_forward_impl(const hyb_layout* layout, hyb_dtype act, hyb_dtype soft, const void* x, hyb_tensor q,
                              hyb_tensor k, hyb_tensor v, hyb_tensor text_k, hyb_tensor text_v,
                              const void* w_gate_soft, const void* w_gate_lin, const void* w_out_soft,
                              const void* w_out_lin, const void* rms_weight, float softmax_scale, float eps, void* y,
                              void* workspace, size_t workspace_bytes, void* stream, const hyb_debug* dbg,
-                             bool after_projection) {
+                             bool after_projection, const SavedPtrs* keep = nullptr) {
   hyb_status st = check_layout(layout, false);
   if (st != HYB_OK) return st;
   st = check_dtypes(layout, act, soft);
@@ -337,6 +345,11 @@ hyb_status attn_forward_impl(const hyb_layout* layout, hyb_dtype act, hyb_dtype 
     a.gates_dbg = dbg ? (float*)dbg->gates : nullptr;
     a.delta_dbg = dbg ? (float*)dbg->delta_f32 : nullptr;
     a.ev = dbg ? (hipEvent_t*)dbg->stage_events : nullptr;
+    if (keep) {  // training forward: the backward's inputs go to the saved buffer
+      a.os = keep->os; a.ol = keep->ol; a.ap = keep->ap; a.gates16 = keep->gates16;
+      a.rinv = keep->rinv; a.lse = keep->lse;
+      a.comb_hi = keep->comb_hi; a.comb_lo = keep->comb_lo; a.comb_z = keep->comb_z;
+    }
     int split, ts, tsplit;
     state_split(d, &split, &ts, &tsplit);
     a.state_split = split;
@@ -550,6 +563,43 @@ enum {
 
 constexpr int kWgradSplit = 4;
 
+// Layout of the saved buffer of a training forward.
+struct SavedPlan {
+  size_t os, ol, ap, g16, rinv, lse, chi, clo, cz, total;
+};
+
+SavedPlan make_saved_plan(const hyb::Dims& d) {
+  SavedPlan p;
+  const size_t M = (size_t)d.B * d.N, hid = d.hid, D = d.D, BH = (size_t)d.B * d.H;
+  size_t o = 0;
+  p.os = o; o = align_up(o + M * hid * 2, 256);
+  p.ol = o; o = align_up(o + M * hid * 2, 256);
+  p.ap = o; o = align_up(o + M * 2 * hid * 2, 256);
+  p.g16 = o; o = align_up(o + M * 2 * hid * 2, 256);
+  p.rinv = o; o = align_up(o + M * 4, 256);
+  p.lse = o; o = align_up(o + BH * d.N * 4 + 256, 256);  // padded like the backward's own copy
+  p.chi = o; o = align_up(o + BH * d.T * D * D * 2, 256);
+  p.clo = o; o = align_up(o + BH * d.T * D * D * 2, 256);
+  p.cz = o; o = align_up(o + BH * d.T * D * 4, 256);
+  p.total = o;
+  return p;
+}
+
+SavedPtrs saved_ptrs(const SavedPlan& p, const void* saved) {
+  char* b = (char*)saved;
+  SavedPtrs k;
+  k.os = (uint16_t*)(b + p.os);
+  k.ol = (uint16_t*)(b + p.ol);
+  k.ap = (uint16_t*)(b + p.ap);
+  k.gates16 = (uint16_t*)(b + p.g16);
+  k.rinv = (float*)(b + p.rinv);
+  k.lse = (float*)(b + p.lse);
+  k.comb_hi = (hyb::bf16_t*)(b + p.chi);
+  k.comb_lo = (hyb::bf16_t*)(b + p.clo);
+  k.comb_z = (float*)(b + p.cz);
+  return k;
+}
+
 struct BwdPlan {
   Plan fwd;
   size_t off[B_COUNT];
@@ -640,8 +690,9 @@ hyb_status hyb_attn_backward(const hyb_layout* layout, const void* x, hyb_tensor
                              const void* w_out_soft, const void* w_out_lin, const void* rms_weight,
                              float softmax_scale, float eps, const void* dy, void* dx, void* dq, void* dk, void* dv,
                              void* dtext_k, void* dtext_v, float* dw_gate_soft, float* dw_gate_lin,
-                             float* dw_out_soft, float* dw_out_lin, float* drms_weight, void* workspace,
-                             size_t workspace_bytes, void* stream, const hyb_bwd_debug* dbg) {
+                             float* dw_out_soft, float* dw_out_lin, float* drms_weight, const void* saved,
+                             size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream,
+                             const hyb_bwd_debug* dbg) {
   g_err[0] = 0;
   hyb_status st = check_backward_layout(layout);
   if (st != HYB_OK) return st;
@@ -669,6 +720,12 @@ hyb_status hyb_attn_backward(const hyb_layout* layout, const void* x, hyb_tensor
   if (!(eps > 0.f) || !isfinite(eps)) return fail(HYB_ERR_INVALID_ARGUMENT, "eps must be finite and > 0");
   if (!(softmax_scale >= 0.f) || !isfinite(softmax_scale))
     return fail(HYB_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  const SavedPlan sp = make_saved_plan(d);
+  if (saved) {
+    if (!aligned(saved, 256)) return fail(HYB_ERR_INVALID_ARGUMENT, "saved is not 256-byte aligned");
+    if (saved_bytes < sp.total)
+      return fail(HYB_ERR_WORKSPACE_TOO_SMALL, "saved has %zu bytes, needs %zu", saved_bytes, sp.total);
+  }
   if (dbg) {
     const void* dp[] = {dbg->d_os, dbg->d_ol, dbg->lse2};
     for (int i = 0; i < 3; ++i)
@@ -686,7 +743,7 @@ hyb_status hyb_attn_backward(const hyb_layout* layout, const void* x, hyb_tensor
                     {(uintptr_t)dw_out_lin, (uintptr_t)dw_out_lin + ww, "dw_out_lin"},
                     {(uintptr_t)drms_weight, (uintptr_t)drms_weight + (size_t)d.hid * 4, "drms_weight"}};
     const int nout = (int)(sizeof(outs) / sizeof(outs[0]));
-    Range ins[9];
+    Range ins[10];
     int nin = 0;
     const hyb_tensor* ts[] = {&q, &k, &v};
     for (int i = 0; i < 3; ++i) {
@@ -702,6 +759,7 @@ hyb_status hyb_attn_backward(const hyb_layout* layout, const void* x, hyb_tensor
     ins[nin++] = {(uintptr_t)x, (uintptr_t)x + act, "x"};
     ins[nin++] = {(uintptr_t)dy, (uintptr_t)dy + act, "dy"};
     ins[nin++] = {(uintptr_t)workspace, (uintptr_t)workspace + workspace_bytes, "workspace"};
+    if (saved) ins[nin++] = {(uintptr_t)saved, (uintptr_t)saved + sp.total, "saved"};
     for (int i = 0; i < nout; ++i) {
       if (!outs[i].lo || outs[i].hi == outs[i].lo) continue;
       for (int j = i + 1; j < nout; ++j)
@@ -800,6 +858,13 @@ hyb_status hyb_attn_backward(const hyb_layout* layout, const void* x, hyb_tensor
   a.dsl = (hyb::bf16_t*)(ws + plan.off[B_DSL]);
   a.dsz = (float*)(ws + plan.off[B_DSZ]);
   a.ev = dbg ? (hipEvent_t*)dbg->stage_events : nullptr;
+  a.recompute = saved == nullptr;
+  if (saved) {  // the training forward's values instead of a recompute
+    const SavedPtrs k = saved_ptrs(sp, saved);
+    a.os = k.os; a.ol = k.ol; a.ap = k.ap; a.gates16 = k.gates16;
+    a.rinv = k.rinv; a.lse = k.lse;
+    a.comb_hi = k.comb_hi; a.comb_lo = k.comb_lo; a.comb_z = k.comb_z;
+  }
 
   hipError_t he = hyb::run_bwd_bf16(d, f, a, s);
   const long long nel = (long long)d.B * d.N * d.hid;
@@ -910,6 +975,49 @@ hyb_status hyb_dit_block_forward(const hyb_layout* layout, hyb_dtype soft, const
   if (he == hipSuccess && ev) he = hipEventRecord(ev[2 * HYB_STAGE_FFN + 1], s);
   if (he != hipSuccess) return fail(HYB_ERR_HIP, "HIP error: %s", hipGetErrorString(he));
   return HYB_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Training forward: the layer plus the values its backward reads.
+extern "C" {
+
+hyb_status hyb_saved_size(const hyb_layout* layout, size_t* bytes) {
+  g_err[0] = 0;
+  hyb_status st = check_backward_layout(layout);
+  if (st != HYB_OK) return st;
+  if (!bytes) return fail(HYB_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = make_saved_plan(make_dims(layout)).total;
+  return HYB_OK;
+}
+
+hyb_status hyb_attn_forward_train(const hyb_layout* layout, const void* x, hyb_tensor q, hyb_tensor k, hyb_tensor v,
+                                  hyb_tensor text_k, hyb_tensor text_v, const void* w_gate_soft,
+                                  const void* w_gate_lin, const void* w_out_soft, const void* w_out_lin,
+                                  const void* rms_weight, float softmax_scale, float eps, void* y, void* saved,
+                                  size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream,
+                                  const hyb_debug* dbg) {
+  g_err[0] = 0;
+  hyb_status st = check_backward_layout(layout);
+  if (st != HYB_OK) return st;
+  const hyb::Dims d = make_dims(layout);
+  const SavedPlan sp = make_saved_plan(d);
+  if (!saved) return fail(HYB_ERR_INVALID_ARGUMENT, "saved is NULL");
+  if (!aligned(saved, 256)) return fail(HYB_ERR_INVALID_ARGUMENT, "saved is not 256-byte aligned");
+  if (saved_bytes < sp.total)
+    return fail(HYB_ERR_WORKSPACE_TOO_SMALL, "saved has %zu bytes, needs %zu", saved_bytes, sp.total);
+  {  // the saved buffer must not overlap y or the workspace
+    const uintptr_t lo = (uintptr_t)saved, hi = lo + sp.total;
+    const uintptr_t ylo = (uintptr_t)y, yhi = ylo + (size_t)d.B * d.N * d.hid * 2;
+    const uintptr_t wlo = (uintptr_t)workspace, whi = wlo + workspace_bytes;
+    if ((y && lo < yhi && ylo < hi) || (workspace && lo < whi && wlo < hi))
+      return fail(HYB_ERR_INVALID_ARGUMENT, "saved overlaps y or the workspace");
+  }
+  const SavedPtrs keep = saved_ptrs(sp, saved);
+  return attn_forward_impl(layout, HYB_BF16, HYB_BF16, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin,
+                           w_out_soft, w_out_lin, rms_weight, softmax_scale, eps, y, workspace, workspace_bytes,
+                           stream, dbg, false, &keep);
 }
 
 }  // extern "C"

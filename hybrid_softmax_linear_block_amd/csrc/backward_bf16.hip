@@ -198,7 +198,7 @@ hipError_t launch_bf16_to_f32(const bf16_t* src, float* dst, long long n, hipStr
 hipError_t run_bwd_bf16(const Dims& d, const Bf16Args& f, const BwdArgs& a, hipStream_t s) {
   const long long M = (long long)d.B * d.N;
   const int hid = d.hid;
-  HYB_BSTAGE(BST_FORWARD, {
+  HYB_BSTAGE(BST_FORWARD, if (a.recompute) {
     HYB_TRY(launch_weights_bf16(d, f, s));
     HYB_TRY(launch_softmax_bf16(d, f, s));
     HYB_TRY(launch_states_bf16(d, f, s));

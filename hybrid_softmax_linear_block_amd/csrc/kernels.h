@@ -96,6 +96,7 @@ struct BwdArgs {
   bf16_t *dsh, *dsl;                       // [B*H][T+1][d][e]
   float* dsz;                              // [B*H][T+1][D]
   hipEvent_t* ev;                          // NULL or 2 events per backward stage
+  bool recompute;                          // false: the saved forward values come from a training forward
 };
 hipError_t run_bwd_bf16(const Dims& d, const Bf16Args& fwd, const BwdArgs& a, hipStream_t s);
 hipError_t launch_bf16_to_f32(const bf16_t* src, float* dst, long long n, hipStream_t s);

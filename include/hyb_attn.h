@@ -233,6 +233,27 @@ typedef struct {
 /* Bytes of device workspace hyb_attn_backward() needs (bf16 activations). */
 hyb_status hyb_backward_workspace_size(const hyb_layout* layout, size_t* bytes);
 
+/* Bytes of the `saved` buffer of hyb_attn_forward_train(). */
+hyb_status hyb_saved_size(const hyb_layout* layout, size_t* bytes);
+
+/*
+ * Training forward: hyb_attn_forward() (act = soft = HYB_BF16) that also
+ * keeps, in `saved` (at least hyb_saved_size() bytes, 256-byte aligned,
+ * caller-owned, not overlapping y or the workspace), every forward value the
+ * backward reads: O_s and O_l (fp16), each softmax row's log-sum-exp, the
+ * combined linear states, the RMS factors, the gates and A'.  Passing that
+ * buffer to hyb_attn_backward() skips the backward's forward recompute.  The
+ * buffer is only meaningful for the layout, inputs and weights of the call
+ * that filled it; the backward does not check that.  Other arguments and
+ * errors as in hyb_attn_forward(); the workspace is hyb_workspace_size().
+ */
+hyb_status hyb_attn_forward_train(const hyb_layout* layout, const void* x, hyb_tensor q, hyb_tensor k, hyb_tensor v,
+                                  hyb_tensor text_k, hyb_tensor text_v, const void* w_gate_soft,
+                                  const void* w_gate_lin, const void* w_out_soft, const void* w_out_lin,
+                                  const void* rms_weight, float softmax_scale, float eps, void* y, void* saved,
+                                  size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream,
+                                  const hyb_debug* dbg);
+
 /*
  *   inputs        as hyb_attn_forward() with act = soft = HYB_BF16 (q, k, v,
  *                 text_k, text_v may be strided views); dy [B, N, hid] bf16
@@ -244,6 +265,10 @@ hyb_status hyb_backward_workspace_size(const hyb_layout* layout, size_t* bytes);
  *                 ([in][out], like the weights), each NULL when that weight
  *                 is frozen (its gradient is then not computed)
  *   drms_weight   float32 [hid] or NULL
+ *   saved         NULL (the call recomputes the forward first) or the buffer
+ *                 a hyb_attn_forward_train() call on the same inputs filled
+ *                 (saved_bytes >= hyb_saved_size()); then no recompute runs
+ *                 and HYB_BSTAGE_FORWARD records an empty interval
  *   workspace     at least hyb_backward_workspace_size() bytes, 256-byte
  *                 aligned; contents on entry ignored
  * All outputs must be 16-byte aligned and must not overlap any input or each
@@ -255,8 +280,9 @@ hyb_status hyb_attn_backward(const hyb_layout* layout, const void* x, hyb_tensor
                              const void* w_out_soft, const void* w_out_lin, const void* rms_weight,
                              float softmax_scale, float eps, const void* dy, void* dx, void* dq, void* dk, void* dv,
                              void* dtext_k, void* dtext_v, float* dw_gate_soft, float* dw_gate_lin,
-                             float* dw_out_soft, float* dw_out_lin, float* drms_weight, void* workspace,
-                             size_t workspace_bytes, void* stream, const hyb_bwd_debug* dbg);
+                             float* dw_out_soft, float* dw_out_lin, float* drms_weight, const void* saved,
+                             size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream,
+                             const hyb_bwd_debug* dbg);
 
 /*
  * One DiT block around the layer -- article section "分阶段适配预训练模型": a

@@ -31,7 +31,8 @@ def test_exports_every_declared_symbol():
                             "hyb_status_string", "hyb_workspace_size", "hyb_qkv_workspace_size",
                             "hyb_qkv_project", "hyb_block_workspace_size", "hyb_block_forward",
                             "hyb_backward_workspace_size", "hyb_attn_backward",
-                            "hyb_dit_block_workspace_size", "hyb_dit_block_forward"])
+                            "hyb_dit_block_workspace_size", "hyb_dit_block_forward", "hyb_saved_size",
+                            "hyb_attn_forward_train"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -203,7 +204,7 @@ def test_backward_validation_errors():
     a0 = dict(x=nxt(), q=T4(nxt(), *st), k=T4(nxt(), *st), v=T4(nxt(), *st), tk=T4(nxt(), *tst),
               tv=T4(nxt(), *tst), wgs=nxt(), wgl=nxt(), wos=nxt(), wol=nxt(), rms=nxt(), scale=0.0, eps=1e-6,
               dy=nxt(), dx=nxt(), dq=nxt(), dk=nxt(), dv=nxt(), dtk=nxt(), dtv=nxt(), dwgs=nxt(), dwgl=nxt(),
-              dwos=nxt(), dwol=nxt(), drms=nxt(), ws=nxt(), wsb=1 << 40)
+              dwos=nxt(), dwol=nxt(), drms=nxt(), sv=None, svb=0, ws=nxt(), wsb=1 << 40)
 
     def call(lay_c=c, **over):
         a = dict(a0)
@@ -211,7 +212,7 @@ def test_backward_validation_errors():
         r = lib.hyb_attn_backward(ctypes.byref(lay_c), a["x"], a["q"], a["k"], a["v"], a["tk"], a["tv"], a["wgs"],
                                   a["wgl"], a["wos"], a["wol"], a["rms"], a["scale"], a["eps"], a["dy"], a["dx"],
                                   a["dq"], a["dk"], a["dv"], a["dtk"], a["dtv"], a["dwgs"], a["dwgl"], a["dwos"],
-                                  a["dwol"], a["drms"], a["ws"], a["wsb"], None, None)
+                                  a["dwol"], a["drms"], a["sv"], a["svb"], a["ws"], a["wsb"], None, None)
         return r, lib.hyb_last_error().decode()
 
     assert call(dy=None)[0] == api.HYB_ERR_INVALID_ARGUMENT
@@ -231,6 +232,15 @@ def test_backward_validation_errors():
     # workspace check with the fake sizes)
     r, msg = call(dwgs=None, dwos=None, drms=None, wsb=1000)
     assert r == api.HYB_ERR_WORKSPACE_TOO_SMALL
+    sv = nxt()
+    assert call(sv=sv + 64, svb=1 << 40)[0] == api.HYB_ERR_INVALID_ARGUMENT          # saved alignment
+    r, msg = call(sv=sv, svb=1000)
+    assert r == api.HYB_ERR_WORKSPACE_TOO_SMALL and "saved" in msg
+    r, msg = call(sv=sv, svb=1 << 40, dq=sv + 4096, wsb=1 << 34)                    # output over saved
+    assert r == api.HYB_ERR_INVALID_ARGUMENT and "saved" in msg
+    n = api.saved_size(lay)
+    M, hid = 15 * 1024, 512
+    assert n >= M * hid * 2 * 6 + 8 * 15 * 1024 * 4
     bad = api.Layout(1, 15, 64, 16, 2, 32).c()
     assert call(lay_c=bad)[0] == api.HYB_ERR_UNSUPPORTED                      # head_dim 32
     big = api.Layout(1, 2, 64, 0, 160, 128).c()

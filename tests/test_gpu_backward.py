@@ -149,3 +149,25 @@ def test_backward_768p_sampled():
         e = gu.errors(got, ref)
         print("768p", name, "max %.2e mean %.2e" % e, flush=True)
         assert e[0] <= TOL_GRAD[0] and e[1] <= TOL_GRAD[1], (name, e)
+
+
+def test_backward_from_training_forward_bit_identical():
+    """forward_train's y equals forward's y, and the backward that reads its
+    saved values (no recompute) gives the recomputing backward's gradients,
+    bit for bit."""
+    import torch
+    w = CASES[3]
+    inp = make_inputs(w)
+    dy = make_grad_output(w)
+    base = run_backward(w, inp, dy)
+    d = {k: _dev(v) for k, v in inp.items()}
+    lay = gu.api_layout(w)
+    args = (lay, d["x"], d["q"], d["k"], d["v"], d["text_k"], d["text_v"], d["w_gs"], d["w_gl"], d["w_os"],
+            d["w_ol"], d["rms_w"])
+    y_plain = api.forward(*args)
+    y_train, saved = api.forward_train(*args)
+    g = api.backward(*args, _dev(dy), saved=saved)
+    torch.cuda.synchronize()
+    assert torch.equal(y_plain, y_train)
+    for k_, v_ in g.items():
+        assert np.array_equal(v_.float().cpu().numpy().astype(np.float64), base[k_]), k_
