@@ -217,7 +217,7 @@ def cpu_baseline(w, inp, budget_s=20.0):
         t0 = time.perf_counter()
         st = oracle.linear_states(inp["k"], inp["v"], inp["text_k"], inp["text_v"], lay)
         t_states = time.perf_counter() - t0
-        per = 64
+        per = 256
         tok = sample_tokens(w, per_frame=per)
         t0 = time.perf_counter()
         o_s = oracle.softmax_branch(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], lay, tokens=tok)
