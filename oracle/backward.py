@@ -290,3 +290,25 @@ def dq_dx_at(inp, lay, dy, tokens, states=None, scale=None, eps=1e-6):
                     dpq = C @ (g / den) - c * (np.dot(g, O) / den)
                     dq[b, i, h] = tau * (ds @ K) + dpq * dphi(qi)
     return dq, ep["dx"]
+
+
+def block_backward(inp, lay, proj, dy, scale=None, eps=1e-6):
+    """Gradients of L = sum(dy * y) for the layer with its Q/K/V projection,
+    y = layer(x; q, k, v = x W_q, x W_k, x W_v) (oracle/projection.py; no
+    rounding between the steps here).  The layer's gradients, then through
+    the projection: dx += dq W_q^T + dk W_k^T + dv W_v^T and
+    dW_q = x^T dq (likewise k, v), heads flattened into the hidden axis.
+    Returns the layer's dict with dx replaced and dw_q, dw_k, dw_v added."""
+    from .projection import qkv_projection
+    x = np.asarray(inp["x"], np.float64)
+    B, N, hid = x.shape
+    q, k, v = qkv_projection(x, proj["w_q"], proj["w_k"], proj["w_v"], lay.heads)
+    g = hybrid_backward(dict(inp, q=q, k=k, v=v), lay, dy, scale=scale, eps=eps)
+    xf = x.reshape(B * N, hid)
+    dx = g["dx"].reshape(B * N, hid)
+    for name, dname in (("w_q", "dq"), ("w_k", "dk"), ("w_v", "dv")):
+        d = g[dname].reshape(B * N, hid)
+        dx = dx + d @ np.asarray(proj[name], np.float64).T
+        g["d" + name] = xf.T @ d
+    g["dx"] = dx.reshape(B, N, hid)
+    return g

@@ -209,3 +209,24 @@ def test_dq_dx_at_sampled_tokens_equal_full_backward():
     dq, dx = BW.dq_dx_at(inp, lay, dy, tok)
     assert np.allclose(dq, full["dq"][:, tok], rtol=1e-10, atol=1e-12)
     assert np.allclose(dx, full["dx"][:, tok], rtol=1e-10, atol=1e-12)
+
+
+def test_block_gradients_match_finite_differences():
+    """Through the Q/K/V projection: dx and the projection weights' gradients
+    against central differences of the block forward."""
+    from oracle.projection import qkv_projection
+    lay = LAYOUTS[0]
+    inp, dy = make(lay, 600)
+    g = np.random.Generator(np.random.PCG64(601))
+    hid = lay.hidden
+    proj = {n: g.standard_normal((hid, hid)) / math.sqrt(hid) for n in ("w_q", "w_k", "w_v")}
+
+    def block_loss(a):
+        q, k, v = qkv_projection(a["x"], a["w_q"], a["w_k"], a["w_v"], lay.heads)
+        return float(np.sum(dy * oracle.hybrid_forward(dict(a, q=q, k=k, v=v), lay)["y"]))
+    gr = BW.block_backward(inp, lay, proj, dy)
+    full = dict(inp, **proj)
+    for j, (name, gname) in enumerate((("x", "dx"), ("w_q", "dw_q"), ("w_k", "dw_k"), ("w_v", "dw_v"),
+                                       ("text_k", "dtext_k"), ("w_gl", "dw_gl"))):
+        err, num, an = check_direction(block_loss, full, name, gr[gname], 700 + j)
+        assert err < 1e-7, (name, num, an)
