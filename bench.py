@@ -32,6 +32,8 @@ METRIC = "hybrid-attn layer Mtokens/s + softmax-branch TFLOP/s (768p-shaped, bf1
 METRIC_BLOCK = "hybrid-attn layer with its Q/K/V projection Mtokens/s (768p-shaped, bf16)"
 METRIC_DIT = "DiT block (Q/K/V projection + hybrid layer + feed-forward) Mtokens/s (768p-shaped, bf16)"
 METRIC_TRAIN = "hybrid-attn layer training step (forward keeping its values + backward) Mtokens/s (768p-shaped, bf16)"
+METRIC_BLOCK_BWD = ("hybrid-attn layer with its Q/K/V projection, backward (recompute + all gradients) Mtokens/s "
+                    "(768p-shaped, bf16)")
 METRIC_BWD = "hybrid-attn layer backward (forward recompute + all gradients) Mtokens/s (768p-shaped, bf16)"
 PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense MFMA TFLOP/s, MI355X published
 PEAK_HBM_GBS = 8000.0  # HBM3E, MI355X published
@@ -268,9 +270,19 @@ def bench_backward(args, w, lay, dev, torch):
         saved = torch.empty(api.saved_size(lay), dtype=torch.uint8, device="cuda")
         fws = torch.empty(api.workspace_size(lay, "bf16"), dtype=torch.uint8, device="cuda")
         y = torch.empty_like(dev["x"])
-    grads = api.backward(*lay_args, dy, workspace=ws, stream=stream)
+    if args.block:
+        pw = {k: torch.from_numpy(v).to("cuda").to(torch.bfloat16) for k, v in make_projection_weights(w).items()}
+        ws = torch.empty(api.block_backward_workspace_size(lay), dtype=torch.uint8, device="cuda")
+        blk_args = (lay, dev["x"], pw["w_q"], pw["w_k"], pw["w_v"], dev["text_k"], dev["text_v"], dev["w_gs"],
+                    dev["w_gl"], dev["w_os"], dev["w_ol"], dev["rms_w"], dy)
+    else:
+        grads = api.backward(*lay_args, dy, workspace=ws, stream=stream)
 
     def step(timer=None, ftimer=None):
+        if args.block:
+            api.block_backward(*blk_args, workspace=ws, stream=stream,
+                               debug={"stage_events": timer.address} if timer else None)
+            return
         if args.train:
             api.forward_train(*lay_args, y=y, saved=saved, workspace=fws, stream=stream,
                               debug={"stage_events": ftimer.address} if ftimer else None)
@@ -315,7 +327,7 @@ def bench_backward(args, w, lay, dev, torch):
             roof[k] = {"bound": bound, "algorithmic": flop, "unit": "TFLOP/s", "achieved": round(ach, 2),
                        "peak": PEAK["bf16"], "frac": round(ach / PEAK["bf16"], 4)}
     out = {
-        "metric": METRIC_TRAIN if args.train else METRIC_BWD,
+        "metric": METRIC_TRAIN if args.train else (METRIC_BLOCK_BWD if args.block else METRIC_BWD),
         "value": round(w.batch * w.n_video / (ms * 1e-3) / 1e6, 4), "unit": "Mtokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.act, "data": "synthetic",

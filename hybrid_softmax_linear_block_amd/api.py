@@ -125,6 +125,13 @@ def load(path=None):
         + [ctypes.c_float, ctypes.c_float] + [ctypes.c_void_p] * 7 + [ctypes.c_void_p] * 5
         + [ctypes.c_void_p, ctypes.c_size_t]
         + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(_BwdDebug)])
+    lib.hyb_block_backward_workspace_size.restype = ctypes.c_int
+    lib.hyb_block_backward_workspace_size.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(ctypes.c_size_t)]
+    lib.hyb_block_backward.restype = ctypes.c_int
+    lib.hyb_block_backward.argtypes = (
+        [ctypes.POINTER(_Layout)] + [ctypes.c_void_p] * 4 + [_Tensor] * 2 + [ctypes.c_void_p] * 5
+        + [ctypes.c_float, ctypes.c_float] + [ctypes.c_void_p] * 4 + [ctypes.c_void_p] * 8
+        + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(_BwdDebug)])
     lib.hyb_saved_size.restype = ctypes.c_int
     lib.hyb_saved_size.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(ctypes.c_size_t)]
     lib.hyb_attn_forward_train.restype = ctypes.c_int
@@ -509,3 +516,55 @@ def dit_block_forward(lay: Layout, x, w_q, w_k, w_v, text_k, text_v, w_gate_soft
         w_ff2.data_ptr(), int(F), float(softmax_scale), float(eps), z.data_ptr(), workspace.data_ptr(),
         workspace.numel(), stream, ctypes.byref(dbg) if dbg is not None else None))
     return z
+
+
+def block_backward_workspace_size(lay: Layout):
+    lib = load()
+    n = ctypes.c_size_t(0)
+    c = lay.c()
+    _check(lib.hyb_block_backward_workspace_size(ctypes.byref(c), ctypes.byref(n)))
+    return n.value
+
+
+BLOCK_WEIGHT_GRADS = ("w_q", "w_k", "w_v") + WEIGHT_GRADS
+
+
+def block_backward(lay: Layout, x, w_q, w_k, w_v, text_k, text_v, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin,
+                   rms_weight, dy, softmax_scale=0.0, eps=1e-6, weight_grads=BLOCK_WEIGHT_GRADS, workspace=None,
+                   debug=None, stream=None):
+    """Gradients of sum(dy * y) for the layer with its Q/K/V projection
+    (bf16).  Returns dx, dtext_k, dtext_v and "d" + name (float32) for the
+    weights named in ``weight_grads``."""
+    import torch
+    lib = load()
+    for t in (x, w_q, w_k, w_v, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin, rms_weight, dy):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("x, weights, rms_weight and dy must be contiguous bfloat16 device tensors")
+    B, N, H, D, L, hid = lay.batch, lay.n_video, lay.heads, lay.head_dim, lay.text_tokens, lay.hidden
+    bf = dict(dtype=torch.bfloat16, device=x.device)
+    out = {"dx": torch.empty((B, N, hid), **bf), "dtext_k": torch.empty((B, L, H, D), **bf),
+           "dtext_v": torch.empty((B, L, H, D), **bf)}
+    wptr = []
+    for name in BLOCK_WEIGHT_GRADS:
+        if name in weight_grads:
+            out["d" + name] = torch.empty((hid,) if name == "rms_weight" else (hid, hid), dtype=torch.float32,
+                                          device=x.device)
+            wptr.append(out["d" + name].data_ptr())
+        else:
+            wptr.append(None)
+    if workspace is None:
+        workspace = torch.empty(block_backward_workspace_size(lay), dtype=torch.uint8, device=x.device)
+    dbg = None
+    if debug:
+        dbg = _BwdDebug(*([_ptr(debug.get(n)) for n in ("d_os", "d_ol", "lse2")] + [debug.get("stage_events")]))
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    c = lay.c()
+    tptr = [out[n].data_ptr() if out[n].numel() else None for n in ("dtext_k", "dtext_v")]
+    _check(lib.hyb_block_backward(
+        ctypes.byref(c), x.data_ptr(), w_q.data_ptr(), w_k.data_ptr(), w_v.data_ptr(), _tensor4(text_k),
+        _tensor4(text_v), w_gate_soft.data_ptr(), w_gate_lin.data_ptr(), w_out_soft.data_ptr(),
+        w_out_lin.data_ptr(), rms_weight.data_ptr(), float(softmax_scale), float(eps), dy.data_ptr(),
+        out["dx"].data_ptr(), tptr[0], tptr[1], *wptr, workspace.data_ptr(), workspace.numel(), stream,
+        ctypes.byref(dbg) if dbg is not None else None))
+    return out

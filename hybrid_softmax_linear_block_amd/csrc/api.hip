@@ -685,15 +685,21 @@ hyb_status hyb_backward_workspace_size(const hyb_layout* layout, size_t* bytes) 
   return HYB_OK;
 }
 
-hyb_status hyb_attn_backward(const hyb_layout* layout, const void* x, hyb_tensor q, hyb_tensor k, hyb_tensor v,
-                             hyb_tensor text_k, hyb_tensor text_v, const void* w_gate_soft, const void* w_gate_lin,
-                             const void* w_out_soft, const void* w_out_lin, const void* rms_weight,
-                             float softmax_scale, float eps, const void* dy, void* dx, void* dq, void* dk, void* dv,
-                             void* dtext_k, void* dtext_v, float* dw_gate_soft, float* dw_gate_lin,
-                             float* dw_out_soft, float* dw_out_lin, float* drms_weight, const void* saved,
-                             size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream,
-                             const hyb_bwd_debug* dbg) {
-  g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+
+// The backward pass.  ld_qkv: row stride of dq, dk, dv (hid for the public
+// call; 3 hid when the block backward interleaves them into one [M][3 hid]
+// operand, whose overlap the output check then skips).
+hyb_status attn_backward_impl(const hyb_layout* layout, const void* x, hyb_tensor q, hyb_tensor k, hyb_tensor v,
+                              hyb_tensor text_k, hyb_tensor text_v, const void* w_gate_soft, const void* w_gate_lin,
+                              const void* w_out_soft, const void* w_out_lin, const void* rms_weight,
+                              float softmax_scale, float eps, const void* dy, void* dx, void* dq, void* dk, void* dv,
+                              int ld_qkv, void* dtext_k, void* dtext_v, float* dw_gate_soft, float* dw_gate_lin,
+                              float* dw_out_soft, float* dw_out_lin, float* drms_weight, const void* saved,
+                              size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream,
+                              const hyb_bwd_debug* dbg) {
   hyb_status st = check_backward_layout(layout);
   if (st != HYB_OK) return st;
   const hyb::Dims d = make_dims(layout);
@@ -731,7 +737,7 @@ hyb_status hyb_attn_backward(const hyb_layout* layout, const void* x, hyb_tensor
     for (int i = 0; i < 3; ++i)
       if (dp[i] && !aligned(dp[i], 16)) return fail(HYB_ERR_INVALID_ARGUMENT, "debug buffer %d not 16-byte aligned", i);
   }
-  {  // outputs: no overlap with each other or with any input
+  if (ld_qkv == (int)d.hid) {  // outputs: no overlap with each other or with any input
     const size_t act = (size_t)d.B * d.N * d.hid * 2, tact = (size_t)d.B * d.L * d.hid * 2, ww = (size_t)d.hid * d.hid * 4;
     Range outs[] = {{(uintptr_t)dx, (uintptr_t)dx + act, "dx"}, {(uintptr_t)dq, (uintptr_t)dq + act, "dq"},
                     {(uintptr_t)dk, (uintptr_t)dk + act, "dk"}, {(uintptr_t)dv, (uintptr_t)dv + act, "dv"},
@@ -826,6 +832,7 @@ hyb_status hyb_attn_backward(const hyb_layout* layout, const void* x, hyb_tensor
   a.comb_hi = f.comb_hi; a.comb_lo = f.comb_lo; a.comb_z = f.comb_z;
   a.dx = (hyb::bf16_t*)dx; a.dq = (hyb::bf16_t*)dq; a.dk = (hyb::bf16_t*)dk; a.dv = (hyb::bf16_t*)dv;
   a.dtk = (hyb::bf16_t*)dtext_k; a.dtv = (hyb::bf16_t*)dtext_v;
+  a.ld_qkv = ld_qkv;
   a.dwgs = dw_gate_soft; a.dwgl = dw_gate_lin; a.dwos = dw_out_soft; a.dwol = dw_out_lin; a.drmsw = drms_weight;
   a.wo_cat = (hyb::bf16_t*)(ws + plan.off[B_WO]);
   a.wg_cat = (hyb::bf16_t*)(ws + plan.off[B_WG]);
@@ -875,6 +882,27 @@ hyb_status hyb_attn_backward(const hyb_layout* layout, const void* x, hyb_tensor
     he = hipMemcpyAsync(dbg->lse2, a.lse, (size_t)d.B * d.H * d.N * 4, hipMemcpyDeviceToDevice, s);
   if (he != hipSuccess) return fail(HYB_ERR_HIP, "HIP error: %s", hipGetErrorString(he));
   return HYB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hyb_status hyb_attn_backward(const hyb_layout* layout, const void* x, hyb_tensor q, hyb_tensor k, hyb_tensor v,
+                             hyb_tensor text_k, hyb_tensor text_v, const void* w_gate_soft, const void* w_gate_lin,
+                             const void* w_out_soft, const void* w_out_lin, const void* rms_weight,
+                             float softmax_scale, float eps, const void* dy, void* dx, void* dq, void* dk, void* dv,
+                             void* dtext_k, void* dtext_v, float* dw_gate_soft, float* dw_gate_lin,
+                             float* dw_out_soft, float* dw_out_lin, float* drms_weight, const void* saved,
+                             size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream,
+                             const hyb_bwd_debug* dbg) {
+  g_err[0] = 0;
+  hyb_status st = check_backward_layout(layout);
+  if (st != HYB_OK) return st;
+  return attn_backward_impl(layout, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin,
+                            rms_weight, softmax_scale, eps, dy, dx, dq, dk, dv, layout->heads * layout->head_dim,
+                            dtext_k, dtext_v, dw_gate_soft, dw_gate_lin, dw_out_soft, dw_out_lin, drms_weight,
+                            saved, saved_bytes, workspace, workspace_bytes, stream, dbg);
 }
 
 }  // extern "C"
@@ -1018,6 +1046,133 @@ hyb_status hyb_attn_forward_train(const hyb_layout* layout, const void* x, hyb_t
   return attn_forward_impl(layout, HYB_BF16, HYB_BF16, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin,
                            w_out_soft, w_out_lin, rms_weight, softmax_scale, eps, y, workspace, workspace_bytes,
                            stream, dbg, false, &keep);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward of the layer with its Q/K/V projection.
+namespace {
+
+struct BlockBwdPlan {
+  size_t wt, q, k, v, layer, dxl, dqkv, wcat, xT, dqkvT, wpart, total;
+  size_t layer_bytes;
+  long long mpad;
+};
+
+BlockBwdPlan make_block_bwd_plan(const hyb::Dims& d) {
+  BlockBwdPlan p;
+  const BwdPlan lb = make_bwd_plan(d);
+  const size_t M = (size_t)d.B * d.N, hid = d.hid;
+  p.mpad = lb.mpad;
+  size_t o = 0;
+  p.wt = o; o = align_up(o + qkv_weight_bytes(d), 256);
+  p.q = o; o = align_up(o + M * hid * 2, 256);
+  p.k = o; o = align_up(o + M * hid * 2, 256);
+  p.v = o; o = align_up(o + M * hid * 2, 256);
+  p.layer = o; o = align_up(o + lb.total, 256);
+  p.layer_bytes = lb.total;
+  p.dxl = o; o = align_up(o + M * hid * 2, 256);
+  p.dqkv = o; o = align_up(o + M * 3 * hid * 2, 256);
+  p.wcat = o; o = align_up(o + 3 * hid * hid * 2, 256);
+  p.xT = o; o = align_up(o + hid * (size_t)p.mpad * 2, 256);
+  p.dqkvT = o; o = align_up(o + 3 * hid * (size_t)p.mpad * 2, 256);
+  p.wpart = o; o = align_up(o + (size_t)kWgradSplit * 3 * hid * hid * 4, 256);
+  p.total = o;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+hyb_status hyb_block_backward_workspace_size(const hyb_layout* layout, size_t* bytes) {
+  g_err[0] = 0;
+  hyb_status st = check_backward_layout(layout);
+  if (st != HYB_OK) return st;
+  if (!bytes) return fail(HYB_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = make_block_bwd_plan(make_dims(layout)).total;
+  return HYB_OK;
+}
+
+hyb_status hyb_block_backward(const hyb_layout* layout, const void* x, const void* w_q, const void* w_k,
+                              const void* w_v, hyb_tensor text_k, hyb_tensor text_v, const void* w_gate_soft,
+                              const void* w_gate_lin, const void* w_out_soft, const void* w_out_lin,
+                              const void* rms_weight, float softmax_scale, float eps, const void* dy, void* dx,
+                              void* dtext_k, void* dtext_v, float* dw_q, float* dw_k, float* dw_v,
+                              float* dw_gate_soft, float* dw_gate_lin, float* dw_out_soft, float* dw_out_lin,
+                              float* drms_weight, void* workspace, size_t workspace_bytes, void* stream,
+                              const hyb_bwd_debug* dbg) {
+  g_err[0] = 0;
+  hyb_status st = check_backward_layout(layout);
+  if (st != HYB_OK) return st;
+  const hyb::Dims d = make_dims(layout);
+  const bool has_text = d.L > 0;
+  {
+    const void* req[] = {x, w_q, w_k, w_v, dy, dx, workspace};
+    const char* names[] = {"x", "w_q", "w_k", "w_v", "dy", "dx", "workspace"};
+    for (int i = 0; i < 7; ++i) {
+      if (!req[i]) return fail(HYB_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+      if (!aligned(req[i], i == 6 ? 256 : 16))
+        return fail(HYB_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", names[i], i == 6 ? 256 : 16);
+    }
+    const void* opt[] = {dw_q, dw_k, dw_v};
+    for (int i = 0; i < 3; ++i)
+      if (opt[i] && !aligned(opt[i], 16)) return fail(HYB_ERR_INVALID_ARGUMENT, "dw_q/k/v %d not 16-byte aligned", i);
+    // dx and the projection-weight gradients must not overlap each other or x, dy
+    const size_t act = (size_t)d.B * d.N * d.hid * 2, ww = (size_t)d.hid * d.hid * 4;
+    Range r[] = {{(uintptr_t)dx, (uintptr_t)dx + act, "dx"}, {(uintptr_t)dw_q, (uintptr_t)dw_q + ww, "dw_q"},
+                 {(uintptr_t)dw_k, (uintptr_t)dw_k + ww, "dw_k"}, {(uintptr_t)dw_v, (uintptr_t)dw_v + ww, "dw_v"},
+                 {(uintptr_t)x, (uintptr_t)x + act, "x"}, {(uintptr_t)dy, (uintptr_t)dy + act, "dy"},
+                 {(uintptr_t)workspace, (uintptr_t)workspace + workspace_bytes, "workspace"}};
+    for (int i = 0; i < 4; ++i) {
+      if (!r[i].lo) continue;
+      for (int j = i + 1; j < 7; ++j)
+        if (r[j].lo && r[i].lo < r[j].hi && r[j].lo < r[i].hi)
+          return fail(HYB_ERR_INVALID_ARGUMENT, "%s overlaps %s", r[i].name, r[j].name);
+    }
+  }
+  if ((st = check_tensor("text_k", text_k, 2, has_text)) != HYB_OK) return st;
+  if ((st = check_tensor("text_v", text_v, 2, has_text)) != HYB_OK) return st;
+  const BlockBwdPlan p = make_block_bwd_plan(d);
+  if (workspace_bytes < p.total)
+    return fail(HYB_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, p.total);
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  // q, k, v views of the workspace buffers: contiguous [B, N, H, D]
+  hyb_tensor tq, tk, tv;
+  const int64_t sb = (int64_t)d.N * d.hid, stok = d.hid, sh = d.D;
+  tq.ptr = ws + p.q; tk.ptr = ws + p.k; tv.ptr = ws + p.v;
+  tq.stride_b = tk.stride_b = tv.stride_b = sb;
+  tq.stride_tok = tk.stride_tok = tv.stride_tok = stok;
+  tq.stride_head = tk.stride_head = tv.stride_head = sh;
+  hipError_t he = run_projection(d, x, w_q, w_k, w_v, ws + p.wt, ws + p.q, ws + p.k, ws + p.v, nullptr, s);
+  if (he != hipSuccess) return fail(HYB_ERR_HIP, "HIP error: %s", hipGetErrorString(he));
+  // the layer's gradients, dq | dk | dv interleaved per token row ([M][3 hid])
+  char* dqkv = ws + p.dqkv;
+  st = attn_backward_impl(layout, x, tq, tk, tv, text_k, text_v, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin,
+                          rms_weight, softmax_scale, eps, dy, ws + p.dxl, dqkv, dqkv + (size_t)d.hid * 2,
+                          dqkv + (size_t)d.hid * 4, 3 * d.hid, dtext_k, dtext_v, dw_gate_soft, dw_gate_lin,
+                          dw_out_soft, dw_out_lin, drms_weight, nullptr, 0, ws + p.layer, p.layer_bytes, stream, dbg);
+  if (st != HYB_OK) return st;
+  hyb::QkvBwdArgs a;
+  a.M = (long long)d.B * d.N;
+  a.mpad = p.mpad;
+  a.hid = d.hid;
+  a.ksplit = kWgradSplit;
+  a.x = (const hyb::bf16_t*)x;
+  a.wq = (const hyb::bf16_t*)w_q; a.wk = (const hyb::bf16_t*)w_k; a.wv = (const hyb::bf16_t*)w_v;
+  a.dxl = (const hyb::bf16_t*)(ws + p.dxl);
+  a.dqkv = (const hyb::bf16_t*)dqkv;
+  a.dx = (hyb::bf16_t*)dx;
+  a.dwq = dw_q; a.dwk = dw_k; a.dwv = dw_v;
+  a.wcat = (hyb::bf16_t*)(ws + p.wcat);
+  a.xT = (hyb::bf16_t*)(ws + p.xT);
+  a.dqkvT = (hyb::bf16_t*)(ws + p.dqkvT);
+  a.wpart = (float*)(ws + p.wpart);
+  he = hyb::run_qkv_backward(a, s);
+  if (he != hipSuccess) return fail(HYB_ERR_HIP, "HIP error: %s", hipGetErrorString(he));
+  return HYB_OK;
 }
 
 }  // extern "C"

@@ -76,22 +76,21 @@ hipError_t transpose_tok(const uint16_t* src, bool f16, long long M, int C, long
   return hipGetLastError();
 }
 
-// out = sum over ksplit partials [ksplit][R][C]; split_rows: row r < hid ->
-// out0[r][c], else out1[r - hid][c] (C = hid); otherwise column c < hid ->
-// out0[r][c], else out1[r][c - hid] (R = hid).  Null outputs are skipped.
+// out = sum over ksplit partials [ksplit][R][C], split into [hid]-sized
+// chunks along the rows (split_rows: chunk t = r / hid -> out_t[r - t hid][c],
+// C = hid) or along the columns (chunk t = c / hid -> out_t[r][c - t hid],
+// R = hid).  Null outputs are skipped.
 __global__ __launch_bounds__(256) void k_wgrad_reduce(const float* __restrict__ part, int ksplit, int R, int C,
                                                       int hid, bool split_rows, float* __restrict__ out0,
-                                                      float* __restrict__ out1) {
+                                                      float* __restrict__ out1, float* __restrict__ out2) {
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long n = (long long)R * C;
   if (idx >= n) return;
   const int r = (int)(idx / C), c = (int)(idx % C);
-  float* dst;
-  if (split_rows) dst = r < hid ? (out0 ? out0 + (long long)r * C + c : nullptr)
-                                : (out1 ? out1 + (long long)(r - hid) * C + c : nullptr);
-  else dst = c < hid ? (out0 ? out0 + (long long)r * hid + c : nullptr)
-                     : (out1 ? out1 + (long long)r * hid + (c - hid) : nullptr);
-  if (!dst) return;
+  const int t = (split_rows ? r : c) / hid;
+  float* o = t == 0 ? out0 : (t == 1 ? out1 : out2);
+  if (!o) return;
+  float* dst = split_rows ? o + (long long)(r - t * hid) * C + c : o + (long long)r * hid + (c - t * hid);
   float v = 0.f;
   for (int z = 0; z < ksplit; ++z) v += part[z * n + idx];
   *dst = v;
@@ -225,7 +224,7 @@ hipError_t run_bwd_bf16(const Dims& d, const Bf16Args& f, const BwdArgs& a, hipS
       HYB_TRY(launch_wgrad_gemm(a.apT, a.dyT, 2 * hid, hid, a.mpad, a.ksplit, a.wpart, s));
       const long long n = 2LL * hid * hid;
       hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((n + rblocks - 1) / rblocks)), dim3(256), 0, s, a.wpart,
-                         a.ksplit, 2 * hid, hid, hid, true, a.dwos, a.dwol);
+                         a.ksplit, 2 * hid, hid, hid, true, a.dwos, a.dwol, nullptr);
       HYB_TRY(hipGetLastError());
     }
     if (a.dwgs || a.dwgl) {
@@ -234,7 +233,7 @@ hipError_t run_bwd_bf16(const Dims& d, const Bf16Args& f, const BwdArgs& a, hipS
       HYB_TRY(launch_wgrad_gemm(a.xT, a.dzT, hid, 2 * hid, a.mpad, a.ksplit, a.wpart, s));
       const long long n = 2LL * hid * hid;
       hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((n + rblocks - 1) / rblocks)), dim3(256), 0, s, a.wpart,
-                         a.ksplit, hid, 2 * hid, hid, false, a.dwgs, a.dwgl);
+                         a.ksplit, hid, 2 * hid, hid, false, a.dwgs, a.dwgl, nullptr);
       HYB_TRY(hipGetLastError());
     }
   });
@@ -253,6 +252,28 @@ hipError_t run_bwd_bf16(const Dims& d, const Bf16Args& f, const BwdArgs& a, hipS
   });
   HYB_BSTAGE(BST_SOFTMAX, HYB_TRY(launch_softmax_backward(d, a, s)));
   HYB_BSTAGE(BST_LINEAR, HYB_TRY(launch_linear_backward(d, a, s)));
+  return hipSuccess;
+}
+
+// Through the Q/K/V projection: dx = dx_layer + [dq | dk | dv] [W_q | W_k | W_v]^T
+// (one GEMM, K = 3 hid) and, when requested, dW_t = x^T d(q, k, v)_t (one
+// token-contraction GEMM into [hid][3 hid], split into the three weights).
+hipError_t run_qkv_backward(const QkvBwdArgs& a, hipStream_t s) {
+  const int hid = a.hid;
+  const size_t row = (size_t)hid * 2;
+  const bf16_t* w[3] = {a.wq, a.wk, a.wv};
+  for (int t = 0; t < 3; ++t)  // wcat row i = (W_q[i], W_k[i], W_v[i])
+    HYB_TRY(hipMemcpy2DAsync(a.wcat + (size_t)t * hid, 3 * row, w[t], row, row, hid, hipMemcpyDeviceToDevice, s));
+  HYB_TRY(launch_resid_gemm(a.M, hid, 3 * hid, a.dqkv, a.wcat, a.dxl, a.dx, s));
+  if (a.dwq || a.dwk || a.dwv) {
+    HYB_TRY(transpose_tok(a.x, false, a.M, hid, a.mpad, a.xT, s));
+    HYB_TRY(transpose_tok(a.dqkv, false, a.M, 3 * hid, a.mpad, a.dqkvT, s));
+    HYB_TRY(launch_wgrad_gemm(a.xT, a.dqkvT, hid, 3 * hid, a.mpad, a.ksplit, a.wpart, s));
+    const long long n = 3LL * hid * hid;
+    hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.wpart, a.ksplit, hid,
+                       3 * hid, hid, false, a.dwq, a.dwk, a.dwv);
+    HYB_TRY(hipGetLastError());
+  }
   return hipSuccess;
 }
 

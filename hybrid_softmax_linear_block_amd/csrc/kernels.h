@@ -75,6 +75,7 @@ struct BwdArgs {
   const float* comb_z;                     // [B*H][T][D]
   // outputs (contiguous [B][tokens][H][D] / [B][N][hid]); weight gradients nullable
   bf16_t *dx, *dq, *dk, *dv, *dtk, *dtv;
+  int ld_qkv;                              // row stride of dq, dk, dv in elements (hid, or 3 hid when interleaved)
   float *dwgs, *dwgl, *dwos, *dwol, *drmsw;
   // scratch
   bf16_t *wo_cat, *wg_cat;                 // [2hid][hid] = [W_os; W_ol], [hid][2hid] rows (W_gs[i], W_gl[i])
@@ -100,6 +101,19 @@ struct BwdArgs {
 };
 hipError_t run_bwd_bf16(const Dims& d, const Bf16Args& fwd, const BwdArgs& a, hipStream_t s);
 hipError_t launch_bf16_to_f32(const bf16_t* src, float* dst, long long n, hipStream_t s);
+
+// Backward through the Q/K/V projection (backward_bf16.hip).
+struct QkvBwdArgs {
+  long long M, mpad;
+  int hid, ksplit;
+  const bf16_t *x, *wq, *wk, *wv;
+  const bf16_t *dxl, *dqkv;     // the layer's dx [M][hid]; [dq | dk | dv] rows [M][3 hid]
+  bf16_t* dx;                   // output [M][hid]
+  float *dwq, *dwk, *dwv;       // nullable [hid][hid]
+  bf16_t *wcat, *xT, *dqkvT;    // scratch [hid][3 hid], [hid][mpad], [3 hid][mpad]
+  float* wpart;                 // [ksplit][hid][3 hid]
+};
+hipError_t run_qkv_backward(const QkvBwdArgs& a, hipStream_t s);
 
 // ---- feed-forward of the block (dit_block.hip) ----
 // z = y + GELU_tanh(RMSNorm(y) W_1) W_2 for y [M][hid] bf16; weights [in][out]

@@ -48,7 +48,7 @@ template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2)))
 void k_lin_bwd_q(Dims d, Tensor4 q, const bf16_t* __restrict__ chi, const bf16_t* __restrict__ clo,
                  const float* __restrict__ cz, float eps, int tt, const float* __restrict__ dol,
-                 const float* __restrict__ dqs, bf16_t* __restrict__ dq, bf16_t* __restrict__ dnum,
+                 const float* __restrict__ dqs, bf16_t* __restrict__ dq, int ldq, bf16_t* __restrict__ dnum,
                  float* __restrict__ dden) {
   constexpr int G = D / 8, KS = D / 16, DB = D / 32;
   using SW = Swz<D>;
@@ -83,6 +83,7 @@ void k_lin_bwd_q(Dims d, Tensor4 q, const bf16_t* __restrict__ chi, const bf16_t
     const bool ok = p < p_end;
     const long long tok = (long long)f * d.n + (ok ? p : p0);
     const long long row = ((long long)b * d.N + tok) * d.hid + (long long)h * D;  // [M][hid] offset
+    const long long qo = ((long long)b * d.N + tok) * ldq + (long long)h * D;      // output row of dq
     const bf16_t* qrow = (const bf16_t*)q.p + tok_off(q, b, tok, h);
     bf16x8 ph[KS], pl[KS];
     float den = 0.f;
@@ -169,7 +170,7 @@ void k_lin_bwd_q(Dims d, Tensor4 q, const bf16_t* __restrict__ chi, const bf16_t
           const float o1 = (acc[4 * jg + 1] + Z[d0 + 1] * ddn) * dphi_f(q4.y) + s4.y;
           const float o2 = (acc[4 * jg + 2] + Z[d0 + 2] * ddn) * dphi_f(q4.z) + s4.z;
           const float o3 = (acc[4 * jg + 3] + Z[d0 + 3] * ddn) * dphi_f(q4.w) + s4.w;
-          *(uint2*)(dq + row + d0) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+          *(uint2*)(dq + qo + d0) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
         }
       }
     }
@@ -234,7 +235,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 void k_lin_bwd_kv(Dims d, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv, const bf16_t* __restrict__ dsh,
                   const bf16_t* __restrict__ dsl, const float* __restrict__ dsz, int tt,
                   const float* __restrict__ dks, const float* __restrict__ dvs, const float* __restrict__ dtks,
-                  const float* __restrict__ dtvs, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
+                  const float* __restrict__ dtvs, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int ldkv,
                   bf16_t* __restrict__ dtk, bf16_t* __restrict__ dtv) {
   constexpr int G = D / 8, KS = D / 16, DB = D / 32;
   using SW = Swz<D>;
@@ -275,8 +276,9 @@ void k_lin_bwd_kv(Dims d, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv, const bf
     const bf16_t* vrow = text ? (const bf16_t*)tv.p + tok_off(tv, b, pc, h)
                               : (const bf16_t*)v.p + tok_off(v, b, (long long)g * d.n + pc, h);
     // [M][hid] row offset of the token's head in the gradient buffers
-    const long long orow = (text ? ((long long)b * d.L + pc) : ((long long)b * d.N + (long long)g * d.n + pc)) *
-                               d.hid + (long long)h * D;
+    const long long tok_row = text ? ((long long)b * d.L + pc) : ((long long)b * d.N + (long long)g * d.n + pc);
+    const long long orow = tok_row * d.hid + (long long)h * D;                       // fp32 partials
+    const long long wrow = tok_row * (text ? d.hid : ldkv) + (long long)h * D;        // bf16 outputs
     bf16x8 vf[KS], ph[KS], pl[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -315,7 +317,7 @@ void k_lin_bwd_kv(Dims d, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv, const bf
           const float o1 = (acc[4 * jg + 1] + Z[d0 + 1]) * dphi_f(k4.y) + s4.y;
           const float o2 = (acc[4 * jg + 2] + Z[d0 + 2]) * dphi_f(k4.z) + s4.z;
           const float o3 = (acc[4 * jg + 3] + Z[d0 + 3]) * dphi_f(k4.w) + s4.w;
-          *(uint2*)(ko + orow + d0) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+          *(uint2*)(ko + wrow + d0) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
         }
       }
     }
@@ -338,7 +340,7 @@ void k_lin_bwd_kv(Dims d, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4 tv, const bf
         for (int jg = 0; jg < 4; ++jg) {
           const int e0 = i * 32 + 8 * jg + 4 * half;
           const float4 s4 = *(const float4*)(vs_ + orow + e0);
-          *(uint2*)(vo + orow + e0) = make_uint2(pack_bf16x2(acc[4 * jg] + s4.x, acc[4 * jg + 1] + s4.y),
+          *(uint2*)(vo + wrow + e0) = make_uint2(pack_bf16x2(acc[4 * jg] + s4.x, acc[4 * jg + 1] + s4.y),
                                                  pack_bf16x2(acc[4 * jg + 2] + s4.z, acc[4 * jg + 3] + s4.w));
         }
       }
@@ -352,10 +354,10 @@ hipError_t launch_linear_backward(const Dims& d, const BwdArgs& a, hipStream_t s
     const long long grid = (long long)d.B * d.H * d.T * ((d.n + tt - 1) / tt);
     if (d.D == 128)
       hipLaunchKernelGGL(k_lin_bwd_q<128>, dim3((unsigned)grid), dim3(256), 0, s, d, a.q, a.comb_hi, a.comb_lo,
-                         a.comb_z, a.eps, tt, a.dol, a.dq_s, a.dq, a.dnum, a.dden);
+                         a.comb_z, a.eps, tt, a.dol, a.dq_s, a.dq, a.ld_qkv, a.dnum, a.dden);
     else
       hipLaunchKernelGGL(k_lin_bwd_q<64>, dim3((unsigned)grid), dim3(256), 0, s, d, a.q, a.comb_hi, a.comb_lo,
-                         a.comb_z, a.eps, tt, a.dol, a.dq_s, a.dq, a.dnum, a.dden);
+                         a.comb_z, a.eps, tt, a.dol, a.dq_s, a.dq, a.ld_qkv, a.dnum, a.dden);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -381,10 +383,10 @@ hipError_t launch_linear_backward(const Dims& d, const BwdArgs& a, hipStream_t s
     const long long grid = (long long)d.B * d.H * (d.T + 1) * ((ntok + tt - 1) / tt);
     if (d.D == 128)
       hipLaunchKernelGGL(k_lin_bwd_kv<128>, dim3((unsigned)grid), dim3(256), 0, s, d, a.k, a.v, a.tk, a.tv, a.dsh,
-                         a.dsl, a.dsz, tt, a.dk_s, a.dv_s, a.dtk_s, a.dtv_s, a.dk, a.dv, a.dtk, a.dtv);
+                         a.dsl, a.dsz, tt, a.dk_s, a.dv_s, a.dtk_s, a.dtv_s, a.dk, a.dv, a.ld_qkv, a.dtk, a.dtv);
     else
       hipLaunchKernelGGL(k_lin_bwd_kv<64>, dim3((unsigned)grid), dim3(256), 0, s, d, a.k, a.v, a.tk, a.tv, a.dsh,
-                         a.dsl, a.dsz, tt, a.dk_s, a.dv_s, a.dtk_s, a.dtv_s, a.dk, a.dv, a.dtk, a.dtv);
+                         a.dsl, a.dsz, tt, a.dk_s, a.dv_s, a.dtk_s, a.dtv_s, a.dk, a.dv, a.ld_qkv, a.dtk, a.dtv);
     return hipGetLastError();
   }
 }

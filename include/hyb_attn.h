@@ -233,6 +233,27 @@ typedef struct {
 /* Bytes of device workspace hyb_attn_backward() needs (bf16 activations). */
 hyb_status hyb_backward_workspace_size(const hyb_layout* layout, size_t* bytes);
 
+/*
+ * Backward of the layer with its Q/K/V projection (hyb_block_forward): stage
+ * B's LoRA adapters on the Q/K/V projections need the gradients through it.
+ * Recomputes q, k, v = x W_q, x W_k, x W_v (bf16) and the layer, runs the
+ * layer's backward, then
+ *   dx = dx_layer + dq W_q^T + dk W_k^T + dv W_v^T   (one GEMM over [dq|dk|dv])
+ *   dW_q = x^T dq, dW_k = x^T dk, dW_v = x^T dv       (float32, each NULL when frozen)
+ * Other gradients and arguments as in hyb_attn_backward() (without `saved`);
+ * workspace of hyb_block_backward_workspace_size() bytes.  dx, dw_q, dw_k,
+ * dw_v must not overlap each other, x, dy or the workspace.
+ */
+hyb_status hyb_block_backward_workspace_size(const hyb_layout* layout, size_t* bytes);
+hyb_status hyb_block_backward(const hyb_layout* layout, const void* x, const void* w_q, const void* w_k,
+                              const void* w_v, hyb_tensor text_k, hyb_tensor text_v, const void* w_gate_soft,
+                              const void* w_gate_lin, const void* w_out_soft, const void* w_out_lin,
+                              const void* rms_weight, float softmax_scale, float eps, const void* dy, void* dx,
+                              void* dtext_k, void* dtext_v, float* dw_q, float* dw_k, float* dw_v,
+                              float* dw_gate_soft, float* dw_gate_lin, float* dw_out_soft, float* dw_out_lin,
+                              float* drms_weight, void* workspace, size_t workspace_bytes, void* stream,
+                              const hyb_bwd_debug* dbg);
+
 /* Bytes of the `saved` buffer of hyb_attn_forward_train(). */
 hyb_status hyb_saved_size(const hyb_layout* layout, size_t* bytes);
 

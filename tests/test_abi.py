@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
                             "hyb_qkv_project", "hyb_block_workspace_size", "hyb_block_forward",
                             "hyb_backward_workspace_size", "hyb_attn_backward",
                             "hyb_dit_block_workspace_size", "hyb_dit_block_forward", "hyb_saved_size",
-                            "hyb_attn_forward_train"])
+                            "hyb_attn_forward_train", "hyb_block_backward_workspace_size", "hyb_block_backward"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -278,3 +278,39 @@ def test_dit_block_validation_errors():
     n = api.dit_block_workspace_size(lay, 2048)
     M, hid = 15 * 1024, 512
     assert n >= api.block_workspace_size(lay) + 2 * M * hid * 2 + M * 2048 * 2 + 2 * 2048 * hid * 2
+
+
+def test_block_backward_validation_errors():
+    lib = api.load()
+    lay = api.Layout(1, 15, 1024, 128, 8, 64)
+    c = lay.c()
+    base = 1 << 40
+    T4 = api._Tensor
+    st = (128 * 512, 512, 64)
+    slot = iter(range(1, 64))
+
+    def nxt():
+        return base + (next(slot) << 34)
+    a0 = dict(x=nxt(), wq=nxt(), wk=nxt(), wv=nxt(), tk=T4(nxt(), *st), tv=T4(nxt(), *st), wgs=nxt(), wgl=nxt(),
+              wos=nxt(), wol=nxt(), rms=nxt(), scale=0.0, eps=1e-6, dy=nxt(), dx=nxt(), dtk=nxt(), dtv=nxt(),
+              dwq=nxt(), dwk=nxt(), dwv=nxt(), dwgs=nxt(), dwgl=nxt(), dwos=nxt(), dwol=nxt(), drms=nxt(),
+              ws=nxt(), wsb=1 << 34)
+
+    def call(**over):
+        a = dict(a0)
+        a.update(over)
+        r = lib.hyb_block_backward(ctypes.byref(c), a["x"], a["wq"], a["wk"], a["wv"], a["tk"], a["tv"], a["wgs"],
+                                   a["wgl"], a["wos"], a["wol"], a["rms"], a["scale"], a["eps"], a["dy"], a["dx"],
+                                   a["dtk"], a["dtv"], a["dwq"], a["dwk"], a["dwv"], a["dwgs"], a["dwgl"], a["dwos"],
+                                   a["dwol"], a["drms"], a["ws"], a["wsb"], None, None)
+        return r, lib.hyb_last_error().decode()
+
+    assert call(wq=None)[0] == api.HYB_ERR_INVALID_ARGUMENT
+    assert call(dwk=a0["dwk"] + 4)[0] == api.HYB_ERR_INVALID_ARGUMENT
+    r, msg = call(dx=a0["x"] + 1024)
+    assert r == api.HYB_ERR_INVALID_ARGUMENT and "overlaps" in msg
+    r, msg = call(dwq=a0["dwk"])
+    assert r == api.HYB_ERR_INVALID_ARGUMENT and "overlaps" in msg
+    r, msg = call(wsb=1000)
+    assert r == api.HYB_ERR_WORKSPACE_TOO_SMALL
+    assert api.block_backward_workspace_size(lay) > api.backward_workspace_size(lay)

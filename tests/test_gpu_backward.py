@@ -171,3 +171,49 @@ def test_backward_from_training_forward_bit_identical():
     assert torch.equal(y_plain, y_train)
     for k_, v_ in g.items():
         assert np.array_equal(v_.float().cpu().numpy().astype(np.float64), base[k_]), k_
+
+
+BLOCK_CASES = [CASES[1], Workload("bwd-block-d128", 1, 5, 60, 16, 2, 128, qkv_scale=0.5, seed=75)]
+
+
+@pytest.mark.parametrize("w", BLOCK_CASES, ids=[w.name for w in BLOCK_CASES])
+def test_block_backward_matches_oracle(w):
+    """Through the Q/K/V projection: dx, dtext_k/v and every weight gradient
+    (the projection's included) against the oracle's block backward, which
+    takes the library's bf16 rounding of q, k, v as its reading of the stored
+    projections (the gradient is evaluated at the stored values)."""
+    import torch
+    from hybrid_softmax_linear_block_amd.inputs import make_projection_weights
+    from oracle.projection import qkv_projection, round_bf16
+    inp = make_inputs(w)
+    dy = make_grad_output(w)
+    pw = make_projection_weights(w)
+    d = {k: _dev(v) for k, v in inp.items()}
+    p = {k: _dev(v) for k, v in pw.items()}
+    g = api.block_backward(gu.api_layout(w), d["x"], p["w_q"], p["w_k"], p["w_v"], d["text_k"], d["text_v"],
+                           d["w_gs"], d["w_gl"], d["w_os"], d["w_ol"], d["rms_w"], _dev(dy))
+    torch.cuda.synchronize()
+    got = {k: v.float().cpu().numpy().astype(np.float64) for k, v in g.items()}
+    # oracle: layer gradients at the bf16-stored projections, then through the projection
+    q, k, v = (round_bf16(t) for t in qkv_projection(inp["x"], pw["w_q"], pw["w_k"], pw["w_v"], w.heads))
+    ref = obw.hybrid_backward(dict(inp, q=q, k=k, v=v), gu.oracle_layout(w), dy)
+    M, hid = w.batch * w.n_video, w.hidden
+    xf = np.asarray(inp["x"], np.float64).reshape(M, hid)
+    dx = ref["dx"].reshape(M, hid)
+    for name, dname in (("w_q", "dq"), ("w_k", "dk"), ("w_v", "dv")):
+        dd = ref[dname].reshape(M, hid)
+        dx = dx + dd @ np.asarray(pw[name], np.float64).T
+        ref["d" + name] = xf.T @ dd
+    ref["dx"] = dx.reshape(w.batch, w.n_video, hid)
+    failed = []
+    for gname, rname in (("dx", "dx"), ("dtext_k", "dtext_k"), ("dtext_v", "dtext_v"), ("dw_q", "dw_q"),
+                         ("dw_k", "dw_k"), ("dw_v", "dw_v"), ("dw_gate_soft", "dw_gs"), ("dw_out_lin", "dw_ol"),
+                         ("drms_weight", "drms_w")):
+        r = ref[rname]
+        if r.size == 0:
+            continue
+        e = gu.errors(got[gname].reshape(r.shape), r)
+        print(w.name, gname, "max %.2e mean %.2e" % e, flush=True)
+        if not (e[0] <= TOL_GRAD[0] and e[1] <= TOL_GRAD[1]):
+            failed.append((gname, e))
+    assert not failed, failed
