@@ -201,6 +201,50 @@ def write_traffic(pmc_dir, w):
     print(json.dumps(rec))
 
 
+def host_info():
+    """CPU model, usable cores and NumPy's BLAS build (for the oracle timings)."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        b = np.show_config(mode="dicts").get("Build Dependencies", {}).get("blas", {})
+        blas = "%s %s" % (b.get("name"), b.get("version"))
+    except Exception:  # pragma: no cover - older NumPy
+        pass
+    return {"cpu_model": model, "cores": len(os.sched_getaffinity(0)), "blas": blas}
+
+
+def oracle_full(w):
+    """Wall time of the fp64 oracle over every token of a workload (no
+    sampling), in the same units as the bench."""
+    import oracle
+    from oracle.layout import Layout as OLayout
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    info = host_info()
+    ctx = threadpool_limits(limits=info["cores"]) if threadpool_limits else None
+    inp = make_inputs(w)
+    lay = OLayout(w.batch, w.frames, w.tokens_per_frame, w.text_tokens, w.heads, w.head_dim,
+                  w.chunk_frames, w.chunk_radius, w.anchor_first, w.anchor_last)
+    try:
+        t0 = time.perf_counter()
+        oracle.hybrid_forward(inp, lay)
+        wall = time.perf_counter() - t0
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    return dict(info, workload=describe(w), kind="oracle, every token (fp64 NumPy)", wall_s=round(wall, 2),
+                value=w.batch * w.n_video / wall / 1e6, unit="Mtokens/s")
+
+
 def cpu_baseline(w, inp, budget_s=20.0):
     """Time the fp64 oracle on the host on a bounded token sample and scale
     to Mtokens/s: full-state build (all tokens) + per-token work measured on
@@ -232,7 +276,9 @@ def cpu_baseline(w, inp, budget_s=20.0):
             ctx.__exit__(None, None, None)
     n_s = len(tok)
     full = t_states + t_rows * (w.n_video / n_s)
+    info = host_info()
     return {"value": w.batch * w.n_video / full / 1e6, "unit": "Mtokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": info["cpu_model"], "blas": info["blas"],
             "sample": ("fp64 NumPy oracle: full per-frame state build over all %d tokens (%.1f s) + softmax, "
                        "readout and epilogue for %d sampled query tokens (%.1f s), per-token part scaled "
                        "linearly to all %d tokens" % (w.n_video, t_states, n_s, t_rows, w.n_video)),
@@ -359,6 +405,8 @@ def main():
                     help="time the backward pass (forward recompute + every gradient) instead of the forward")
     ap.add_argument("--train", action="store_true",
                     help="time a training step: forward keeping its values, then the backward reading them")
+    ap.add_argument("--oracle-full", action="store_true",
+                    help="only time the fp64 oracle over every token of --workload (host only) and print JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--write-traffic", metavar="PMC_DIR",
@@ -367,6 +415,9 @@ def main():
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(args.write_traffic, WORKLOADS[args.workload])
+        return
+    if args.oracle_full:
+        print(json.dumps(oracle_full(WORKLOADS[args.workload])), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the layer shards by heads; "
