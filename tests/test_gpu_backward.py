@@ -34,6 +34,8 @@ CASES = [
     Workload("bwd-chunked", 1, 9, 40, 36, 2, 64, chunk_frames=2, qkv_scale=0.5, seed=73),
     Workload("bwd-no-anchor-r0", 1, 6, 64, 8, 2, 128, chunk_radius=0, anchor_first=False, anchor_last=False,
              qkv_scale=0.5, seed=74),
+    Workload("bwd-tiny-frames-hid192", 2, 4, 5, 3, 3, 64, qkv_scale=0.5, seed=76),   # 5 tokens/frame, hid 192
+    Workload("bwd-one-frame", 1, 1, 90, 10, 2, 64, qkv_scale=0.5, seed=77),
 ]
 
 NAMES = [("dx", "dx"), ("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dtext_k", "dtext_k"),
