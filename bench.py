@@ -94,6 +94,10 @@ def stage_work(w, soft, block=False, ffn_hidden=0):
     }
     if soft:
         work["quant"] = ("hbm", (3 * B * N + 2 * B * L) * hid * (es + 1))
+    if soft == "fp8_mx":
+        # gate and output weights read in bf16, written as codes + exponents;
+        # x read in bf16, written as codes + exponents (unless the projection did)
+        work["weights"] = ("hbm", 2 * (2 * hid * hid) * (2 + 1 + 1.0 / 32) + B * N * hid * (2 + 1 + 1.0 / 32))
     if block:
         # x [B*N][hid] @ [hid][3 hid]: 2 * B*N * hid * 3 hid
         work["qkv"] = ("mfma", 2.0 * B * N * hid * 3 * hid)
@@ -124,7 +128,8 @@ def stage_roofline(w, soft, stage_ms, block=False, ffn_hidden=0):
         if t <= 0:
             continue
         if bound == "mfma":
-            peak = PEAK["fp8" if (soft and k == "softmax") else w.act]
+            fp8 = soft and (k == "softmax" or (soft == "fp8_mx" and k in ("gate", "out", "qkv")))
+            peak = PEAK["fp8" if fp8 else w.act]
             ach = amount / (t * 1e-3) / 1e12
             out[k] = {"bound": "mfma", "algorithmic": amount, "unit": "TFLOP/s", "achieved": round(ach, 2),
                       "peak": peak, "frac": round(ach / peak, 4)}
@@ -141,7 +146,8 @@ def describe(w):
                 w.name, w.batch, w.frames, w.tokens_per_frame, w.heads, w.head_dim, w.hidden, w.text_tokens,
                 w.chunk_frames, w.chunk_radius,
                 "/".join(str(a) for a, on in ((0, w.anchor_first), (w.frames - 1, w.anchor_last)) if on) or "none",
-                w.act, " (softmax fp8)" if w.soft == "fp8" else ""))
+                w.act, {"fp8": " (softmax fp8)", "fp8_mx": " (fp8 version: e4m3 softmax branch, MX e4m3 GEMMs)"}.get(
+                    w.soft, "")))
 
 
 def traffic_for(kernel_key, workload):
@@ -401,6 +407,8 @@ def main():
                     help="time the layer with its Q/K/V projection (x -> q, k, v -> y) instead of the layer")
     ap.add_argument("--dit", action="store_true",
                     help="time one DiT block: projection, layer and the feed-forward (4 x hid)")
+    ap.add_argument("--fp8-mx", action="store_true",
+                    help="the fp8 version: e4m3 softmax branch and MX e4m3 GEMMs (hidden size a multiple of 256)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (forward recompute + every gradient) instead of the forward")
     ap.add_argument("--train", action="store_true",
@@ -443,7 +451,9 @@ def main():
     dt = torch.float32 if w.act == "f32" else torch.bfloat16
     dev = {k: torch.from_numpy(v).to("cuda").to(dt) for k, v in inp.items()}
     lay = layout_of(w)
-    soft = "fp8" if w.soft == "fp8" else None
+    soft = "fp8_mx" if args.fp8_mx else ("fp8" if w.soft == "fp8" else None)
+    if args.fp8_mx:
+        w = w.with_(soft="fp8_mx")
     if args.backward or args.train:
         bench_backward(args, w, lay, dev, torch)
         return
@@ -517,7 +527,8 @@ def main():
     out = {
         "metric": METRIC_DIT if args.dit else (METRIC_BLOCK if args.block else METRIC), "value": round(value, 4), "unit": "Mtokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.act, "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16 + e4m3 (MX GEMMs, fp8 softmax)" if soft == "fp8_mx" else w.act,
+        "data": "synthetic",
         "config": {"workload": describe(w), "batch": w.batch, "video_tokens": w.n_video,
                    "text_tokens": w.text_tokens, "heads": w.heads, "head_dim": w.head_dim,
                    "parallelism": "none (1 GPU)"},

@@ -14,7 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhybattn.so")
 
 HYB_OK, HYB_ERR_INVALID_ARGUMENT, HYB_ERR_UNSUPPORTED, HYB_ERR_WORKSPACE_TOO_SMALL, HYB_ERR_HIP = range(5)
-DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
+DTYPES = {"f32": 0, "bf16": 1, "fp8": 2, "fp8_mx": 3}  # fp8_mx: fp8 softmax branch + MX e4m3 GEMMs
 
 
 class HybError(RuntimeError):

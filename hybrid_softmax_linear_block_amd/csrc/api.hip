@@ -46,9 +46,13 @@ hyb_status check_layout(const hyb_layout* L, bool tables_only) {
 
 hyb_status check_dtypes(const hyb_layout* L, hyb_dtype act, hyb_dtype soft) {
   if (act != HYB_F32 && act != HYB_BF16) return fail(HYB_ERR_UNSUPPORTED, "activation dtype must be F32 or BF16");
-  if (soft != act && !(soft == HYB_FP8_E4M3 && act == HYB_BF16))
-    return fail(HYB_ERR_UNSUPPORTED, "softmax dtype must equal the activation dtype, or be FP8_E4M3 with BF16");
+  if (soft != act && !((soft == HYB_FP8_E4M3 || soft == HYB_FP8_MX) && act == HYB_BF16))
+    return fail(HYB_ERR_UNSUPPORTED,
+                "softmax dtype must equal the activation dtype, or be FP8_E4M3 / FP8_MX with BF16");
   if (act == HYB_BF16 && L->head_dim == 32) return fail(HYB_ERR_UNSUPPORTED, "bf16 path needs head_dim 64 or 128");
+  if (soft == HYB_FP8_MX && (L->heads * L->head_dim) % 256 != 0)
+    return fail(HYB_ERR_UNSUPPORTED, "FP8_MX needs a hidden size that is a multiple of 256 (got %d)",
+                L->heads * L->head_dim);
   return HYB_OK;
 }
 
@@ -85,8 +89,11 @@ void state_split(const hyb::Dims& d, int* split, int* ts, int* tsplit) {
 
 enum {
   W_OS, W_OL, W_SS, W_RINV, W_PART, W_PRE, W_CHI, W_CLO, W_CZ, W_AP, W_WG, W_WO,
-  W_Q8, W_K8, W_V8, W_TK8, W_TV8, W_SC, W_AM, W_STATES, W_COMB, W_COUNT
+  W_Q8, W_K8, W_V8, W_TK8, W_TV8, W_SC, W_AM, W_STATES, W_COMB, W_X8, W_XS, W_AS, W_WGS, W_WOS, W_COUNT
 };
+
+// Token rows of the MX exponent arrays: whole 256-token GEMM tiles.
+size_t mx_rows(const hyb::Dims& d) { return ((size_t)d.B * d.N + 255) / 256 * 256; }
 
 struct Plan {
   size_t off[W_COUNT];
@@ -118,7 +125,15 @@ Plan make_plan(const hyb::Dims& d, hyb_dtype act, hyb_dtype soft) {
     sz[W_AP] = BN * 2 * hid * 2;
     sz[W_WG] = 2 * hid * hid * 2;
     sz[W_WO] = 2 * hid * hid * 2;
-    if (soft == HYB_FP8_E4M3) {
+    if (soft == HYB_FP8_MX) {  // e4m3 GEMM operands (codes reuse W_WG, W_WO, W_AP)
+      const size_t mp = mx_rows(d);
+      sz[W_X8] = BN * hid;
+      sz[W_XS] = hid / 32 * mp;
+      sz[W_AS] = 2 * hid / 32 * mp;
+      sz[W_WGS] = hid / 32 * 2 * hid;
+      sz[W_WOS] = 2 * hid / 32 * hid;
+    }
+    if (soft == HYB_FP8_E4M3 || soft == HYB_FP8_MX) {
       const size_t vt = (size_t)d.T * ((d.n + 63) / 64) * 64;  // per (b,h) padded video keys
       const size_t lt = (size_t)((d.L + 63) / 64) * 64;
       sz[W_Q8] = BN * hid;
@@ -320,8 +335,16 @@ hyb_status attn_forward_impl(const hyb_layout* layout, hyb_dtype act, hyb_dtype 
     a.rmsw = (const hyb::bf16_t*)rms_weight;
     a.scale_log2 = sl2;
     a.eps = eps;
-    a.fp8 = soft == HYB_FP8_E4M3;
+    a.fp8 = soft == HYB_FP8_E4M3 || soft == HYB_FP8_MX;
     a.qkv_absmax_ready = a.fp8 && after_projection;
+    a.mx = soft == HYB_FP8_MX;
+    a.mx_x_ready = a.mx && after_projection;
+    a.mpad = (long long)mx_rows(d);
+    a.x8 = (uint8_t*)(ws + plan.off[W_X8]);
+    a.xs = (uint8_t*)(ws + plan.off[W_XS]);
+    a.aps = (uint8_t*)(ws + plan.off[W_AS]);
+    a.wgs8 = (uint8_t*)(ws + plan.off[W_WGS]);
+    a.wos8 = (uint8_t*)(ws + plan.off[W_WOS]);
     a.os = (uint16_t*)(ws + plan.off[W_OS]);
     a.ol = (uint16_t*)(ws + plan.off[W_OL]);
     a.ss = (float*)(ws + plan.off[W_SS]);
@@ -461,7 +484,7 @@ namespace {
 // Block workspace: [layer plan | projection weights | q | k | v].
 struct BlockPlan {
   Plan layer;
-  size_t wt, q, k, v, total;
+  size_t wt, q, k, v, wts, total;  // wts: MX exponents of the projection weights
 };
 
 BlockPlan make_block_plan(const hyb::Dims& d, hyb_dtype soft) {
@@ -472,7 +495,8 @@ BlockPlan make_block_plan(const hyb::Dims& d, hyb_dtype soft) {
   b.q = b.wt + qkv_weight_bytes(d);
   b.k = b.q + act;
   b.v = b.k + act;
-  b.total = b.v + act;
+  b.wts = b.v + act;
+  b.total = b.wts + (soft == HYB_FP8_MX ? align_up((size_t)d.hid / 32 * 3 * d.hid, 256) : 0);
   return b;
 }
 
@@ -541,8 +565,25 @@ hyb_status hyb_block_forward(const hyb_layout* layout, hyb_dtype soft, const voi
   hipError_t he = hipSuccess;
   if (ev) he = hipEventRecord(ev[2 * HYB_STAGE_QKV], s);
   // fp8: the projection writes the absmax of q, k, v straight into the layer's absmax buffer
-  uint32_t* amx = soft == HYB_FP8_E4M3 ? (uint32_t*)(ws + bp.layer.off[W_AM]) : nullptr;
-  if (he == hipSuccess) he = run_projection(d, x, w_q, w_k, w_v, ws + bp.wt, ws + bp.q, ws + bp.k, ws + bp.v, amx, s);
+  uint32_t* amx = soft != HYB_BF16 ? (uint32_t*)(ws + bp.layer.off[W_AM]) : nullptr;
+  if (soft == HYB_FP8_MX) {
+    // MX projection: x is quantised once, into the layer's buffers, for this
+    // GEMM and the gate GEMM
+    uint8_t* x8 = (uint8_t*)(ws + bp.layer.off[W_X8]);
+    uint8_t* xs = (uint8_t*)(ws + bp.layer.off[W_XS]);
+    uint8_t* wt8 = (uint8_t*)(ws + bp.wt);
+    uint8_t* wts = (uint8_t*)(ws + bp.wts);
+    if (he == hipSuccess)
+      he = hyb::launch_mx_weights(2, (const hyb::bf16_t*)w_q, (const hyb::bf16_t*)w_k, (const hyb::bf16_t*)w_v, d.hid,
+                                  wt8, wts, s);
+    if (he == hipSuccess)
+      he = hyb::launch_mx_rows((const hyb::bf16_t*)x, (long long)d.B * d.N, d.hid, (long long)mx_rows(d), x8, xs, s);
+    if (he == hipSuccess)
+      he = hyb::launch_qkv_gemm_mx(d, x8, xs, (long long)mx_rows(d), wt8, wts, (hyb::bf16_t*)(ws + bp.q),
+                                   (hyb::bf16_t*)(ws + bp.k), (hyb::bf16_t*)(ws + bp.v), amx, s);
+  } else if (he == hipSuccess) {
+    he = run_projection(d, x, w_q, w_k, w_v, ws + bp.wt, ws + bp.q, ws + bp.k, ws + bp.v, amx, s);
+  }
   if (he == hipSuccess && ev) he = hipEventRecord(ev[2 * HYB_STAGE_QKV + 1], s);
   if (he != hipSuccess) return fail(HYB_ERR_HIP, "HIP error: %s", hipGetErrorString(he));
   return attn_forward_impl(layout, HYB_BF16, soft, x, tq, tk, tv, text_k, text_v, w_gate_soft, w_gate_lin,

@@ -36,8 +36,17 @@ hipError_t launch_f16_to_f32(const uint16_t* src, float* dst, long long n, hipSt
   return hipGetLastError();
 }
 
+// MX operands of the gate and output GEMMs: weights, and x unless the
+// projection already quantised it.
+static hipError_t quantise_mx(const Dims& d, const Bf16Args& a, hipStream_t s) {
+  HYB_TRY(launch_mx_weights(0, a.wgs, a.wgl, nullptr, d.hid, (uint8_t*)a.wg_t, a.wgs8, s));
+  HYB_TRY(launch_mx_weights(1, a.wos, a.wol, nullptr, d.hid, (uint8_t*)a.wo_t, a.wos8, s));
+  if (!a.mx_x_ready) HYB_TRY(launch_mx_rows(a.x, (long long)d.B * d.N, d.hid, a.mpad, a.x8, a.xs, s));
+  return hipSuccess;
+}
+
 hipError_t run_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
-  HYB_STAGE(ST_WEIGHTS, launch_weights_bf16(d, a, s));
+  HYB_STAGE(ST_WEIGHTS, a.mx ? quantise_mx(d, a, s) : launch_weights_bf16(d, a, s));
   if (a.fp8) {
     HYB_STAGE(ST_QUANT, launch_quant_fp8(d, a, s));
     HYB_STAGE(ST_SOFTMAX, launch_softmax_fp8(d, a, s));
@@ -48,8 +57,8 @@ hipError_t run_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
   HYB_STAGE(ST_STATES, launch_states_bf16(d, a, s));
   HYB_STAGE(ST_SCAN, launch_scan_bf16(d, a, s));
   HYB_STAGE(ST_READOUT, launch_readout_bf16(d, a, s));
-  HYB_STAGE(ST_GATE, launch_gate_gemm_bf16(d, a, s));
-  HYB_STAGE(ST_OUT, launch_out_gemm_bf16(d, a, s));
+  HYB_STAGE(ST_GATE, a.mx ? launch_gate_gemm_mx(d, a, s) : launch_gate_gemm_bf16(d, a, s));
+  HYB_STAGE(ST_OUT, a.mx ? launch_out_gemm_mx(d, a, s) : launch_out_gemm_bf16(d, a, s));
   return hipSuccess;
 }
 

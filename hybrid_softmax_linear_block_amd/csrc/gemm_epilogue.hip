@@ -16,6 +16,7 @@
 #include <type_traits>
 
 #include "kernels_bf16.h"
+#include "mx_common.h"
 
 namespace hyb {
 
@@ -53,6 +54,13 @@ struct GemmArgs {
   float* part;
   // feed-forward (EPI_GELU): out[M][N] = bf16(GELU_tanh(acc))
   bf16_t* out;
+  // MX operands (MX = true): A and Bt hold e4m3 codes ([M][ldk], [N][ldk]
+  // bytes); sa [K/128][mpad][4] and sb [K/128][N][4] hold one E8M0 exponent
+  // per 32 contraction elements of each row (mpad: M rounded up to 256)
+  const uint8_t *sa, *sb;
+  long long mpad;
+  // gate epilogue with MX output: A' codes [M][2 hid] and exponents [2 hid / 128][mpad][4]
+  uint8_t *ap8, *aps;
 };
 
 // GELU, tanh form: 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))), with
@@ -70,18 +78,30 @@ __device__ __forceinline__ float gelu_tanh_f(float u) {
 // k-tile t is multiplied.  The k loop is unrolled by ST so that every LDS
 // address is a per-lane base plus an immediate, and the DMA source is a
 // scalar base (bumped per k-tile) plus a fixed per-lane offset.
-template <int WM, int WN, int WTM, int WFN, int BK, int ST, int WPE, int EPI, int GM = 1>
+//
+// MX = true: e4m3 operands with E8M0 block exponents (OCP microscaling), on
+// the 32x32x64 scaled f8f6f4 MFMA, which applies both operands' exponents in
+// hardware.  A k-tile then holds 2 BK fp8 elements in the same 2 BK-byte rows,
+// and one more 1 KB chunk per k-tile and operand carries the exponents of
+// its rows (4 bytes per row: the tile's four 32-element blocks), loaded by
+// 16 lanes of every wave.
+template <int WM, int WN, int WTM, int WFN, int BK, int ST, int WPE, int EPI, int GM = 1, bool MX = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN),
                           amdgpu_waves_per_eu(WPE, WPE)))
 void k_gemm_bf16(GemmArgs g) {
   constexpr int NWV = WM * WN;
   constexpr int BM = WM * WTM * 32, BN = WN * WFN * 32;
+  constexpr int ESZ = MX ? 1 : 2;                           // operand element bytes
+  constexpr int KT = MX ? 2 * BK : BK;                      // contraction elements per k-tile
   constexpr int G = BK / 8, RPC = 64 / G;                   // granules per row, rows per 1 KB chunk
   constexpr int CA = BM / RPC / NWV, CB = BN / RPC / NWV;   // chunks per wave
-  constexpr int LPT = CA + CB;                              // loads per k-tile per wave
+  constexpr int LPT = CA + CB + (MX ? 1 : 0);               // loads per k-tile per wave
   static_assert(CA >= 1 && CB >= 1 && (BM / RPC) % NWV == 0 && (BN / RPC) % NWV == 0, "tile/chunk mismatch");
   static_assert(LPT * ST < 64, "vmcnt range");
-  constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2, SBYTES = ABYTES + BBYTES;
+  static_assert(!MX || (BM == 256 && BN == 256 && NWV == 8 && BK == 64), "MX tiles: 256 x 256, 8 waves, 128-deep");
+  constexpr int ABYTES = BM * BK * 2, BBYTES = BN * BK * 2;
+  constexpr int XBYTES = MX ? (BM + BN) * 4 : 0;            // block exponents of the k-tile's rows
+  constexpr int SBYTES = ABYTES + BBYTES + XBYTES;
   using SW = Swz<BK>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[ST * SBYTES / 2];
 
@@ -117,19 +137,28 @@ void k_gemm_bf16(GemmArgs g) {
   // DMA sources: scalar bases at k = 0, per-lane byte offsets (rows past M
   // repeat the last row; never stored)
   const long long mlast = g.M - 1 - m0;
-  const char* abase = (const char*)(g.A + m0 * ldk + (long long)kz * g.K);
-  const char* bbase = (const char*)(g.Bt + (long long)n0 * ldk + (long long)kz * g.K);
+  const char* abase = (const char*)g.A + (m0 * ldk + (long long)kz * g.K) * ESZ;
+  const char* bbase = (const char*)g.Bt + ((long long)n0 * ldk + (long long)kz * g.K) * ESZ;
   unsigned aoff[CA], boff[CB];
 #pragma unroll
   for (int i = 0; i < CA; ++i) {
     const int row = (wave * CA + i) * RPC + lane / G;
     const long long r = row < mlast ? row : mlast;
-    aoff[i] = (unsigned)(r * ldk * 2) + ((lane % G) ^ SW::key(row)) * 16;
+    aoff[i] = (unsigned)(r * ldk * ESZ) + ((lane % G) ^ SW::key(row)) * 16;
   }
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
     const int row = (wave * CB + i) * RPC + lane / G;
-    boff[i] = (unsigned)((long long)row * ldk * 2) + ((lane % G) ^ SW::key(row)) * 16;
+    boff[i] = (unsigned)((long long)row * ldk * ESZ) + ((lane % G) ^ SW::key(row)) * 16;
+  }
+  // MX: waves 0-3 load the exponents of the tile's 256 A rows, waves 4-7
+  // those of its 256 B rows, 256 bytes (16 lanes) each.  The exponent rows of
+  // A are padded to mpad, so the chunk of the last token tile is in bounds.
+  const uint8_t* xbase = nullptr;
+  long long xstride = 0;
+  if constexpr (MX) {
+    xbase = wave < 4 ? g.sa + (m0 + 64 * wave) * 4 : g.sb + ((long long)n0 + 64 * (wave - 4)) * 4;
+    xstride = (wave < 4 ? g.mpad : (long long)g.N) * 4;  // bytes per 128-deep exponent group
   }
   const unsigned lds0 = lds_addr(lds);
   auto issue = [&](int kt, int stage) {
@@ -140,12 +169,55 @@ void k_gemm_bf16(GemmArgs g) {
     for (int i = 0; i < CA; ++i) dma16(ab, aoff[i], la + (wave * CA + i) * 1024);
 #pragma unroll
     for (int i = 0; i < CB; ++i) dma16(bb, boff[i], lb + (wave * CB + i) * 1024);
+    if constexpr (MX) {
+      if (lane < 16) dma16(xbase + (long long)(kz * (g.K / KT) + kt) * xstride, lane * 16, lb + BBYTES + wave * 256);
+    }
   };
   // one k-tile: all operand reads first, then the MFMAs
   auto mma = [&](auto stc) {
     constexpr int STG = decltype(stc)::value;
     const uint16_t* at = lds + STG * SBYTES / 2;
     const uint16_t* bt_ = at + ABYTES / 2;
+    if constexpr (MX) {
+      // k-step ks (64 fp8): lane half h feeds bytes [64 ks + 16 h, +16) and
+      // [64 ks + 32 + 16 h, +16) of its row (the MFMA's k order), and the
+      // exponent of block 2 ks + h (the scale register of lane half h covers
+      // the step's block h)
+      const uint32_t* xa = (const uint32_t*)(bt_ + BBYTES / 2);
+      const uint32_t* xb = xa + BM;
+      i32x8 fa[2][WTM], fb[2][WFN];
+      uint32_t ea[WTM], eb[WFN];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int i = 0; i < WTM; ++i) {
+          const int row = wm * WTM * 32 + i * 32 + l32;
+          const uint4 u0 = *(const uint4*)&at[SW::off(row, 32 * ks + 8 * half)];
+          const uint4 u1 = *(const uint4*)&at[SW::off(row, 32 * ks + 16 + 8 * half)];
+          fa[ks][i] = i32x8{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+        }
+#pragma unroll
+        for (int f = 0; f < WFN; ++f) {
+          const int row = wn * WFN * 32 + f * 32 + l32;
+          const uint4 u0 = *(const uint4*)&bt_[SW::off(row, 32 * ks + 8 * half)];
+          const uint4 u1 = *(const uint4*)&bt_[SW::off(row, 32 * ks + 16 + 8 * half)];
+          fb[ks][f] = i32x8{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) ea[i] = xa[wm * WTM * 32 + i * 32 + l32] >> (8 * half);
+#pragma unroll
+      for (int f = 0; f < WFN; ++f) eb[f] = xb[wn * WFN * 32 + f * 32 + l32] >> (8 * half);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int f = 0; f < WFN; ++f)
+#pragma unroll
+          for (int i = 0; i < WTM; ++i)
+            acc[f][i] = mfma32_f8_mx(fb[ks][f], fa[ks][i], acc[f][i], (int)(eb[f] >> (16 * ks)),
+                                     (int)(ea[i] >> (16 * ks)));
+      return;
+    }
     uint4 ta[BK / 16][WTM], tb[BK / 16][WFN];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
@@ -170,7 +242,7 @@ void k_gemm_bf16(GemmArgs g) {
         }
   };
 
-  const int nk = g.K / BK;
+  const int nk = g.K / KT;
   // k-tile kt in stage STG: issue k-tile kt + ST - 1 into the stage read at
   // kt - 1 (free after the previous barrier), multiply, wait for kt + 1.
   auto step = [&](int kt, auto stc) {
@@ -365,19 +437,40 @@ void k_gemm_bf16(GemmArgs g) {
           }
       }
 #pragma unroll
-      for (int f = 0; f < WFN; ++f)
+      for (int f = 0; f < WFN; ++f) {
+        float4 av[4];
+        float amax = 0.f;
 #pragma unroll
         for (int jg = 0; jg < 4; ++jg) {
           const int n = nw + 32 * f + 8 * jg;
           const float g0 = sigmoid_f(acc[f][i][4 * jg]), g1 = sigmoid_f(acc[f][i][4 * jg + 1]);
           const float g2 = sigmoid_f(acc[f][i][4 * jg + 2]), g3 = sigmoid_f(acc[f][i][4 * jg + 3]);
-          uint2 st;
-          st.x = pack_f16x2(g0 * val[f][jg].x, g1 * val[f][jg].y);
-          st.y = pack_f16x2(g2 * val[f][jg].z, g3 * val[f][jg].w);
-          *(uint2*)(g.ap + m * (2LL * g.hid) + n) = st;
+          av[jg] = make_float4(g0 * val[f][jg].x, g1 * val[f][jg].y, g2 * val[f][jg].z, g3 * val[f][jg].w);
+          if constexpr (MX) {
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(av[jg].x), fabsf(av[jg].y)), fmaxf(fabsf(av[jg].z), fabsf(av[jg].w))));
+          } else {
+            uint2 st;
+            st.x = pack_f16x2(av[jg].x, av[jg].y);
+            st.y = pack_f16x2(av[jg].z, av[jg].w);
+            *(uint2*)(g.ap + m * (2LL * g.hid) + n) = st;
+          }
           if (g.gates_dbg) *(float4*)(g.gates_dbg + m * (2LL * g.hid) + n) = make_float4(g0, g1, g2, g3);
           if (g.gates16) store_f16x4(g.gates16 + m * (2LL * g.hid) + n, g0, g1, g2, g3);
         }
+        if constexpr (MX) {
+          // A' as MX e4m3: the 32 features of block f of this token sit in
+          // lanes l and l ^ 32 (4 groups of 4 each)
+          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          const int se = mx_exponent(amax);
+          const float inv = mx_inverse_scale(se);
+          const int nb = nw - 4 * half + 32 * f;  // first feature of the block
+          uint8_t* cp = g.ap8 + m * (2LL * g.hid) + nw + 32 * f;
+#pragma unroll
+          for (int jg = 0; jg < 4; ++jg)
+            *(uint32_t*)(cp + 8 * jg) = e4m3x4(av[jg].x * inv, av[jg].y * inv, av[jg].z * inv, av[jg].w * inv);
+          if (half == 0) g.aps[((long long)(nb >> 7) * g.mpad + m) * 4 + ((nb >> 5) & 3)] = (uint8_t)(se + 127);
+        }
+      }
     } else {
       uint2 xv[WFN][4];
 #pragma unroll
@@ -439,21 +532,26 @@ hipError_t launch_weights_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) 
   return hipGetLastError();
 }
 
-template <int WM, int WN, int WTM, int WFN, int BK, int ST, int WPE, int EPI, int GM = 1>
+template <int WM, int WN, int WTM, int WFN, int BK, int ST, int WPE, int EPI, int GM = 1, bool MX = false>
 static hipError_t launch_gemm(GemmArgs g, hipStream_t s) {
   constexpr int BM = WM * WTM * 32, BN = WN * WFN * 32;
+  constexpr int KT = MX ? 2 * BK : BK, ESZ = MX ? 1 : 2;
   if (g.ldk == 0) g.ldk = g.K;
   if (g.ksplit < 1 || EPI != EPI_WGRAD) g.ksplit = 1;
-  if (g.N % BN != 0 || g.K % BK != 0 || g.K < BK ||
+  if (g.N % BN != 0 || g.K % KT != 0 || g.K < KT ||
       ((EPI == EPI_GATE || EPI == EPI_QKV || EPI == EPI_DA) && g.hid % BN != 0) ||
       (long long)g.K * g.ksplit > g.ldk)
     return hipErrorInvalidValue;
+  // MX: exponent rows of A padded to whole token tiles; no split contraction
+  if (MX && (g.ksplit != 1 || g.ldk != g.K || !g.sa || !g.sb || g.mpad < (g.M + BM - 1) / BM * BM ||
+             (EPI == EPI_GATE && (!g.ap8 || !g.aps))))
+    return hipErrorInvalidValue;
   // 32-bit per-lane DMA offsets: a tile's rows span < 4 GiB
-  if ((long long)BM * g.ldk * 2 >= (1LL << 32) || (long long)BN * g.ldk * 2 >= (1LL << 32))
+  if ((long long)BM * g.ldk * ESZ >= (1LL << 32) || (long long)BN * g.ldk * ESZ >= (1LL << 32))
     return hipErrorInvalidValue;
   const long long grid = ((g.M + BM - 1) / BM) * (g.N / BN) * g.ksplit;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gemm_bf16<WM, WN, WTM, WFN, BK, ST, WPE, EPI, GM>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((k_gemm_bf16<WM, WN, WTM, WFN, BK, ST, WPE, EPI, GM, MX>), dim3((unsigned)grid),
                      dim3(64 * WM * WN), 0, s, g);
   return hipGetLastError();
 }
@@ -538,6 +636,72 @@ hipError_t launch_out_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s)
   if (g.N % 256 == 0) return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_OUT, 2>(g, s);
   if (g.N % 128 == 0) return launch_gemm<2, 2, 4, 2, 32, 3, 2, EPI_OUT>(g, s);
   return launch_gemm<2, 2, 4, 1, 32, 3, 2, EPI_OUT>(g, s);
+}
+
+// ---- MX (e4m3 + E8M0 block exponents) variants --------------------------------
+// Operands come from the quantisers in mx_quant.hip; hid % 256 == 0.
+
+hipError_t launch_gate_gemm_mx(const Dims& d, const Bf16Args& a, hipStream_t s) {
+  GemmArgs g = base_args(d, a);
+  g.A = (const uint16_t*)a.x8;
+  g.sa = a.xs;
+  g.Bt = a.wg_t;
+  g.sb = a.wgs8;
+  g.mpad = a.mpad;
+  g.N = 2 * d.hid;
+  g.K = d.hid;
+  g.os = a.os;
+  g.ol = a.ol;
+  g.rinv = a.rinv;
+  g.rmsw = a.rmsw;
+  g.ap8 = (uint8_t*)a.ap;
+  g.aps = a.aps;
+  g.gates_dbg = a.gates_dbg;
+  g.gates16 = a.gates16;
+  return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_GATE, 4, true>(g, s);
+}
+
+hipError_t launch_out_gemm_mx(const Dims& d, const Bf16Args& a, hipStream_t s) {
+  GemmArgs g = base_args(d, a);
+  g.A = a.ap;
+  g.sa = a.aps;
+  g.Bt = a.wo_t;
+  g.sb = a.wos8;
+  g.mpad = a.mpad;
+  g.N = d.hid;
+  g.K = 2 * d.hid;
+  g.x = a.x;
+  g.y = a.y;
+  g.delta_dbg = a.delta_dbg;
+  return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_OUT, 2, true>(g, s);
+}
+
+hipError_t launch_qkv_gemm_mx(const Dims& d, const uint8_t* x8, const uint8_t* xs, long long mpad,
+                              const uint8_t* wt8, const uint8_t* wts, bf16_t* q, bf16_t* k, bf16_t* v,
+                              uint32_t* absmax, hipStream_t s) {
+  if (absmax) {
+    hipError_t e = launch_zero_u32(absmax, 3 * d.B * d.H, s);
+    if (e != hipSuccess) return e;
+  }
+  GemmArgs g = {};
+  g.M = (long long)d.B * d.N;
+  g.hid = d.hid;
+  g.H = d.H;
+  g.B = d.B;
+  g.n_video = d.N;
+  g.D = d.D;
+  g.A = (const uint16_t*)x8;
+  g.sa = xs;
+  g.Bt = (const uint16_t*)wt8;
+  g.sb = wts;
+  g.mpad = mpad;
+  g.N = 3 * d.hid;
+  g.K = d.hid;
+  g.qo = q;
+  g.ko = k;
+  g.vo = v;
+  g.absmax = absmax;
+  return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_QKV, 4, true>(g, s);
 }
 
 // ---- backward pass ---------------------------------------------------------

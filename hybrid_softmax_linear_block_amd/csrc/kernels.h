@@ -41,6 +41,14 @@ struct Bf16Args {
   float* scales;          // [5][B][H] dequantisation scales
   uint32_t* absmax;       // [5][B][H] absmax bit patterns
   bool qkv_absmax_ready;  // absmax[0 .. 3*B*H) already holds q, k, v (from the projection)
+  // MX fp8 GEMMs (gate and output): e4m3 codes with E8M0 exponents per 32
+  // contraction elements; wg_t / wo_t / ap then hold codes, and
+  bool mx;
+  bool mx_x_ready;        // x8 / xs already written (by the projection)
+  uint8_t *x8, *xs;       // x codes [B*N][hid], exponents [hid/128][mpad][4]
+  uint8_t* aps;           // A' exponents [2 hid/128][mpad][4]
+  uint8_t *wgs8, *wos8;   // weight exponents [hid/128][2 hid][4], [2 hid/128][hid][4]
+  long long mpad;         // B*N rounded up to 256
   bf16_t* y;
   float *gates_dbg, *delta_dbg;
   hipEvent_t* ev;         // NULL or 2 events per stage (timing hook)
@@ -57,6 +65,17 @@ hipError_t launch_qkv_weights(const bf16_t* wq, const bf16_t* wk, const bf16_t* 
                               hipStream_t s);
 hipError_t launch_qkv_gemm(const Dims& d, const bf16_t* x, const bf16_t* wt, bf16_t* q, bf16_t* k, bf16_t* v,
                            uint32_t* absmax, hipStream_t s);
+// MX fp8 operands (mx_quant.hip): x [M][K] bf16 -> e4m3 codes [M][K] and
+// E8M0 exponents [K/128][mpad][4]; weights (mode 0 gate, 1 out, 2 q/k/v) ->
+// codes [N][K] and exponents [K/128][N][4].  The projection GEMM on them
+// (gemm_epilogue.hip), with the outputs and absmax of launch_qkv_gemm.
+hipError_t launch_mx_rows(const bf16_t* x, long long M, int K, long long mpad, uint8_t* codes, uint8_t* ex,
+                          hipStream_t s);
+hipError_t launch_mx_weights(int mode, const bf16_t* w0, const bf16_t* w1, const bf16_t* w2, int hid,
+                             uint8_t* codes, uint8_t* ex, hipStream_t s);
+hipError_t launch_qkv_gemm_mx(const Dims& d, const uint8_t* x8, const uint8_t* xs, long long mpad,
+                              const uint8_t* wt8, const uint8_t* wts, bf16_t* q, bf16_t* k, bf16_t* v,
+                              uint32_t* absmax, hipStream_t s);
 // fp16 bits -> float32 (debug copies of the fp16 branch outputs)
 hipError_t launch_f16_to_f32(const uint16_t* src, float* dst, long long n, hipStream_t s);
 

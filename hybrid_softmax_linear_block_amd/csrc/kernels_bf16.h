@@ -15,6 +15,10 @@ hipError_t launch_weights_bf16(const Dims& d, const Bf16Args& a, hipStream_t s);
 hipError_t launch_gate_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s);
 hipError_t launch_out_gemm_bf16(const Dims& d, const Bf16Args& a, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
+// MX fp8 GEMMs (gemm_epilogue.hip) and their quantisers (mx_quant.hip)
+hipError_t launch_gate_gemm_mx(const Dims& d, const Bf16Args& a, hipStream_t s);
+hipError_t launch_out_gemm_mx(const Dims& d, const Bf16Args& a, hipStream_t s);
+
 // backward pass
 hipError_t launch_da_gemm(const Dims& d, const bf16_t* dy, const bf16_t* wo_cat, const uint16_t* gsv,
                           const uint16_t* os, const uint16_t* ol, const float* rinv, const bf16_t* rmsw,

@@ -61,7 +61,18 @@ typedef enum {
   HYB_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
 } hyb_status;
 
-typedef enum { HYB_F32 = 0, HYB_BF16 = 1, HYB_FP8_E4M3 = 2 } hyb_dtype;
+/* HYB_FP8_MX (as `soft`, with bf16 activations) is the whole fp8 version:
+ * the softmax branch as with HYB_FP8_E4M3, and the gate GEMM, the output
+ * GEMM and (hyb_block_forward) the Q/K/V projection on OCP microscaling
+ * e4m3 operands -- one power-of-two (E8M0) scale per 32 consecutive
+ * contraction elements, the smallest that keeps the block's largest
+ * magnitude within 448 (no saturation), elements rounded to nearest even,
+ * products accumulated in fp32.  Activations (x, A') are blocked along the
+ * feature axis of each token, weights along the input axis of each output
+ * column; A' is quantised in the gate GEMM's epilogue.  The article's
+ * performance section names an "FP8 version" without saying which products
+ * it quantises; this is the library's reading.  Needs hid % 256 == 0. */
+typedef enum { HYB_F32 = 0, HYB_BF16 = 1, HYB_FP8_E4M3 = 2, HYB_FP8_MX = 3 } hyb_dtype;
 
 /* Shape and window of one call.
  *   video tokens N = frames * tokens_per_frame, token index = f * n + p
@@ -106,7 +117,8 @@ enum {
  *   delta_f32 [B, N, hid]    y - x before rounding to the activation dtype
  *   gates     [B, N, 2*hid]  [g_s | g_l]
  *   scales    [5, B, H]      fp8 dequantisation scales of q, k, v, text_k,
- *                            text_v (only written when soft == HYB_FP8_E4M3)
+ *                            text_v (only written when soft is HYB_FP8_E4M3
+ *                            or HYB_FP8_MX)
  *   stage_events  NULL or an array of 2*HYB_STAGE_COUNT hipEvent_t created by
  *                 the caller; events 2s and 2s+1 are recorded on `stream`
  *                 right before and after stage s (for timing; a stage that
@@ -130,8 +142,8 @@ hyb_status hyb_layout_tables(const hyb_layout* layout, int32_t* soft_frames, int
                              int32_t* fwd, int32_t* bwd);
 
 /* Bytes of device workspace hyb_attn_forward() needs for this layout and
- * dtype combination (act: HYB_F32 or HYB_BF16; soft: act or HYB_FP8_E4M3
- * with act == HYB_BF16). */
+ * dtype combination (act: HYB_F32 or HYB_BF16; soft: act, or HYB_FP8_E4M3 or
+ * HYB_FP8_MX with act == HYB_BF16). */
 hyb_status hyb_workspace_size(const hyb_layout* layout, hyb_dtype act, hyb_dtype soft, size_t* bytes);
 
 /* The hybrid attention layer, y = x + delta.
@@ -187,7 +199,9 @@ hyb_status hyb_qkv_project(const hyb_layout* layout, const void* x, const void* 
 /*
  * The layer with its input projection: q, k, v = hyb_qkv_project(x) into the
  * workspace, then hyb_attn_forward() on them (activations bf16; soft is
- * HYB_BF16 or HYB_FP8_E4M3).  With fp8 the projection's absmax is the one
+ * HYB_BF16, HYB_FP8_E4M3 or HYB_FP8_MX; with HYB_FP8_MX the projection runs
+ * on MX e4m3 operands too, sharing x's codes with the gate GEMM).  With fp8
+ * the projection's absmax is the one
  * the softmax branch's quantisation uses, so the layer scans only the text
  * tensors for theirs.  Arguments as in hyb_attn_forward(); the workspace
  * (hyb_block_workspace_size(), 256-byte aligned) also holds q, k, v; dbg's

@@ -42,6 +42,12 @@ Parity status per function (what pins it, in ``tests/test_oracle_*.py``):
                                       invariance, zero / identity / one-hot
                                       feed-forward weights, composition with
                                       the layer oracle.
+  mx.mx_exponent / mx_quantise /      pinned: closed forms and brute-force
+  mx_matmul / epilogue_mx /           minimality of the block exponent,
+  hybrid_forward_mx                   torch's float8_e4m3fn rounding, exact
+                                      round trips, block extent and axis, the
+                                      format's error bound, exact products of
+                                      representable operands, W_o = 0.
   Anchor frames as queries (they attend to every frame): parity unpinned --
   the article says only that anchors interact with the other frames.
 """
@@ -51,3 +57,4 @@ from .hybrid import (phi, softmax_branch, linear_states, linear_branch,  # noqa:
 from . import projection  # noqa: F401
 from . import backward  # noqa: F401
 from . import dit  # noqa: F401
+from . import mx  # noqa: F401

@@ -43,7 +43,7 @@ def run_gpu(w, inp, debug=True, dev=None, **kw):
                "scales": torch.empty(5, B, H, **f32)}
     y = api.forward(api_layout(w), dev["x"], dev["q"], dev["k"], dev["v"], dev["text_k"], dev["text_v"],
                     dev["w_gs"], dev["w_gl"], dev["w_os"], dev["w_ol"], dev["rms_w"],
-                    soft="fp8" if w.soft == "fp8" else None, debug=dbg, **kw)
+                    soft=w.soft if w.soft in ("fp8", "fp8_mx") else None, debug=dbg, **kw)
     torch.cuda.synchronize()
     out = {"y": y.float().cpu().numpy().astype(np.float64)}
     if dbg:

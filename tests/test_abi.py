@@ -314,3 +314,21 @@ def test_block_backward_validation_errors():
     r, msg = call(wsb=1000)
     assert r == api.HYB_ERR_WORKSPACE_TOO_SMALL
     assert api.block_backward_workspace_size(lay) > api.backward_workspace_size(lay)
+
+
+def test_fp8_mx_mode_validation():
+    """HYB_FP8_MX needs bf16 activations and a hidden size that is a multiple
+    of 256; its workspace adds the e4m3 GEMM operands to the fp8 one."""
+    from hybrid_softmax_linear_block_amd import api
+    bad = api.Layout(1, 2, 64, 0, 3, 64)      # hid 192
+    with pytest.raises(api.HybError) as e:
+        api.workspace_size(bad, "bf16", "fp8_mx")
+    assert "256" in str(e.value)
+    with pytest.raises(api.HybError):
+        api.workspace_size(api.Layout(1, 2, 64, 0, 4, 64), "f32", "fp8_mx")
+    ok = api.Layout(2, 3, 100, 16, 4, 64)     # hid 256, 600 tokens -> 768 exponent rows
+    w8 = api.workspace_size(ok, "bf16", "fp8")
+    wmx = api.workspace_size(ok, "bf16", "fp8_mx")
+    M, hid, mpad = 600, 256, 768
+    assert wmx - w8 >= M * hid + (hid // 32) * mpad * 3 + (hid // 32) * 2 * hid * 2
+    assert api.block_workspace_size(ok, "fp8_mx") > api.block_workspace_size(ok, "fp8")

@@ -1,0 +1,137 @@
+"""GPU parity of the fp8 version with MX e4m3 GEMMs (soft = "fp8_mx")
+through the C ABI, against oracle/mx.py.
+
+The gate GEMM is checked against its exact MX definition (both sides take
+the same e4m3 codes and block exponents of x and W_g; only the kernel's fp32
+accumulation differs).  The output GEMM is checked from the kernel's own
+branch outputs and gates: the oracle forms A' from them in float64 and
+quantises it.  The kernel quantises its fp32 A', whose RMS factor comes from
+its own sum of squares, so an element whose value lies within ~1e-5 of an
+e4m3 rounding boundary can take the neighbouring code (one step, 2^-4
+relative, of one of 2 hid terms); a wrong exponent or block (factor-2 or
+larger errors) fails the bounds by far.
+The layer output is checked against the unquantised oracle with the fp8
+bound.  (Bounds and their derivation at GATE_ATOL and MX_DELTA_TOL.)  The projection of the block call is checked through the linear
+branch, which reads q, k, v exactly as the projection stored them."""
+import numpy as np
+import pytest
+
+from hybrid_softmax_linear_block_amd import api
+from hybrid_softmax_linear_block_amd.inputs import WORKLOADS, Workload, make_inputs, make_projection_weights
+from oracle import mx
+from oracle import projection as oproj
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+# Gates in (0, 1) from the MFMA's fp32 sums of exact e4m3 products (hid <= 512
+# terms; measured 1.5e-5, the matrix core's own accumulation of each 64-term
+# step included).  One wrong x or W code alone moves a gate by ~3e-4, a wrong
+# block exponent by far more (0.46 measured with a mis-mapped operand).
+GATE_ATOL = 5e-5
+# Output GEMM from the kernel's own A' inputs: mean at the bf16 bound; max at
+# the fp8 bound, since an A' element within ~1e-5 of an e4m3 rounding
+# boundary can round the other way on the two sides (one 2^-4 step of one of
+# 2 hid terms; measured max 1.0e-2, mean 2e-4; a wrong exponent gives mean 0.38).
+MX_DELTA_TOL = (4e-2, 2e-3)
+MX_CASES = [WORKLOADS[2].with_(name="mx-workload2", soft="fp8_mx"),
+            Workload("mx-ragged-b2-d128", 2, 5, 100, 37, 2, 128, soft="fp8_mx", seed=61),
+            Workload("mx-notext-d64", 1, 4, 130, 0, 4, 64, soft="fp8_mx", seed=62)]
+
+
+def _hid(a, w):
+    return np.asarray(a).reshape(w.batch, w.n_video, w.hidden)
+
+
+def _check_gemms(w, inp, g):
+    """Gate GEMM against its MX definition; output GEMM from the kernel's own
+    branch outputs and gates."""
+    x = np.asarray(inp["x"], np.float64)
+    wg = np.concatenate([inp["w_gs"], inp["w_gl"]], axis=1)
+    gates_ref = 1.0 / (1.0 + np.exp(-mx.mx_matmul(x, wg)))
+    gerr = np.abs(g["gates"] - gates_ref).max()
+    hid = w.hidden
+    gs, gl = g["gates"][..., :hid], g["gates"][..., hid:]
+    ol = _hid(g["o_lin"], w)
+    r = ol * np.asarray(inp["rms_w"], np.float64) / np.sqrt(np.mean(ol * ol, axis=-1, keepdims=True) + 1e-6)
+    a_p = np.concatenate([gs * _hid(g["o_soft"], w), gl * r], axis=-1)
+    delta_ref = mx.mx_matmul(a_p, np.concatenate([inp["w_os"], inp["w_ol"]], axis=0))
+    derr = gu.errors(g["delta_f32"], delta_ref)
+    return gerr, derr
+
+
+@pytest.mark.parametrize("w", MX_CASES, ids=[w.name for w in MX_CASES])
+def test_mx_layer(w):
+    inp = make_inputs(w)
+    print("case", w.name, flush=True)
+    g = gu.run_gpu(w, inp)
+    gerr, derr = _check_gemms(w, inp, g)
+    ref = gu.run_oracle(w, inp)
+    rep_y, bad_y = gu.compare(w, g, ref, keys=("y",), tol=gu.TOL["fp8"])
+    rep_l, bad_l = gu.compare(w, g, ref, keys=("o_l",), tol=gu.TOL["bf16"])
+    print(w.name, "gates |err| %.2e" % gerr, "delta vs MX(A') W_o max %.2e mean %.2e" % derr, rep_y, rep_l,
+          flush=True)
+    assert gerr <= GATE_ATOL, gerr
+    assert derr[0] <= MX_DELTA_TOL[0] and derr[1] <= MX_DELTA_TOL[1], derr
+    assert not bad_y, bad_y
+    assert not bad_l, bad_l
+
+
+@pytest.mark.parametrize("w", MX_CASES[:2], ids=[w.name for w in MX_CASES[:2]])
+def test_mx_block(w):
+    """hyb_block_forward with MX: the projection's stored q, k, v (seen
+    through the linear branch, against the oracle's MX projection rounded to
+    bf16), the gates from the x codes the projection wrote, and the output
+    GEMM as above."""
+    import torch
+    inp = make_inputs(w)
+    wts = make_projection_weights(w)
+    print("case", w.name, flush=True)
+    dev = {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda").to(torch.bfloat16) for k, v in inp.items()}
+    wd = {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda").to(torch.bfloat16) for k, v in wts.items()}
+    f32 = dict(dtype=torch.float32, device="cuda")
+    B, N, H, D, hid = w.batch, w.n_video, w.heads, w.head_dim, w.hidden
+    dbg = {"o_soft": torch.empty(B, N, H, D, **f32), "o_lin": torch.empty(B, N, H, D, **f32),
+           "delta_f32": torch.empty(B, N, hid, **f32), "gates": torch.empty(B, N, 2 * hid, **f32)}
+    y = api.block_forward(gu.api_layout(w), dev["x"], wd["w_q"], wd["w_k"], wd["w_v"], dev["text_k"],
+                          dev["text_v"], dev["w_gs"], dev["w_gl"], dev["w_os"], dev["w_ol"], dev["rms_w"],
+                          soft="fp8_mx", debug=dbg)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy().astype(np.float64) for k, v in dbg.items()}
+    g["y"] = y.float().cpu().numpy().astype(np.float64)
+    q, k, v = mx.qkv_projection_mx(inp["x"], wts["w_q"], wts["w_k"], wts["w_v"], w.heads)
+    ref_inp = dict(inp, q=oproj.round_bf16(q), k=oproj.round_bf16(k), v=oproj.round_bf16(v))
+    ref = gu.run_oracle(w, ref_inp)
+    gerr, derr = _check_gemms(w, inp, g)
+    rep_l, bad_l = gu.compare(w, g, ref, keys=("o_l",), tol=gu.TOL["bf16"])
+    rep_y, bad_y = gu.compare(w, g, ref, keys=("y",), tol=gu.TOL["fp8"])
+    print(w.name, "gates |err| %.2e" % gerr, "delta max %.2e mean %.2e" % derr, rep_l, rep_y, flush=True)
+    assert gerr <= GATE_ATOL, gerr
+    assert derr[0] <= MX_DELTA_TOL[0] and derr[1] <= MX_DELTA_TOL[1], derr
+    assert not bad_l, bad_l
+    assert not bad_y, bad_y
+
+
+def test_mx_768p_sampled():
+    """768p shape in the bench's launch configuration: both MX GEMMs on a
+    sample of tokens (MX blocks lie within a token row, so a row of the
+    reference needs only that token)."""
+    import torch
+    w = WORKLOADS[3].with_(soft="fp8_mx")
+    inp = make_inputs(w)
+    print("case", w.name, "fp8_mx", flush=True)
+    g = gu.run_gpu(w, inp)
+    rng = np.random.default_rng(7)
+    tok = np.sort(rng.choice(w.n_video, 256, replace=False))
+    sub = dict(inp, x=np.asarray(inp["x"])[:, tok])
+    gs = {"gates": g["gates"][:, tok], "o_soft": g["o_soft"][:, tok], "o_lin": g["o_lin"][:, tok],
+          "delta_f32": g["delta_f32"][:, tok]}
+    ws = w.with_(frames=1, tokens_per_frame=tok.size)
+    gerr, derr = _check_gemms(ws, sub, gs)
+    print("768p mx gates |err| %.2e" % gerr, "delta max %.2e mean %.2e" % derr, flush=True)
+    # 3072-term fp32 sums
+    assert gerr <= 3 * GATE_ATOL, gerr
+    assert derr[0] <= MX_DELTA_TOL[0] and derr[1] <= MX_DELTA_TOL[1], derr
+    del g
+    torch.cuda.empty_cache()
+
