@@ -96,8 +96,10 @@ def stage_work(w, soft, block=False, ffn_hidden=0):
         work["quant"] = ("hbm", (3 * B * N + 2 * B * L) * hid * (es + 1))
     if soft == "fp8_mx":
         # gate and output weights read in bf16, written as codes + exponents;
-        # x read in bf16, written as codes + exponents (unless the projection did)
-        work["weights"] = ("hbm", 2 * (2 * hid * hid) * (2 + 1 + 1.0 / 32) + B * N * hid * (2 + 1 + 1.0 / 32))
+        # x read in bf16, written as codes + exponents (in the projection's
+        # stage when there is one)
+        work["weights"] = ("hbm", 2 * (2 * hid * hid) * (2 + 1 + 1.0 / 32)
+                           + (0 if block else B * N * hid * (2 + 1 + 1.0 / 32)))
     if block:
         # x [B*N][hid] @ [hid][3 hid]: 2 * B*N * hid * 3 hid
         work["qkv"] = ("mfma", 2.0 * B * N * hid * 3 * hid)
@@ -524,8 +526,11 @@ def main():
     value = w.batch * w.n_video / (ms * 1e-3) / 1e6
     sw = stage_work(w, soft, True, ffn_hidden)
     layer_flop = wc["layer_flop"] + (sw["qkv"][1] if args.block else 0.0) + (sw["ffn"][1] if args.dit else 0.0)
+    metric = METRIC_DIT if args.dit else (METRIC_BLOCK if args.block else METRIC)
+    if soft == "fp8_mx":
+        metric = metric.replace("bf16)", "fp8 version: e4m3 softmax branch, MX e4m3 GEMMs)")
     out = {
-        "metric": METRIC_DIT if args.dit else (METRIC_BLOCK if args.block else METRIC), "value": round(value, 4), "unit": "Mtokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": metric, "value": round(value, 4), "unit": "Mtokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 + e4m3 (MX GEMMs, fp8 softmax)" if soft == "fp8_mx" else w.act,
         "data": "synthetic",
