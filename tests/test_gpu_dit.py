@@ -31,7 +31,7 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(torch.bfloat16)
 
 
-def _run(w, inp, pw, fw, block_only=False):
+def _run(w, inp, pw, fw, block_only=False, soft=None):
     import torch
     d = {k: _dev(v) for k, v in inp.items()}
     p = {k: _dev(v) for k, v in pw.items()}
@@ -39,11 +39,11 @@ def _run(w, inp, pw, fw, block_only=False):
     lay = gu.api_layout(w)
     if block_only:
         out = api.block_forward(lay, d["x"], p["w_q"], p["w_k"], p["w_v"], d["text_k"], d["text_v"], d["w_gs"],
-                                d["w_gl"], d["w_os"], d["w_ol"], d["rms_w"])
+                                d["w_gl"], d["w_os"], d["w_ol"], d["rms_w"], soft=soft)
     else:
         out = api.dit_block_forward(lay, d["x"], p["w_q"], p["w_k"], p["w_v"], d["text_k"], d["text_v"],
                                     d["w_gs"], d["w_gl"], d["w_os"], d["w_ol"], d["rms_w"], f["w_n"], f["w_1"],
-                                    f["w_2"])
+                                    f["w_2"], soft=soft)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64)
 
@@ -73,6 +73,23 @@ def test_dit_block_zero_ffn_is_block_bit_exact():
     fw = make_ffn_weights(w)
     fw["w_2"] = np.zeros_like(fw["w_2"])
     assert np.array_equal(_run(w, inp, pw, fw), _run(w, inp, pw, fw, block_only=True))
+
+
+def test_dit_block_fp8_mx():
+    """The DiT block in the fp8 version (MX projection, layer and GEMMs; the
+    feed-forward in bf16): W_2 = 0 gives the block output bit for bit, and
+    the feed-forward matches the oracle from the library's own layer output."""
+    w = CASES[2]  # hid 256
+    inp = make_inputs(w)
+    pw = make_projection_weights(w)
+    fw = make_ffn_weights(w)
+    y = _run(w, inp, pw, fw, block_only=True, soft="fp8_mx")
+    z = _run(w, inp, pw, fw, soft="fp8_mx")
+    e = gu.errors(z, odit.ffn(y, fw["w_n"], fw["w_1"], fw["w_2"]))
+    print(w.name, "fp8_mx z from gpu y max %.2e mean %.2e" % e, flush=True)
+    assert e[0] <= TOL_BLOCK[0] and e[1] <= TOL_BLOCK[1], e
+    fz = dict(fw, w_2=np.zeros_like(fw["w_2"]))
+    assert np.array_equal(_run(w, inp, pw, fz, soft="fp8_mx"), y)
 
 
 def test_dit_block_768p_ffn_sampled():
