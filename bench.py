@@ -130,7 +130,7 @@ def stage_roofline(w, soft, stage_ms, block=False, ffn_hidden=0):
         if t <= 0:
             continue
         if bound == "mfma":
-            fp8 = soft and (k == "softmax" or (soft == "fp8_mx" and k in ("gate", "out", "qkv")))
+            fp8 = soft and (k == "softmax" or (soft == "fp8_mx" and k in ("gate", "out", "qkv", "ffn")))
             peak = PEAK["fp8" if fp8 else w.act]
             ach = amount / (t * 1e-3) / 1e12
             out[k] = {"bound": "mfma", "algorithmic": amount, "unit": "TFLOP/s", "achieved": round(ach, 2),

@@ -955,6 +955,7 @@ namespace {
 struct DitPlan {
   BlockPlan block;
   size_t y, h, u, w1t, w2t, total;
+  size_t h8, hs, us, w1s, w2s;  // MX operands of the feed-forward (HYB_FP8_MX)
 };
 
 DitPlan make_dit_plan(const hyb::Dims& d, hyb_dtype soft, int F) {
@@ -967,6 +968,15 @@ DitPlan make_dit_plan(const hyb::Dims& d, hyb_dtype soft, int F) {
   p.u = o; o = align_up(o + M * (size_t)F * 2, 256);
   p.w1t = o; o = align_up(o + (size_t)F * hid * 2, 256);
   p.w2t = o; o = align_up(o + (size_t)F * hid * 2, 256);
+  p.h8 = p.hs = p.us = p.w1s = p.w2s = 0;
+  if (soft == HYB_FP8_MX) {  // u, w1t, w2t hold the codes
+    const size_t mp = mx_rows(d);
+    p.h8 = o; o = align_up(o + M * hid, 256);
+    p.hs = o; o = align_up(o + hid / 32 * mp, 256);
+    p.us = o; o = align_up(o + (size_t)F / 32 * mp, 256);
+    p.w1s = o; o = align_up(o + hid / 32 * (size_t)F, 256);
+    p.w2s = o; o = align_up(o + (size_t)F / 32 * hid, 256);
+  }
   p.total = o;
   return p;
 }
@@ -977,6 +987,8 @@ hyb_status check_dit(const hyb_layout* layout, hyb_dtype soft, int32_t F) {
   st = check_dtypes(layout, HYB_BF16, soft);
   if (st != HYB_OK) return st;
   if (F <= 0 || F % 64) return fail(HYB_ERR_INVALID_ARGUMENT, "ffn_hidden must be a positive multiple of 64 (got %d)", F);
+  if (soft == HYB_FP8_MX && F % 256)
+    return fail(HYB_ERR_UNSUPPORTED, "FP8_MX needs ffn_hidden to be a multiple of 256 (got %d)", F);
   return HYB_OK;
 }
 
@@ -1039,6 +1051,13 @@ hyb_status hyb_dit_block_forward(const hyb_layout* layout, hyb_dtype soft, const
     a.w1t = (hyb::bf16_t*)(ws + p.w1t);
     a.w2t = (hyb::bf16_t*)(ws + p.w2t);
     a.z = (hyb::bf16_t*)z;
+    a.mx = soft == HYB_FP8_MX;
+    a.mpad = (long long)mx_rows(d);
+    a.h8 = (uint8_t*)(ws + p.h8);
+    a.hs = (uint8_t*)(ws + p.hs);
+    a.us = (uint8_t*)(ws + p.us);
+    a.w1s = (uint8_t*)(ws + p.w1s);
+    a.w2s = (uint8_t*)(ws + p.w2s);
     he = hyb::run_ffn_bf16(a, s);
   }
   if (he == hipSuccess && ev) he = hipEventRecord(ev[2 * HYB_STAGE_FFN + 1], s);

@@ -8,6 +8,7 @@
 // the library's reading).  Two MFMA GEMMs from the layer's GEMM kernel: the
 // first with a GELU epilogue, the second with the residual epilogue.
 #include "kernels_bf16.h"
+#include "mx_common.h"
 
 namespace hyb {
 
@@ -39,7 +40,28 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const bf16_t* __restrict__
   }
 }
 
+// The fp8 version: the normalised input (stored in bf16) and the weights as
+// MX e4m3 operands, the GELU output quantised in the first GEMM's epilogue.
+static hipError_t run_ffn_mx(const FfnArgs& a, hipStream_t s) {
+  hipError_t e = launch_mx_weights_kn(a.w1, a.hid, a.F, (uint8_t*)a.w1t, a.w1s, s);  // [hid][F] -> codes [F][hid]
+  if (e != hipSuccess) return e;
+  e = launch_mx_weights_kn(a.w2, a.F, a.hid, (uint8_t*)a.w2t, a.w2s, s);            // [F][hid] -> codes [hid][F]
+  if (e != hipSuccess) return e;
+  const long long blocks = (a.M + 3) / 4;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_rmsnorm_rows, dim3((unsigned)blocks), dim3(256), 0, s, a.y, a.wn, a.M, a.hid, a.eps, a.h);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_mx_rows(a.h, a.M, a.hid, a.mpad, a.h8, a.hs, s);
+  if (e != hipSuccess) return e;
+  e = launch_gelu_gemm_mx(a.M, a.hid, a.F, a.h8, a.hs, a.mpad, (const uint8_t*)a.w1t, a.w1s, (uint8_t*)a.u, a.us, s);
+  if (e != hipSuccess) return e;
+  return launch_resid_gemm_mx(a.M, a.hid, a.F, (const uint8_t*)a.u, a.us, a.mpad, (const uint8_t*)a.w2t, a.w2s, a.y,
+                              a.z, s);
+}
+
 hipError_t run_ffn_bf16(const FfnArgs& a, hipStream_t s) {
+  if (a.mx) return run_ffn_mx(a, s);
   // weights into the GEMMs' [N][K] operand layout
   hipError_t e = transpose_tok(a.w1, false, a.hid, a.F, a.hid, a.w1t, s);  // [hid][F] -> [F][hid]
   if (e != hipSuccess) return e;

@@ -293,14 +293,36 @@ void k_gemm_bf16(GemmArgs g) {
       const long long m = m0 + wm * WTM * 32 + i * 32 + l32;
       if (m >= g.M) continue;
 #pragma unroll
-      for (int f = 0; f < WFN; ++f)
+      for (int f = 0; f < WFN; ++f) {
+        if constexpr (MX) {
+          // GELU output as MX e4m3 (block f of the token: lanes l and l ^ 32)
+          float4 uv[4];
+          float amax = 0.f;
 #pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          const int n = n0 + wn * WFN * 32 + 32 * f + 8 * jg + 4 * half;
-          *(uint2*)(g.out + m * g.N + n) =
-              make_uint2(pack_bf16x2(gelu_tanh_f(acc[f][i][4 * jg]), gelu_tanh_f(acc[f][i][4 * jg + 1])),
-                         pack_bf16x2(gelu_tanh_f(acc[f][i][4 * jg + 2]), gelu_tanh_f(acc[f][i][4 * jg + 3])));
+          for (int jg = 0; jg < 4; ++jg) {
+            uv[jg] = make_float4(gelu_tanh_f(acc[f][i][4 * jg]), gelu_tanh_f(acc[f][i][4 * jg + 1]),
+                                 gelu_tanh_f(acc[f][i][4 * jg + 2]), gelu_tanh_f(acc[f][i][4 * jg + 3]));
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(uv[jg].x), fabsf(uv[jg].y)), fmaxf(fabsf(uv[jg].z), fabsf(uv[jg].w))));
+          }
+          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          const int se = mx_exponent(amax);
+          const float inv = mx_inverse_scale(se);
+          const int nb = n0 + wn * WFN * 32 + 32 * f;  // first feature of the block
+          uint8_t* cp = g.ap8 + m * g.N + nb + 4 * half;
+#pragma unroll
+          for (int jg = 0; jg < 4; ++jg)
+            *(uint32_t*)(cp + 8 * jg) = e4m3x4(uv[jg].x * inv, uv[jg].y * inv, uv[jg].z * inv, uv[jg].w * inv);
+          if (half == 0) g.aps[((long long)(nb >> 7) * g.mpad + m) * 4 + ((nb >> 5) & 3)] = (uint8_t)(se + 127);
+        } else {
+#pragma unroll
+          for (int jg = 0; jg < 4; ++jg) {
+            const int n = n0 + wn * WFN * 32 + 32 * f + 8 * jg + 4 * half;
+            *(uint2*)(g.out + m * g.N + n) =
+                make_uint2(pack_bf16x2(gelu_tanh_f(acc[f][i][4 * jg]), gelu_tanh_f(acc[f][i][4 * jg + 1])),
+                           pack_bf16x2(gelu_tanh_f(acc[f][i][4 * jg + 2]), gelu_tanh_f(acc[f][i][4 * jg + 3])));
+          }
         }
+      }
     }
     return;
   }
@@ -544,7 +566,7 @@ static hipError_t launch_gemm(GemmArgs g, hipStream_t s) {
     return hipErrorInvalidValue;
   // MX: exponent rows of A padded to whole token tiles; no split contraction
   if (MX && (g.ksplit != 1 || g.ldk != g.K || !g.sa || !g.sb || g.mpad < (g.M + BM - 1) / BM * BM ||
-             (EPI == EPI_GATE && (!g.ap8 || !g.aps))))
+             ((EPI == EPI_GATE || EPI == EPI_GELU) && (!g.ap8 || !g.aps))))
     return hipErrorInvalidValue;
   // 32-bit per-lane DMA offsets: a tile's rows span < 4 GiB
   if ((long long)BM * g.ldk * ESZ >= (1LL << 32) || (long long)BN * g.ldk * ESZ >= (1LL << 32))
@@ -702,6 +724,43 @@ hipError_t launch_qkv_gemm_mx(const Dims& d, const uint8_t* x8, const uint8_t* x
   g.vo = v;
   g.absmax = absmax;
   return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_QKV, 4, true>(g, s);
+}
+
+// Feed-forward GEMMs on MX operands: u = GELU(h W_1) written as MX codes
+// (u8 [M][F], us [F/128][mpad][4]), then out = resid + u W_2.
+hipError_t launch_gelu_gemm_mx(long long M, int hid, int F, const uint8_t* h8, const uint8_t* hs, long long mpad,
+                               const uint8_t* w1c, const uint8_t* w1s, uint8_t* u8, uint8_t* us, hipStream_t s) {
+  GemmArgs g = {};
+  g.M = M;
+  g.N = F;
+  g.K = hid;
+  g.hid = hid;
+  g.A = (const uint16_t*)h8;
+  g.sa = hs;
+  g.Bt = (const uint16_t*)w1c;
+  g.sb = w1s;
+  g.mpad = mpad;
+  g.ap8 = u8;
+  g.aps = us;
+  return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_GELU, 4, true>(g, s);
+}
+
+hipError_t launch_resid_gemm_mx(long long M, int N, int K, const uint8_t* a8, const uint8_t* as, long long mpad,
+                                const uint8_t* bc, const uint8_t* bs, const bf16_t* resid, bf16_t* out,
+                                hipStream_t s) {
+  GemmArgs g = {};
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.hid = N;
+  g.A = (const uint16_t*)a8;
+  g.sa = as;
+  g.Bt = (const uint16_t*)bc;
+  g.sb = bs;
+  g.mpad = mpad;
+  g.x = resid;
+  g.y = out;
+  return launch_gemm<4, 2, 2, 4, 64, 2, 2, EPI_RES, 2, true>(g, s);
 }
 
 // ---- backward pass ---------------------------------------------------------

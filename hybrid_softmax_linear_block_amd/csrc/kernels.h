@@ -144,6 +144,11 @@ struct FfnArgs {
   float eps;
   const bf16_t *y, *wn, *w1, *w2;
   bf16_t *h, *u, *w1t, *w2t, *z;
+  // MX fp8 GEMMs: u, w1t and w2t then hold e4m3 codes, with
+  bool mx;
+  uint8_t *h8, *hs, *us, *w1s, *w2s;  // h codes [M][hid]; exponents [hid/128][mpad][4], [F/128][mpad][4],
+                                      // [hid/128][F][4], [F/128][hid][4]
+  long long mpad;                     // M rounded up to 256
 };
 hipError_t run_ffn_bf16(const FfnArgs& a, hipStream_t s);
 

@@ -18,6 +18,12 @@ hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
 // MX fp8 GEMMs (gemm_epilogue.hip) and their quantisers (mx_quant.hip)
 hipError_t launch_gate_gemm_mx(const Dims& d, const Bf16Args& a, hipStream_t s);
 hipError_t launch_out_gemm_mx(const Dims& d, const Bf16Args& a, hipStream_t s);
+hipError_t launch_gelu_gemm_mx(long long M, int hid, int F, const uint8_t* h8, const uint8_t* hs, long long mpad,
+                               const uint8_t* w1c, const uint8_t* w1s, uint8_t* u8, uint8_t* us, hipStream_t s);
+hipError_t launch_resid_gemm_mx(long long M, int N, int K, const uint8_t* a8, const uint8_t* as, long long mpad,
+                                const uint8_t* bc, const uint8_t* bs, const bf16_t* resid, bf16_t* out,
+                                hipStream_t s);
+hipError_t launch_mx_weights_kn(const bf16_t* w, int K, int N, uint8_t* codes, uint8_t* ex, hipStream_t s);
 
 // backward pass
 hipError_t launch_da_gemm(const Dims& d, const bf16_t* dy, const bf16_t* wo_cat, const uint16_t* gsv,

@@ -108,6 +108,38 @@ __global__ __launch_bounds__(256) void k_mx_weights(const bf16_t* __restrict__ w
   ex[((long long)(kb >> 2) * N + n) * 4 + (kb & 3)] = (uint8_t)(se + 127);
 }
 
+// Any [K][N] row-major weight ([in][out]) -> codes [N][K], exponents
+// [K/128][N][4] (the feed-forward weights).
+__global__ __launch_bounds__(256) void k_mx_weights_kn(const bf16_t* __restrict__ w, int K, int N,
+                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ ex) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (long long)N * (K / 32)) return;
+  const int n = (int)(t % N), kb = (int)(t / N);
+  float v[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    v[j] = bf16_to_f32(w[(long long)(kb * 32 + j) * N + n]);
+    amax = fmaxf(amax, fabsf(v[j]));
+  }
+  const int se = mx_exponent(amax);
+  const float inv = mx_inverse_scale(se);
+  uint32_t q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = e4m3x4(v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv);
+  uint4* dst = (uint4*)(codes + (long long)n * K + kb * 32);
+  dst[0] = make_uint4(q[0], q[1], q[2], q[3]);
+  dst[1] = make_uint4(q[4], q[5], q[6], q[7]);
+  ex[((long long)(kb >> 2) * N + n) * 4 + (kb & 3)] = (uint8_t)(se + 127);
+}
+
+hipError_t launch_mx_weights_kn(const bf16_t* w, int K, int N, uint8_t* codes, uint8_t* ex, hipStream_t s) {
+  if (K % 128 != 0 || N <= 0) return hipErrorInvalidValue;
+  const long long blocks = ((long long)N * (K / 32) + 255) / 256;
+  hipLaunchKernelGGL(k_mx_weights_kn, dim3((unsigned)blocks), dim3(256), 0, s, w, K, N, codes, ex);
+  return hipGetLastError();
+}
+
 hipError_t launch_mx_rows(const bf16_t* x, long long M, int K, long long mpad, uint8_t* codes, uint8_t* ex,
                           hipStream_t s) {
   if (K % 128 != 0 || mpad < M || mpad % 256 != 0) return hipErrorInvalidValue;

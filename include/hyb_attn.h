@@ -329,7 +329,10 @@ hyb_status hyb_attn_backward(const hyb_layout* layout, const void* x, hyb_tensor
  *                                                  no biases)
  *   ffn_norm_weight [hid]; w_ff1 [hid][ffn_hidden]; w_ff2 [ffn_hidden][hid]
  *   (bf16, [in][out]); ffn_hidden a positive multiple of 64 (4 * hid in the
- *   usual block).  z [B, N, hid] bf16 may alias x.  Other arguments as in
+ *   usual block; a multiple of 256 with soft == HYB_FP8_MX, where both
+ *   feed-forward GEMMs also take MX e4m3 operands: the normalised y from its
+ *   bf16 value, the GELU output from its fp32 value).  z [B, N, hid] bf16
+ *   may alias x.  Other arguments as in
  *   hyb_block_forward(); the workspace (hyb_dit_block_workspace_size())
  *   also holds y, the normalised y, the GELU output and the transposed
  *   feed-forward weights; dbg's stage_events include HYB_STAGE_FFN.

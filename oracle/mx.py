@@ -27,7 +27,10 @@ Readings taken where the pages are silent (the library implements the same):
     (the kernel accumulates in fp32);
   * A' = [g_s * O_s | g_l * RMSNorm(O_l)] is quantised as computed (in the
     library, from its fp32 value in the gate GEMM's epilogue); the gates
-    themselves are not quantised.
+    themselves are not quantised;
+  * in the DiT block's feed-forward, the normalised input is quantised from
+    its stored bf16 value and the GELU output as computed (in the library,
+    in the first GEMM's epilogue).
 
 Pinned by tests/test_oracle_mx.py: the exponent's closed forms and its
 minimality by brute force, element rounding against torch's float8_e4m3fn
@@ -38,9 +41,10 @@ exactly-representable special cases.
 """
 import numpy as np
 
+from .dit import gelu_tanh, rmsnorm
 from .fp8 import round_e4m3, softmax_branch_fp8
 from .hybrid import _rows, linear_branch, linear_states, sigmoid
-from .projection import project
+from .projection import project, round_bf16
 
 BLOCK = 32
 E4M3_MAX = 448.0
@@ -125,3 +129,12 @@ def hybrid_forward_mx(inp, lay, scale=None, eps=1e-6, tokens=None):
                      inp["rms_w"], eps=eps)
     ep.update({"o_s": o_s, "o_l": o_l, "tokens": rows})
     return ep
+
+
+def ffn_mx(y, w_n, w_1, w_2, eps=1e-6):
+    """The feed-forward of oracle/dit.py with MX GEMMs:
+    z = y + MX(GELU(MX(bf16(RMSNorm(y))) MX(W_1))) MX(W_2)."""
+    y = np.asarray(y, np.float64)
+    h = round_bf16(rmsnorm(y, w_n, eps))
+    u = gelu_tanh(mx_matmul(h, w_1))
+    return y + mx_matmul(u, w_2)

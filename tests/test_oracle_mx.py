@@ -145,3 +145,26 @@ def test_mutations_are_caught():
             test_block_extent_and_axis()
     finally:
         mx.mx_round = orig_round
+
+
+def test_ffn_mx():
+    """W_2 = 0 gives y exactly; otherwise the MX feed-forward stays within the
+    format's bound of the exact one (oracle/dit.ffn) for representable-free
+    random data: each MX product is within (2 2^-4 + 2^-8) sum|a||w| of the
+    exact product of its inputs, and GELU is 1.13-Lipschitz."""
+    from oracle import dit
+    rng = np.random.default_rng(8)
+    y = rng.standard_normal((2, 10, 64))
+    w_n = 1 + 0.1 * rng.standard_normal(64)
+    w_1 = rng.standard_normal((64, 256)) * 0.05
+    w_2 = rng.standard_normal((256, 64)) * 0.05
+    np.testing.assert_array_equal(mx.ffn_mx(y, w_n, w_1, np.zeros_like(w_2)), y)
+    z = mx.ffn_mx(y, w_n, w_1, w_2)
+    ref = dit.ffn(y, w_n, w_1, w_2)
+    h = dit.rmsnorm(y, w_n)
+    c = 2 * 2.0 ** -4 + 2.0 ** -8
+    e1 = (np.abs(h) @ np.abs(w_1)) * c + np.abs(h - mx.round_bf16(h)) @ np.abs(w_1)  # first product
+    u = dit.gelu_tanh(h @ w_1)
+    bound = 1.13 * e1 @ np.abs(w_2) + ((np.abs(u) + 1.13 * e1) @ np.abs(w_2)) * c
+    assert np.all(np.abs(z - ref) <= bound + 1e-12)
+    assert np.abs(z - ref).max() > 0  # quantisation is visible
