@@ -332,3 +332,9 @@ def test_fp8_mx_mode_validation():
     M, hid, mpad = 600, 256, 768
     assert wmx - w8 >= M * hid + (hid // 32) * mpad * 3 + (hid // 32) * 2 * hid * 2
     assert api.block_workspace_size(ok, "fp8_mx") > api.block_workspace_size(ok, "fp8")
+    # the DiT block's MX feed-forward needs ffn_hidden % 256 == 0
+    with pytest.raises(api.HybError) as e:
+        api.dit_block_workspace_size(ok, 320, "fp8_mx")
+    assert "256" in str(e.value)
+    assert api.dit_block_workspace_size(ok, 320, "fp8") > 0
+    assert api.dit_block_workspace_size(ok, 1024, "fp8_mx") > api.dit_block_workspace_size(ok, 1024, "fp8")
