@@ -320,9 +320,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
     }
   }
 
-  floatx16 oacc_v[DB], oacc_t[DB];  // video and text parts (different V scales)
+  // One accumulator for video and text: the video keys' V scale sv is
+  // carried as sv / stv from the first text tile on, the text keys' stv at
+  // the end, so O = sv sum_video P V8 + stv sum_text P TV8 without a second
+  // 64-register accumulator.
+  floatx16 oacc[DB];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) { oacc_v[i] = zero16(); oacc_t[i] = zero16(); }
+  for (int i = 0; i < DB; ++i) oacc[i] = zero16();
   float m_run = -INFINITY, l_run = 0.f;
 
   Cursor ci, cc;  // issue cursor (NS - 1 tiles ahead), compute cursor
@@ -344,7 +348,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
   constexpr float kSlack8 = 0.75f, kLogPscale = 8.f;
 
   // One tile t of the video (TEXT = false) or text keys.
-  auto tile = [&](auto textc, int t, floatx16 (&oacc)[DB], float dq) {
+  auto tile = [&](auto textc, int t, float dq) {
     constexpr bool TEXT = decltype(textc)::value;
     const int buf = t % NS;
     const bool more = t + NS - 1 < total;
@@ -395,8 +399,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
       for (int i = 0; i < DB; ++i)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          oacc_v[i][j] *= alpha;
-          oacc_t[i][j] *= alpha;
+          oacc[i][j] *= alpha;
         }
     }
     // P * 2^8 to e4m3, packed in operand order e = 16*kb + j
@@ -433,11 +436,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
     tile_barrier();
   };
   const float dqv = sq * sk * sl2, dqt = sq * stk * sl2;  // logit scales in log2 units
-  for (int t = 0; t < nvid; ++t) tile(std::integral_constant<bool, false>{}, t, oacc_v, dqv);
-  for (int t = nvid; t < total; ++t) tile(std::integral_constant<bool, true>{}, t, oacc_t, dqt);
+  for (int t = 0; t < nvid; ++t) tile(std::integral_constant<bool, false>{}, t, dqv);
+  const bool has_text = total > nvid;
+  if (has_text) {
+    const float r = sv / stv;  // scales are > 0 (1 for an all-zero tensor)
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) oacc[i][j] *= r;
+  }
+  for (int t = nvid; t < total; ++t) tile(std::integral_constant<bool, true>{}, t, dqt);
 
   const float l_tot = xor32_sum(l_run);
-  const float cv = sv / l_tot, ct = stv / l_tot;
+  const float c = (has_text ? stv : sv) / l_tot;
   if (row_ok) {
     uint16_t* op = os + (((long long)b * d.N + qtok) * d.H + h) * D;
 #pragma unroll
@@ -445,12 +456,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
         const int d0 = i * 32 + 8 * jg + 4 * half;
-        float4 o4;
-        o4.x = oacc_v[i][4 * jg] * cv + oacc_t[i][4 * jg] * ct;
-        o4.y = oacc_v[i][4 * jg + 1] * cv + oacc_t[i][4 * jg + 1] * ct;
-        o4.z = oacc_v[i][4 * jg + 2] * cv + oacc_t[i][4 * jg + 2] * ct;
-        o4.w = oacc_v[i][4 * jg + 3] * cv + oacc_t[i][4 * jg + 3] * ct;
-        store_f16x4(op + d0, o4.x, o4.y, o4.z, o4.w);
+        store_f16x4(op + d0, oacc[i][4 * jg] * c, oacc[i][4 * jg + 1] * c, oacc[i][4 * jg + 2] * c,
+                    oacc[i][4 * jg + 3] * c);
       }
   }
 }
@@ -512,11 +519,13 @@ static hipError_t launch_attn8(const Dims& d, const Bf16Args& a, hipStream_t s) 
 hipError_t launch_softmax_fp8(const Dims& d, const Bf16Args& a, hipStream_t s) {
   // ring depth: 2 stages measured faster than 3 or 4 at both head sizes
   // (D = 128 at the 768p shape: 10.5 against 12.8 ms; D = 64 on the fp8
-  // workload: 0.43-0.445 against 0.455-0.47 ms).  At D = 64 the kernel fits
-  // three waves per SIMD (<= 168 registers), which hides more of its
-  // vector-ALU latency: 0.375-0.40 against 0.44-0.46 ms.
-  if (d.D == 128) return launch_attn8<128, 4, 2, 2>(d, a, s);
-  if (d.D == 64) return launch_attn8<64, 4, 2, 3>(d, a, s);
+  // workload: 0.43-0.445 against 0.455-0.47 ms).  With one output
+  // accumulator the kernel fits three waves per SIMD at D = 128 (166
+  // registers: 10.4 against 10.9 ms) and four at D = 64 (128 registers:
+  // 0.38-0.40 against 0.45-0.47 ms at two), which hide more of its
+  // vector-ALU latency.
+  if (d.D == 128) return launch_attn8<128, 4, 2, 3>(d, a, s);
+  if (d.D == 64) return launch_attn8<64, 4, 2, 4>(d, a, s);
   return hipErrorInvalidValue;
 }
 
