@@ -2,18 +2,22 @@
 //
 // The VDN-H3 article's performance section reports an "FP8 version" of the
 // model without saying which products run in fp8.  With the fp8 GEMM option
-// the Q/K/V projection, the gate GEMM and the output GEMM take e4m3 operands
-// with one power-of-two (E8M0) scale per 32 consecutive contraction
-// elements (the OCP microscaling block format), which gfx950's scaled MFMA
-// applies in hardware.  The block exponent is the smallest one that keeps
-// the block's largest magnitude within e4m3's 448 (mx_exponent), so no
-// element saturates; elements are rounded to nearest even.
+// the Q/K/V projection, the gate GEMM, the output GEMM and the DiT block's
+// feed-forward GEMMs take e4m3 operands with one power-of-two (E8M0) scale
+// per 32 consecutive contraction elements (the OCP microscaling block
+// format), which gfx950's scaled MFMA applies in hardware.  The block
+// exponent is the smallest one that keeps the block's largest magnitude
+// within e4m3's 448 (mx_exponent), so no element saturates; elements are
+// rounded to nearest even.
 //
 // Layouts (bytes):
 //   codes      [rows][K]            row-major, contraction contiguous
 //   exponents  [K / 128][rows][4]   byte j of word (g, r) = block 4 g + j of row r
-// Activation exponent arrays have mpad rows (tokens rounded up to 256); the
-// rows past the last token hold exponent 0 (scale 1) and are never stored.
+// Activation exponent arrays have mpad rows (tokens rounded up to 256), so
+// that a GEMM's last token tile loads whole exponent chunks.  k_mx_rows fills
+// the rows past the last token with exponent 0 (scale 1); the GEMM epilogues
+// that quantise A' and the GELU output leave them unset.  Either way they
+// only feed output rows that are never stored.
 #include "kernels_bf16.h"
 #include "mx_common.h"
 
