@@ -41,7 +41,8 @@ GATE_ATOL = 1e-6
 MX_DELTA_TOL = (4e-2, 2e-3)
 MX_CASES = [WORKLOADS[2].with_(name="mx-workload2", soft="fp8_mx"),
             Workload("mx-ragged-b2-d128", 2, 5, 100, 37, 2, 128, soft="fp8_mx", seed=61),
-            Workload("mx-notext-d64", 1, 4, 130, 0, 4, 64, soft="fp8_mx", seed=62)]
+            Workload("mx-notext-d64", 1, 4, 130, 0, 4, 64, soft="fp8_mx", seed=62),
+            Workload("mx-one-partial-tile", 1, 2, 50, 3, 2, 128, soft="fp8_mx", seed=65)]  # 100 tokens
 
 
 def _hid(a, w):
