@@ -195,7 +195,9 @@ def forward(lay: Layout, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin, w_
     Tensors are torch device tensors in the activation dtype (float32 or
     bfloat16): x [B, N, hid]; q, k, v [B, N, H, D]; text_k, text_v
     [B, L, H, D]; weights [hid, hid] ([in][out]); rms_weight [hid].  ``soft``
-    is None (same as the activations) or "fp8".  ``debug`` may map any of
+    is None (same as the activations), "fp8" (e4m3 softmax branch) or
+    "fp8_mx" (the fp8 version: also the gate and output GEMMs on MX e4m3
+    operands; bf16 activations, hid % 256 == 0).  ``debug`` may map any of
     o_soft, o_lin, delta_f32, gates, scales to float32 device tensors, and
     "stage_events" to the address of an array of 2 * len(STAGES) hipEvent_t
     (see ``StageTimer``).
