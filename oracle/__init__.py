@@ -42,6 +42,16 @@ Parity status per function (what pins it, in ``tests/test_oracle_*.py``):
                                       invariance, zero / identity / one-hot
                                       feed-forward weights, composition with
                                       the layer oracle.
+  fp8.round_e4m3 / quantise           pinned: torch's float8_e4m3fn conversion,
+                                      the format's closed forms.
+  fp8.softmax_branch_fp8              pinned: uniform scores (mean of the
+                                      quantised values), probabilities on the
+                                      e4m3 grid and unrounded probabilities
+                                      (both equal to softmax_branch on the
+                                      dequantised inputs), hand-derived codes
+                                      of a frame-tiled walk, a maximum rising
+                                      inside a tile, a subnormal code; planted
+                                      mistakes are caught.
   mx.mx_exponent / mx_quantise /      pinned: closed forms and brute-force
   mx_matmul / epilogue_mx /           minimality of the block exponent,
   hybrid_forward_mx                   torch's float8_e4m3fn rounding, exact

@@ -2,22 +2,45 @@
 infrastructure only).
 
 The VDN-H3 article's performance section reports an "FP8 version" without
-saying which operations are fp8.  The library's reading: the softmax
-branch's Q, K, V (video and text) are quantised per (tensor, batch, head)
-with scale s = absmax / 448 and both products run on fp8 inputs.  This module
-computes what that quantised problem gives in exact arithmetic, so that the
-GPU's fp8 kernel can be checked against the computation it is meant to do,
-while the layer output is checked against the unquantised oracle.
+saying which operations are fp8.  The library's reading, which this module
+writes out:
 
-Decisions that pick a quantised code are taken in float32, as the kernel
-takes them: s = float32(absmax) / 448, inv = 1 / s, x * inv in float32, then
-round-to-nearest-even to e4m3 with saturation at +-448.
+* the softmax branch's Q, K, V (video and text) are quantised per
+  (tensor, batch, head) with scale s = absmax / 448, round-to-nearest-even
+  and saturation; the scores are the exact products of the codes times the
+  two scales;
+* the probabilities that multiply V are rounded to e4m3 after scaling by
+  2^8 (so that values down to 2^-17 stay representable), against a running
+  row maximum taken per 64-key tile: the keys are walked frame by frame
+  through S(f) in ascending frame order, each frame in tiles of 64 keys from
+  its first token (the last tile of a frame may be short), then the text in
+  tiles of 64; the running maximum m (log2 units) starts at -inf and moves to
+  a tile's maximum only when that exceeds m by more than 0.75, so every
+  scaled probability stays at most 2^8.75 < 448; when m moves, the sums
+  gathered so far are multiplied by 2^(m_old - m_new);
+* the normaliser sums the probabilities before their e4m3 rounding.
+
+The result depends on the order of the walk (a probability's code depends on
+the maximum seen up to its tile), which is why the walk is part of the
+reading.  Decisions that pick a code or move the maximum are taken in
+float32, as the kernel takes them: the scale s = float32(absmax) / 448,
+x * (1 / s) in float32; the score of two code vectors rounded to float32,
+times the float32 factor (s_q s_k) tau log2(e); the tile maximum compared
+with m + 0.75 in float32; the scaled probability 2^(score + 8 - m) formed as
+a float32 fused multiply-add followed by a float32 exp2.  Sums, the rescale
+factors and the final division run in float64.
 
 e4m3 (OCP FP8 E4M3): 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits;
 normal numbers 2^-6 .. 448, subnormals in steps of 2^-9, no infinities.
 
-Pinned by tests/test_oracle_fp8.py against torch's float8_e4m3fn conversion
-and by closed forms of the format (max, min subnormal, ties to even).
+Pinned by tests/test_oracle_fp8.py: the rounding against torch's
+float8_e4m3fn conversion and the format's closed forms; the branch by
+uniform scores (the mean of the quantised values), inputs whose scaled
+probabilities are all on the e4m3 grid (then equal to the unquantised
+softmax branch on the dequantised inputs), unrounded probabilities against
+the unquantised branch on random data, and hand-derived codes for a
+frame-tiled walk, a maximum that rises inside a tile and a subnormal code;
+planted mistakes in each step fail one of them.
 """
 import math
 
@@ -26,6 +49,10 @@ import numpy as np
 from .layout import frame_sets
 
 E4M3_MAX = 448.0
+KEY_TILE = 64          # keys per tile of the walk
+P_SLACK = 0.75         # log2 units the running maximum may lag a tile maximum
+P_SCALE_LOG2 = 8.0     # probabilities are rounded as P * 2^8
+LOG2E = 1.4426950408889634
 
 
 def round_e4m3(x):
@@ -39,29 +66,94 @@ def round_e4m3(x):
     return np.sign(x) * np.minimum(q, E4M3_MAX)
 
 
-def quantise(x, axes=(1, 3)):
+def quantise_codes(x, axes=(1, 3)):
     """Per-(batch, head) quantisation of a [B, tokens, H, D] tensor.
-    Returns (dequantised values float64, scales float32 [B, H])."""
+    Returns (e4m3 code values float64, scales float32 [B, H]); the
+    dequantised tensor is codes * scale."""
     x32 = np.asarray(x, np.float32)
+    if x32.shape[1] == 0:
+        return np.zeros(x32.shape), np.ones((x32.shape[0], x32.shape[2]), np.float32)
     amax = np.max(np.abs(x32), axis=axes, keepdims=True)
     s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
     inv = (np.float32(1.0) / s).astype(np.float32)
     codes = round_e4m3((x32 * inv).astype(np.float32))
-    return codes * s.astype(np.float64), s.reshape(s.shape[0], s.shape[2])
+    return codes, s.reshape(s.shape[0], s.shape[2])
 
 
-def softmax_branch_fp8(q, k, v, text_k, text_v, lay, scale=None, tokens=None, p_scale=256.0):
-    """Softmax branch on the quantised inputs, in float64, with the
-    probabilities rounded to e4m3 (after scaling by p_scale) in the P V
-    product and exact in the normaliser."""
+def quantise(x, axes=(1, 3)):
+    """Per-(batch, head) quantisation of a [B, tokens, H, D] tensor.
+    Returns (dequantised values float64, scales float32 [B, H])."""
+    codes, s = quantise_codes(x, axes)
+    return codes * s.astype(np.float64)[:, None, :, None], s
+
+
+def scale_log2(D, scale=None):
+    """float32 tau log2(e), tau = scale if given (> 0), else 1/sqrt(D) in
+    float32."""
+    tau = np.float32(scale) if scale else np.float32(1.0) / np.sqrt(np.float32(D))
+    return np.float32(tau * np.float32(LOG2E))
+
+
+def key_tiles(frames, n, L):
+    """The walk: (segment, first key, key count) per tile; segment "v" is the
+    video tensor (first key = token index), "t" the text."""
+    out = []
+    for g in sorted(frames):
+        for t0 in range(0, n, KEY_TILE):
+            out.append(("v", g * n + t0, min(KEY_TILE, n - t0)))
+    for t0 in range(0, L, KEY_TILE):
+        out.append(("t", t0, min(KEY_TILE, L - t0)))
+    return out
+
+
+def _exp2_f32(a32):
+    return np.exp2(np.asarray(a32, np.float32)).astype(np.float32)
+
+
+def online_rows(qc, tiles, round_p=True):
+    """Walk of one block of query rows.
+
+    qc: [R, D] query codes.  tiles: list of (key codes [n_t, D], dequantised
+    values [n_t, D] float64, float32 logit factor (s_q s_k) tau log2(e)).
+    Returns [R, D] float64."""
+    R, D = qc.shape
+    m = np.full(R, -np.inf, np.float32)
+    l = np.zeros(R)
+    acc = np.zeros((R, D))
+    slack = np.float32(P_SLACK)
+    for kc, vd, dq in tiles:
+        s32 = (qc @ kc.T).astype(np.float32)                        # exact sums, rounded once
+        mx = (s32.max(axis=1) * dq).astype(np.float32)
+        grow = mx > m + slack
+        m_new = np.where(grow, mx, m).astype(np.float32)
+        alpha = np.where(grow, np.exp2(m.astype(np.float64) - m_new.astype(np.float64)), 1.0)
+        alpha = np.where(np.isneginf(m), 0.0, alpha)
+        acc *= alpha[:, None]
+        l *= alpha
+        m = m_new
+        moff = (np.float32(P_SCALE_LOG2) - m).astype(np.float32)
+        # fused multiply-add: s dq + moff is exact in float64, rounded once
+        arg = (s32.astype(np.float64) * np.float64(dq) + moff.astype(np.float64)[:, None]).astype(np.float32)
+        p = _exp2_f32(arg).astype(np.float64)                       # P * 2^8
+        pw = round_e4m3(p) if round_p else p
+        acc += pw @ vd
+        l += p.sum(axis=1)
+    return acc / l[:, None]
+
+
+def softmax_branch_fp8(q, k, v, text_k, text_v, lay, scale=None, tokens=None, round_p=True):
+    """Softmax branch on the quantised inputs with the e4m3 probability
+    rounding of the reading above; round_p=False keeps the probabilities
+    unrounded (the quantisation of Q, K and V alone).  Returns
+    [B, len(tokens), H, D] float64 (all video tokens when tokens is None)."""
     B, N, H, D = q.shape
-    n = lay.tokens_per_frame
-    tau = 1.0 / math.sqrt(D) if not scale else float(scale)
-    qq, _ = quantise(q)
-    kq, _ = quantise(k)
-    vq, _ = quantise(v)
-    tkq, _ = quantise(text_k) if text_k.shape[1] else (np.zeros(text_k.shape), None)
-    tvq, _ = quantise(text_v) if text_v.shape[1] else (np.zeros(text_v.shape), None)
+    n, L = lay.tokens_per_frame, text_k.shape[1]
+    sl2 = scale_log2(D, scale)
+    qc, sq = quantise_codes(q)
+    kc, sk = quantise_codes(k)
+    vc, sv = quantise_codes(v)
+    tkc, stk = quantise_codes(text_k)
+    tvc, stv = quantise_codes(text_v)
     sets = frame_sets(lay.frames, lay.chunk_frames, lay.chunk_radius, lay.anchor_first, lay.anchor_last)
     rows = np.arange(N) if tokens is None else np.asarray(tokens)
     out = np.zeros((B, rows.size, H, D))
@@ -70,26 +162,24 @@ def softmax_branch_fp8(q, k, v, text_k, text_v, lay, scale=None, tokens=None, p_
         sel = np.nonzero(frame_of == f)[0]
         if sel.size == 0:
             continue
-        kt = np.concatenate([np.arange(g * n, (g + 1) * n) for g in sorted(sets[f][0])])
+        walk = key_tiles(sets[f][0], n, L)
         for b in range(B):
             for h in range(H):
-                K = np.concatenate([kq[b, kt, h], tkq[b, :, h]])
-                V = np.concatenate([vq[b, kt, h], tvq[b, :, h]])
-                s = tau * (qq[b, rows[sel], h] @ K.T)
-                s -= s.max(axis=1, keepdims=True)
-                p = np.exp(s)
-                pq = round_e4m3(p * p_scale) / p_scale
-                out[b, sel, h] = (pq @ V) / p.sum(axis=1, keepdims=True)
+                dqv = np.float32(np.float32(sq[b, h] * sk[b, h]) * sl2)
+                dqt = np.float32(np.float32(sq[b, h] * stk[b, h]) * sl2)
+                tiles = []
+                for seg, t0, cnt in walk:
+                    if seg == "v":
+                        tiles.append((kc[b, t0:t0 + cnt, h], vc[b, t0:t0 + cnt, h] * np.float64(sv[b, h]), dqv))
+                    else:
+                        tiles.append((tkc[b, t0:t0 + cnt, h], tvc[b, t0:t0 + cnt, h] * np.float64(stv[b, h]),
+                                      dqt))
+                for s0 in range(0, sel.size, 512):
+                    ii = sel[s0:s0 + 512]
+                    out[b, ii, h] = online_rows(qc[b, rows[ii], h], tiles, round_p)
     return out
 
 
 def scales(inp):
     """float32 dequantisation scales [5, B, H] of q, k, v, text_k, text_v."""
-    out = []
-    for name in ("q", "k", "v", "text_k", "text_v"):
-        x = inp[name]
-        if x.shape[1] == 0:
-            out.append(np.ones((x.shape[0], x.shape[2]), np.float32))
-        else:
-            out.append(quantise(x)[1])
-    return np.stack(out)
+    return np.stack([quantise_codes(inp[name])[1] for name in ("q", "k", "v", "text_k", "text_v")])

@@ -13,6 +13,27 @@ TOL = {  # (max |err| / max |ref|, mean relative error)
     "fp8": (4e-2, 4e-2),
 }
 
+# fp8 softmax output against the e4m3 emulation (oracle/fp8.py), which takes
+# every code and every move of the running maximum in float32 as the kernel
+# does.  What is left between the two: the fp16 storage of O_s (at most 2^-11
+# relative per element), float32 accumulation of up to ~25,000 products in
+# the matrix cores and of the normaliser, and rare codes that flip where
+# v_exp_f32 (1 ulp) puts a scaled probability on the other side of an e4m3
+# rounding boundary (one key's weight moves by at most 2^-3 relative).  Each
+# is well below the bf16 bounds, which are used here; a probability rounded
+# against another maximum moves O_s by ~3% mean, a wrong code or scale by
+# 100%.
+FP8_EMU_TOL = (1e-2, 2e-3)
+
+# Limit of the fp8 reading itself: what per-(tensor, batch, head) absmax
+# quantisation of Q, K, V (with the 1% x8 outliers of the fp8 workload) and
+# e4m3 probabilities leave on O_s against the unquantised oracle.  The
+# emulation gives max 0.184 / mean 0.057 on the fp8 workload (every token;
+# 0.210 / 0.058 on 64 sampled tokens per frame), Q/K/V quantisation alone
+# 0.184 / 0.048, probability rounding alone 0.010 / 0.023.  The layer output
+# stays within the fp8 bound (TOL["fp8"]).
+FP8_READING_LIMIT = (0.25, 0.065)
+
 
 def oracle_layout(w):
     return OLayout(w.batch, w.frames, w.tokens_per_frame, w.text_tokens, w.heads, w.head_dim,
