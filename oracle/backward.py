@@ -312,3 +312,49 @@ def block_backward(inp, lay, proj, dy, scale=None, eps=1e-6):
         g["d" + name] = xf.T @ d
     g["dx"] = dx.reshape(B, N, hid)
     return g
+
+
+def key_side_grads(inp, lay, dy, heads, scale=None, eps=1e-6, rows_per_block=4096, log=None):
+    """Key-side gradients of the layer for a subset of heads, at sizes where
+    hybrid_backward would be slow: dk, dv [B, N, len(heads), D] and dtext_k,
+    dtext_v [B, L, len(heads), D] for those heads, and the weight gradients
+    dw_gl, dw_ol [hid, hid] and drms_w [hid], which do not involve O_s.
+
+    dL/dO_s and dL/dO_l come from epilogue_backward run on row blocks (its
+    d_os = (dy W_os^T) G_s and d_ol, dw_gl, dw_ol, drms_w never read O_s,
+    which is passed as zeros; the weight gradients are sums over rows); the
+    softmax and linear reverse steps then run on the chosen heads alone,
+    since both branches are independent per (batch, head).  ``log``, if
+    given, is called with a short message after each of those steps."""
+    from .hybrid import linear_branch
+    log = log or (lambda msg: None)
+    q, k, v, tk, tv = (np.asarray(inp[n]) for n in ("q", "k", "v", "text_k", "text_v"))
+    B, N, H, D = q.shape
+    hid = H * D
+    st = linear_states(k, v, tk, tv, lay)
+    o_l = linear_branch(q, st, lay, eps=eps).reshape(B, N, hid)
+    log("linear branch forward done")
+    x = np.asarray(inp["x"])
+    dyv = np.asarray(dy)
+    d_os = np.zeros((B, N, len(heads), D))
+    d_ol = np.zeros((B, N, len(heads), D))
+    dw_gl = np.zeros((hid, hid))
+    dw_ol = np.zeros((hid, hid))
+    drms_w = np.zeros(hid)
+    for r0 in range(0, N, rows_per_block):
+        sl = slice(r0, min(N, r0 + rows_per_block))
+        ep = epilogue_backward(x[:, sl], np.zeros((B, sl.stop - r0, hid)), o_l[:, sl], inp["w_gs"], inp["w_gl"],
+                               inp["w_os"], inp["w_ol"], inp["rms_w"], dyv[:, sl], eps=eps)
+        d_os[:, sl] = ep["d_os"].reshape(B, -1, H, D)[:, :, heads]
+        d_ol[:, sl] = ep["d_ol"].reshape(B, -1, H, D)[:, :, heads]
+        dw_gl += ep["dw_gl"]
+        dw_ol += ep["dw_ol"]
+        drms_w += ep["drms_w"]
+        log("epilogue reverse: rows %d of %d" % (sl.stop, N))
+    sub = [np.ascontiguousarray(a[:, :, heads]) for a in (q, k, v, tk, tv)]
+    _, sk, sv, stk, stv = softmax_backward(*sub, lay, d_os, scale=scale)
+    log("softmax branch reverse done")
+    _, lk, lv, ltk, ltv = linear_backward(*sub, lay, d_ol, eps=eps)
+    log("linear branch reverse done")
+    return {"dk": sk + lk, "dv": sv + lv, "dtext_k": stk + ltk, "dtext_v": stv + ltv,
+            "dw_gl": dw_gl, "dw_ol": dw_ol, "drms_w": drms_w}

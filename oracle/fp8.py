@@ -110,20 +110,65 @@ def _exp2_f32(a32):
     return np.exp2(np.asarray(a32, np.float32)).astype(np.float32)
 
 
-def online_rows(qc, tiles, round_p=True):
+def ambiguous_step(p, rel):
+    """For scaled probabilities p (0 <= p < 448) known to a relative accuracy
+    rel: the distance between the two e4m3 values around p where p lies within
+    rel * p of the rounding boundary between them, else 0."""
+    p = np.asarray(p, np.float64)
+    step = np.exp2(np.floor(np.log2(np.maximum(p, 2.0 ** -6))) - 3.0)
+    mid = np.floor(p / step) * step + step / 2
+    return np.where(np.abs(p - mid) <= rel * p, step, 0.0)
+
+
+def online_rows(qc, tiles, round_p=True, mfma_prec=0.0, perturb=None):
     """Walk of one block of query rows.
 
     qc: [R, D] query codes.  tiles: list of (key codes [n_t, D], dequantised
     values [n_t, D] float64, float32 logit factor (s_q s_k) tau log2(e)).
-    Returns [R, D] float64."""
+    Returns ([R, D] float64, [R] margin, [R, D] bound or None).
+
+    margin: the smallest |tile maximum - (m + slack)| over the row's
+    decisions after the first (inf with one tile), less the error those
+    decisions may carry under the model below: a row with margin <= 0 may
+    decide otherwise on hardware and round its later probabilities against
+    another maximum.
+
+    mfma_prec > 0 gives a bound on how far hardware may land from this
+    result when its matrix instruction returns each step of 64 products
+    (64 consecutive head dimensions of a score, 64 keys of a tile for the
+    probability-value product) only to within mfma_prec times the largest
+    |product| of the step, its exp2 and fused multiply-add carry a float32
+    ulp, and its float32 running sums one ulp per add.  Every scaled
+    probability is then known to a relative accuracy rel; one within rel of
+    an e4m3 rounding boundary may take the other code; a moved maximum
+    rescales what was gathered by a factor known to the error of both
+    maxima.  perturb (a numpy Generator) moves every score, probability and
+    product step by a random amount inside that model -- the deviation the
+    bound has to cover."""
     R, D = qc.shape
     m = np.full(R, -np.inf, np.float32)
     l = np.zeros(R)
     acc = np.zeros((R, D))
+    margin = np.full(R, np.inf)
     slack = np.float32(P_SLACK)
+    bound = np.zeros((R, D)) if mfma_prec else None
+    mag = np.zeros((R, D))        # sum of |code| |value| gathered so far (units of the current maximum)
+    em = np.zeros(R)              # error bound of the running maximum (log2 units)
+    rmax = np.zeros(R)            # largest relative error of a probability or rescale in the row
+    fp32_sums = len(tiles) * 2.0 ** -24
+    steps = [slice(d0, min(D, d0 + 64)) for d0 in range(0, D, 64)]
     for kc, vd, dq in tiles:
         s32 = (qc @ kc.T).astype(np.float32)                        # exact sums, rounded once
+        if mfma_prec:
+            # largest |q_d k_d| of each 64-dimension step, bounded by max|q_d| max|k_d|
+            big = sum(np.abs(qc[:, st]).max(axis=1)[:, None] * np.abs(kc[:, st]).max(axis=1)[None, :]
+                      for st in steps)
+            et = mfma_prec * big * float(dq)                        # error bound of each log2-score
+            if perturb is not None:
+                s32 = (s32 + mfma_prec * big * perturb.uniform(-1, 1, big.shape)).astype(np.float32)
         mx = (s32.max(axis=1) * dq).astype(np.float32)
+        dec_err = 2.0 * et.max(axis=1) if mfma_prec else 0.0
+        margin = np.minimum(margin, np.where(np.isneginf(m), np.inf, np.abs(mx - (m + slack)) - dec_err))
         grow = mx > m + slack
         m_new = np.where(grow, mx, m).astype(np.float32)
         alpha = np.where(grow, np.exp2(m.astype(np.float64) - m_new.astype(np.float64)), 1.0)
@@ -135,17 +180,45 @@ def online_rows(qc, tiles, round_p=True):
         # fused multiply-add: s dq + moff is exact in float64, rounded once
         arg = (s32.astype(np.float64) * np.float64(dq) + moff.astype(np.float64)[:, None]).astype(np.float32)
         p = _exp2_f32(arg).astype(np.float64)                       # P * 2^8
+        if perturb is not None:
+            p = p * (1.0 + 2.0 ** -22 * perturb.uniform(-1, 1, p.shape))
         pw = round_e4m3(p) if round_p else p
-        acc += pw @ vd
+        prod = pw @ vd
+        if mfma_prec:
+            mag_new = np.abs(pw) @ np.abs(vd)
+            pv_err = mfma_prec * np.abs(pw).max(axis=1)[:, None] * np.abs(vd).max(axis=0)[None, :] \
+                + fp32_sums * mag_new
+            if perturb is not None:
+                prod = prod + pv_err * perturb.uniform(-1, 1, prod.shape)
+            em_new = np.where(grow, et.max(axis=1), em)
+            ea = np.where(grow & (alpha > 0), np.log(2.0) * (em + em_new) + 2.0 ** -22, 0.0)
+            em = em_new
+            # one float32 ulp of the exponent argument (and of 8 - m) moves P by ln 2 ulp
+            ulp = np.spacing(np.abs(arg)).astype(np.float64) + np.spacing(np.abs(moff)).astype(np.float64)[:, None]
+            rel = np.log(2.0) * (et + em[:, None] + ulp) + 2.0 ** -21
+            rmax = np.maximum(rmax, np.maximum(rel.max(axis=1), ea))
+            bound = alpha[:, None] * (bound + ea[:, None] * mag)
+            mag = alpha[:, None] * mag + mag_new
+            bound += pv_err + (ambiguous_step(p, rel) @ np.abs(vd) if round_p else 0.0)
+        acc += prod
         l += p.sum(axis=1)
-    return acc / l[:, None]
+    out = acc / l[:, None]
+    if mfma_prec:
+        bound = bound / l[:, None] + (rmax + fp32_sums)[:, None] * np.abs(out)
+    return out, margin, bound
 
 
-def softmax_branch_fp8(q, k, v, text_k, text_v, lay, scale=None, tokens=None, round_p=True):
+def softmax_branch_fp8(q, k, v, text_k, text_v, lay, scale=None, tokens=None, round_p=True, margins=False,
+                       mfma_prec=0.0, perturb=None):
     """Softmax branch on the quantised inputs with the e4m3 probability
     rounding of the reading above; round_p=False keeps the probabilities
     unrounded (the quantisation of Q, K and V alone).  Returns
-    [B, len(tokens), H, D] float64 (all video tokens when tokens is None)."""
+    [B, len(tokens), H, D] float64 (all video tokens when tokens is None);
+    with margins=True also [B, len(tokens), H]: per row, how close (log2
+    units) its closest decision on the running maximum came to going the
+    other way (less its error under mfma_prec, see online_rows); with
+    mfma_prec > 0 also the [B, len(tokens), H, D] deviation bound of
+    online_rows.  perturb: see online_rows."""
     B, N, H, D = q.shape
     n, L = lay.tokens_per_frame, text_k.shape[1]
     sl2 = scale_log2(D, scale)
@@ -157,6 +230,8 @@ def softmax_branch_fp8(q, k, v, text_k, text_v, lay, scale=None, tokens=None, ro
     sets = frame_sets(lay.frames, lay.chunk_frames, lay.chunk_radius, lay.anchor_first, lay.anchor_last)
     rows = np.arange(N) if tokens is None else np.asarray(tokens)
     out = np.zeros((B, rows.size, H, D))
+    marg = np.full((B, rows.size, H), np.inf)
+    bnd = np.zeros((B, rows.size, H, D)) if mfma_prec else None
     frame_of = rows // n
     for f in range(lay.frames):
         sel = np.nonzero(frame_of == f)[0]
@@ -176,8 +251,13 @@ def softmax_branch_fp8(q, k, v, text_k, text_v, lay, scale=None, tokens=None, ro
                                       dqt))
                 for s0 in range(0, sel.size, 512):
                     ii = sel[s0:s0 + 512]
-                    out[b, ii, h] = online_rows(qc[b, rows[ii], h], tiles, round_p)
-    return out
+                    o, mg, bd = online_rows(qc[b, rows[ii], h], tiles, round_p, mfma_prec, perturb)
+                    out[b, ii, h], marg[b, ii, h] = o, mg
+                    if mfma_prec:
+                        bnd[b, ii, h] = bd
+    if mfma_prec:
+        return out, marg, bnd
+    return (out, marg) if margins else out
 
 
 def scales(inp):

@@ -48,7 +48,7 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(torch.bfloat16)
 
 
-def run_backward(w, inp, dy, weight_grads=api.WEIGHT_GRADS):
+def run_backward(w, inp, dy, weight_grads=api.WEIGHT_GRADS, **kw):
     import torch
     d = {k: _dev(v) for k, v in inp.items()}
     B, N, H, D = w.batch, w.n_video, w.heads, w.head_dim
@@ -56,20 +56,18 @@ def run_backward(w, inp, dy, weight_grads=api.WEIGHT_GRADS):
     dbg = {"d_os": torch.empty(B, N, H, D, **f32), "d_ol": torch.empty(B, N, H, D, **f32),
            "lse2": torch.empty(B, H, N, **f32)}
     g = api.backward(gu.api_layout(w), d["x"], d["q"], d["k"], d["v"], d["text_k"], d["text_v"], d["w_gs"],
-                     d["w_gl"], d["w_os"], d["w_ol"], d["rms_w"], _dev(dy), weight_grads=weight_grads, debug=dbg)
+                     d["w_gl"], d["w_os"], d["w_ol"], d["rms_w"], _dev(dy), weight_grads=weight_grads, debug=dbg,
+                     **kw)
     torch.cuda.synchronize()
     out = {k: v.float().cpu().numpy().astype(np.float64) for k, v in g.items()}
     out.update({k: v.cpu().numpy().astype(np.float64) for k, v in dbg.items()})
     return out
 
 
-@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
-def test_backward_matches_oracle(w):
-    inp = make_inputs(w)
-    dy = make_grad_output(w)
+def check_backward(w, inp, dy, scale=None):
     print("case", w.name, flush=True)
-    got = run_backward(w, inp, dy)
-    ref = obw.hybrid_backward(inp, gu.oracle_layout(w), dy)
+    got = run_backward(w, inp, dy, softmax_scale=scale or 0.0)
+    ref = obw.hybrid_backward(inp, gu.oracle_layout(w), dy, scale=scale)
     B, N, H = w.batch, w.n_video, w.heads
     # intermediates: dL/dO_s, dL/dO_l and the softmax row statistics
     e = gu.errors(got["d_os"], ref["d_os"])
@@ -93,6 +91,28 @@ def test_backward_matches_oracle(w):
         if not (e[0] <= TOL_GRAD[0] and e[1] <= TOL_GRAD[1]):
             failed.append((gname, e))
     assert not failed, failed
+
+
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
+def test_backward_matches_oracle(w):
+    check_backward(w, make_inputs(w), make_grad_output(w))
+
+
+def test_backward_sharp_attention():
+    """Inputs on which the forward kernel's running maximum moves mid-walk
+    (tests/test_gpu_parity.sharp_inputs): the saved row statistics and every
+    gradient that recomputes P from them."""
+    from tests.test_gpu_parity import SHARP, rescale_fraction, sharp_inputs
+    for w in SHARP:
+        inp = sharp_inputs(w)
+        assert rescale_fraction(w, inp) >= 0.5
+        check_backward(w, inp, make_grad_output(w))
+
+
+def test_backward_softmax_scale():
+    """A non-zero softmax_scale through the backward's C ABI."""
+    w = Workload("bwd-scale", 1, 5, 96, 24, 2, 64, qkv_scale=0.7, seed=78)
+    check_backward(w, make_inputs(w), make_grad_output(w), scale=0.21)
 
 
 def test_frozen_weights_are_not_written_and_rest_unchanged():
@@ -131,7 +151,8 @@ def test_backward_head_major_strides_bit_identical():
 
 def test_backward_768p_sampled():
     """768p shape, the bench's launch configuration: dq and dx on sampled
-    tokens against the oracle evaluated one token at a time (full states)."""
+    tokens against the oracle evaluated one token at a time (full states);
+    the key-side gradients are checked by test_backward_768p_key_side."""
     import torch
     from hybrid_softmax_linear_block_amd.inputs import sample_tokens
     w = WORKLOADS[3]
@@ -151,6 +172,41 @@ def test_backward_768p_sampled():
         e = gu.errors(got, ref)
         print("768p", name, "max %.2e mean %.2e" % e, flush=True)
         assert e[0] <= TOL_GRAD[0] and e[1] <= TOL_GRAD[1], (name, e)
+
+
+def test_backward_768p_key_side():
+    """768p shape, the bench's launch configuration: the key-side gradients
+    of the dK/dV kernel and the linear branch (dk, dv, dtext_k, dtext_v) for
+    every key of two heads, and the weight gradients dW_gate_lin,
+    dW_out_lin and drms_weight in full.  Oracle: dL/dO_s and dL/dO_l from the
+    epilogue's reverse step (row blocks; neither depends on O_s), then the
+    softmax and linear branches' reverse steps on the two heads alone (the
+    branches are independent per head)."""
+    import torch
+    w = WORKLOADS[3]
+    heads = [0, 13]
+    inp = make_inputs(w)
+    dy = make_grad_output(w)
+    d = {k: _dev(v) for k, v in inp.items()}
+    g = api.backward(gu.api_layout(w), d["x"], d["q"], d["k"], d["v"], d["text_k"], d["text_v"], d["w_gs"],
+                     d["w_gl"], d["w_os"], d["w_ol"], d["rms_w"], _dev(dy),
+                     weight_grads=("w_gate_lin", "w_out_lin", "rms_weight"))
+    torch.cuda.synchronize()
+    got = {k: g[k][:, :, heads].float().cpu().numpy().astype(np.float64) for k in ("dk", "dv", "dtext_k", "dtext_v")}
+    for k in ("dw_gate_lin", "dw_out_lin", "drms_weight"):
+        got[k] = g[k].float().cpu().numpy().astype(np.float64)
+    del g
+    torch.cuda.empty_cache()
+    print("768p key side: GPU done, oracle", flush=True)
+    ref = obw.key_side_grads(inp, gu.oracle_layout(w), dy, heads, log=lambda m: print("oracle:", m, flush=True))
+    failed = []
+    for gname, rname in (("dk", "dk"), ("dv", "dv"), ("dtext_k", "dtext_k"), ("dtext_v", "dtext_v"),
+                         ("dw_gate_lin", "dw_gl"), ("dw_out_lin", "dw_ol"), ("drms_weight", "drms_w")):
+        e = gu.errors(got[gname].reshape(ref[rname].shape), ref[rname])
+        print("768p", gname, "max %.2e mean %.2e" % e, flush=True)
+        if not (e[0] <= TOL_GRAD[0] and e[1] <= TOL_GRAD[1]):
+            failed.append((gname, e))
+    assert not failed, failed
 
 
 def test_backward_from_training_forward_bit_identical():

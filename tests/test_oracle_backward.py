@@ -211,6 +211,21 @@ def test_dq_dx_at_sampled_tokens_equal_full_backward():
     assert np.allclose(dx, full["dx"][:, tok], rtol=1e-10, atol=1e-12)
 
 
+def test_key_side_grads_equal_full_backward():
+    """The head-subset form used at full size equals the full backward on
+    those heads (row blocks smaller than the token count, so the weight
+    gradients are summed over several blocks)."""
+    for lay in LAYOUTS[:2]:
+        inp, dy = make(lay, 510)
+        full = BW.hybrid_backward(inp, lay, dy, scale=0.4)
+        heads = [lay.heads - 1] if lay.heads > 1 else [0]
+        part = BW.key_side_grads(inp, lay, dy, heads, scale=0.4, rows_per_block=7)
+        for name in ("dk", "dv", "dtext_k", "dtext_v"):
+            assert np.allclose(part[name], full[name][:, :, heads], rtol=1e-10, atol=1e-12), name
+        for name in ("dw_gl", "dw_ol", "drms_w"):
+            assert np.allclose(part[name], full[name], rtol=1e-10, atol=1e-12), name
+
+
 def test_block_gradients_match_finite_differences():
     """Through the Q/K/V projection: dx and the projection weights' gradients
     against central differences of the block forward."""

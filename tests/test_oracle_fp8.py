@@ -241,13 +241,14 @@ def _source_mutant(fn_name, old, new):
     return ns[fn_name]
 
 
-def _final_max_rows(qc, tiles, round_p=True):
+def _final_max_rows(qc, tiles, round_p=True, mfma_prec=0.0, perturb=None):
     """The earlier reading: every probability rounded against the row's final
     maximum."""
     s = np.concatenate([(qc @ kc.T) * np.float64(dq) for kc, _, dq in tiles], axis=1)
     vd = np.concatenate([v for _, v, _ in tiles], axis=0)
     p = np.exp2(s - s.max(axis=1, keepdims=True) + fp8.P_SCALE_LOG2)
-    return ((fp8.round_e4m3(p) if round_p else p) @ vd) / p.sum(axis=1, keepdims=True)
+    out = ((fp8.round_e4m3(p) if round_p else p) @ vd) / p.sum(axis=1, keepdims=True)
+    return out, np.full(qc.shape[0], np.inf), None
 
 
 def _tiles_across_frames(frames, n, L):
@@ -326,3 +327,47 @@ def test_fp8_reading_gap_on_the_fp8_workload():
     assert gap[0] <= FP8_READING_LIMIT[0] and gap[1] <= FP8_READING_LIMIT[1], gap
     assert gap_qkv[0] >= 0.9 * gap[0]
     assert gap_p[0] <= 0.03 and 0.01 <= gap_p[1] <= 0.04, gap_p
+
+
+def test_decision_margins():
+    """margins=True: inf for a one-tile walk; the frame-tiled walk's rows
+    decide at tile maxima t1 = 0.514 (against 0 + 0.75), t2 = 0.9 (against
+    0.75) and 0 (against t2 + 0.75): smallest margin 0.15."""
+    groups = [(0, 32, 0), (32, 32, 256)]
+    inp, lay, tau = _coded_case(1, 64, groups, 0.9 * 65536 / 448 ** 2)
+    _, marg = _branch(inp, lay, scale=tau, margins=True)
+    assert np.all(np.isinf(marg))
+    groups = [(0, 64, 0), (64, 32, 256), (96, 32, 448), (128, 32, 0), (160, 32, 0)]
+    inp, lay, tau = _coded_case(2, 96, groups, 0.9 * 65536 / 448 ** 2)
+    out, marg = _branch(inp, lay, scale=tau, margins=True)
+    np.testing.assert_allclose(marg, 0.15, rtol=1e-5)
+    np.testing.assert_array_equal(out, _branch(inp, lay, scale=tau))
+
+
+def test_deviation_bound_covers_the_summation_model():
+    """mfma_prec > 0: with every score, probability and product step moved at
+    random inside the model (perturb), each output element stays within the
+    bound -- on random data with outliers and sharp rows, text and ragged
+    frames, at D = 64 (one step per score) and D = 128 (two), for the rows
+    whose decisions cannot flip (margin > 0).  The bound is not vacuous: a
+    16x smaller one is exceeded."""
+    for D, seed in ((64, 14), (128, 15)):
+        lay = Layout(2, 6, 150, 70, 2, D)
+        rng = np.random.default_rng(seed)
+        inp = {n: _rand((2, 900 if n in ("q", "k", "v") else 70, 2, D), rng, D ** -0.25) for n in
+               ("q", "k", "v", "text_k", "text_v")}
+        for n in ("q", "k", "v", "text_k", "text_v"):
+            mask = rng.random(inp[n].shape) < 0.01
+            inp[n][mask] *= np.float32(8.0)
+        prec = 2.0 ** -10.5
+        out, marg, bnd = _branch(inp, lay, mfma_prec=prec)
+        np.testing.assert_array_equal(out, _branch(inp, lay))
+        ok = marg > 0
+        assert ok.mean() > 0.97, ok.mean()
+        worst = 0.0
+        for s in range(3):
+            pert, _, _ = _branch(inp, lay, mfma_prec=prec, perturb=np.random.default_rng(100 + s))
+            diff = np.abs(pert - out)[ok]
+            assert np.all(diff <= bnd[ok]), (D, (diff / bnd[ok]).max())
+            worst = max(worst, float((diff / np.maximum(bnd[ok] / 16, 1e-300)).max()))
+        assert worst > 1.0, worst
