@@ -97,6 +97,11 @@ def load(path=None):
         [ctypes.POINTER(_Layout), ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         + [_Tensor] * 5 + [ctypes.c_void_p] * 5 + [ctypes.c_float, ctypes.c_float]
         + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(_Debug)])
+    lib.hyb_attn_forward_noalloc.restype = ctypes.c_int
+    lib.hyb_attn_forward_noalloc.argtypes = (
+        [ctypes.POINTER(_Layout), ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        + [_Tensor] * 5 + [ctypes.c_void_p] * 5 + [ctypes.c_float, ctypes.c_float]
+        + [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Debug)])
     lib.hyb_qkv_workspace_size.restype = ctypes.c_int
     lib.hyb_qkv_workspace_size.argtypes = [ctypes.POINTER(_Layout), ctypes.POINTER(ctypes.c_size_t)]
     lib.hyb_qkv_project.restype = ctypes.c_int
@@ -232,6 +237,50 @@ def forward(lay: Layout, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin, w_
         workspace.numel(), stream, ctypes.byref(dbg) if dbg is not None else None)
     _check(st)
     return y
+
+
+NOALLOC_SCRATCH_BYTES = 256 * 1024 * 1024  # HYB_NOALLOC_SCRATCH_BYTES in include/hyb_attn.h
+
+
+def forward_noalloc(lay: Layout, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin,
+                    rms_weight, y, soft=None, softmax_scale=0.0, eps=1e-6, debug=None, stream=None):
+    """hyb_attn_forward_noalloc: the layer of ``forward`` with the library's
+    built-in scratch instead of a workspace.  ``y`` must be given (this call
+    allocates nothing, not even its output); the other arguments are those of
+    ``forward``.  Calls on one GPU share the scratch: do not overlap them."""
+    lib = load()
+    act = _act_of(x, (x, q, k, v, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin, rms_weight, y),
+                  (x, w_gate_soft, w_gate_lin, w_out_soft, w_out_lin, rms_weight, y))
+    dbg = None
+    if debug:
+        dbg = _Debug(*([_ptr(debug.get(n)) for n in ("o_soft", "o_lin", "delta_f32", "gates", "scales")]
+                       + [debug.get("stage_events")]))
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    c = lay.c()
+    st = lib.hyb_attn_forward_noalloc(
+        ctypes.byref(c), DTYPES[act], DTYPES[soft or act], x.data_ptr(),
+        _tensor4(q), _tensor4(k), _tensor4(v), _tensor4(text_k), _tensor4(text_v),
+        w_gate_soft.data_ptr(), w_gate_lin.data_ptr(), w_out_soft.data_ptr(), w_out_lin.data_ptr(),
+        rms_weight.data_ptr(), float(softmax_scale), float(eps), y.data_ptr(), stream,
+        ctypes.byref(dbg) if dbg is not None else None)
+    _check(st)
+    return y
+
+
+def _act_of(x, same_dtype, contiguous):
+    import torch
+    act = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(x.dtype)
+    if act is None:
+        raise ValueError("activations must be float32 or bfloat16")
+    for t in same_dtype:
+        if t.dtype != x.dtype or not t.is_cuda:
+            raise ValueError("all tensors must be device tensors of the activation dtype")
+    for t in contiguous:
+        if not t.is_contiguous():
+            raise ValueError("x, y, weights and rms_weight must be contiguous")
+    return act
 
 
 def qkv_workspace_size(lay: Layout):

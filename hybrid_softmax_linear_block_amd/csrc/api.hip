@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/hyb_attn.h"
 #include "kernels.h"
 
@@ -435,6 +437,67 @@ hyb_status hyb_attn_forward(const hyb_layout* layout, hyb_dtype act, hyb_dtype s
   return attn_forward_impl(layout, act, soft, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin, w_out_soft,
                            w_out_lin, rms_weight, softmax_scale, eps, y, workspace, workspace_bytes, stream, dbg,
                            false);
+}
+
+}  // extern "C"
+
+// Scratch of hyb_attn_forward_noalloc.  Each GPU the library runs on holds
+// its own copy from the first use until the process ends.  In host code the
+// name is only a handle for hipGetSymbolAddress: kernels and copies get the
+// device address that call returns, kept per device below.
+static __device__ __align__(256) unsigned char scratch[HYB_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch array on the calling thread's current
+// device, looked up once per device.
+hyb_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HYB_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(HYB_ERR_UNSUPPORTED, "device index %d is beyond the %d devices the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(HYB_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HYB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hyb_status hyb_attn_forward_noalloc(const hyb_layout* layout, hyb_dtype act, hyb_dtype soft, const void* x,
+                                    hyb_tensor q, hyb_tensor k, hyb_tensor v, hyb_tensor text_k, hyb_tensor text_v,
+                                    const void* w_gate_soft, const void* w_gate_lin, const void* w_out_soft,
+                                    const void* w_out_lin, const void* rms_weight, float softmax_scale, float eps,
+                                    void* y, void* stream, const hyb_debug* dbg) {
+  g_err[0] = 0;
+  hyb_status st = check_layout(layout, false);
+  if (st != HYB_OK) return st;
+  if ((st = check_dtypes(layout, act, soft)) != HYB_OK) return st;
+  const size_t need = make_plan(make_dims(layout), act, soft).total;
+  if (need > (size_t)HYB_NOALLOC_SCRATCH_BYTES)
+    return fail(HYB_ERR_WORKSPACE_TOO_SMALL,
+                "this call needs %zu bytes of scratch, the built-in scratch of hyb_attn_forward_noalloc holds %zu; "
+                "use hyb_attn_forward with a workspace",
+                need, (size_t)HYB_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws)) != HYB_OK) return st;
+  return attn_forward_impl(layout, act, soft, x, q, k, v, text_k, text_v, w_gate_soft, w_gate_lin, w_out_soft,
+                           w_out_lin, rms_weight, softmax_scale, eps, y, ws, (size_t)HYB_NOALLOC_SCRATCH_BYTES, stream,
+                           dbg, false);
 }
 
 hyb_status hyb_qkv_workspace_size(const hyb_layout* layout, size_t* bytes) {

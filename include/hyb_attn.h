@@ -33,15 +33,17 @@
  * Conventions for every call:
  *   - All tensor pointers are device memory owned by the caller.  The library
  *     never allocates or frees memory; scratch space is the caller's
- *     workspace, sized with hyb_workspace_size().
+ *     workspace, sized with hyb_workspace_size() (hyb_attn_forward_noalloc:
+ *     a device array built into the library).
  *   - hyb_attn_forward() only enqueues work on `stream` and returns; it never
  *     synchronises.  Device faults surface at the caller's next sync.
  *   - Every argument is validated before the first launch; on failure nothing
  *     is launched, the status is returned and hyb_last_error() (thread-local)
  *     describes it.  A failed launch returns HYB_ERR_HIP.
  *   - The library keeps no mutable global state besides the thread-local
- *     error message; concurrent calls on different streams with distinct
- *     workspaces are independent.
+ *     error message and the built-in scratch of hyb_attn_forward_noalloc
+ *     (with its per-device address table); concurrent calls on different
+ *     streams with distinct workspaces are independent.
  */
 #ifndef HYB_ATTN_H
 #define HYB_ATTN_H
@@ -167,6 +169,36 @@ hyb_status hyb_attn_forward(const hyb_layout* layout, hyb_dtype act, hyb_dtype s
                             const void* rms_weight, float softmax_scale, float eps,
                             void* y, void* workspace, size_t workspace_bytes,
                             void* stream, const hyb_debug* dbg);
+
+/*
+ * hyb_attn_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, layer and results as
+ * hyb_attn_forward (the same kernels run), but its scratch is a device array
+ * built into the library:
+ *   - HYB_NOALLOC_SCRATCH_BYTES (256 MiB) per GPU, reserved on each GPU the
+ *     library runs this call on, from its first call there until the
+ *     process ends; the calling thread's current device is the one used and
+ *     `stream` must belong to it;
+ *   - a call whose hyb_workspace_size() exceeds it returns
+ *     HYB_ERR_WORKSPACE_TOO_SMALL before touching the GPU (it holds, e.g.,
+ *     every precision of a 2 x 15 x 1024-token, 512-hidden layer, 146 to
+ *     208 MiB; not the 768p-shaped layer, 1.6 GB and more);
+ *   - every call on one GPU shares that GPU's array and leaves its contents
+ *     behind (nothing in it is read before the call writes it): calls that
+ *     overlap on one GPU, on any streams, race -- serialise them;
+ *   - it calls no allocating routine (no hipMalloc, hipFree or library
+ *     allocator); the first call on a device looks the array's address up
+ *     with hipGetSymbolAddress.
+ */
+#define HYB_NOALLOC_SCRATCH_BYTES (256u * 1024u * 1024u)
+hyb_status hyb_attn_forward_noalloc(const hyb_layout* layout, hyb_dtype act, hyb_dtype soft,
+                                    const void* x, hyb_tensor q, hyb_tensor k, hyb_tensor v,
+                                    hyb_tensor text_k, hyb_tensor text_v,
+                                    const void* w_gate_soft, const void* w_gate_lin,
+                                    const void* w_out_soft, const void* w_out_lin,
+                                    const void* rms_weight, float softmax_scale, float eps,
+                                    void* y, void* stream, const hyb_debug* dbg);
 
 /*
  * Q/K/V input projection -- the step before the layer.  Article section

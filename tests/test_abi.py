@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol():
                             "hyb_qkv_project", "hyb_block_workspace_size", "hyb_block_forward",
                             "hyb_backward_workspace_size", "hyb_attn_backward",
                             "hyb_dit_block_workspace_size", "hyb_dit_block_forward", "hyb_saved_size",
-                            "hyb_attn_forward_train", "hyb_block_backward_workspace_size", "hyb_block_backward"])
+                            "hyb_attn_forward_train", "hyb_block_backward_workspace_size", "hyb_block_backward",
+                            "hyb_attn_forward_noalloc"])
     for n in names:
         assert hasattr(lib, n), n
 
@@ -338,3 +339,22 @@ def test_fp8_mx_mode_validation():
     assert "256" in str(e.value)
     assert api.dit_block_workspace_size(ok, 320, "fp8") > 0
     assert api.dit_block_workspace_size(ok, 1024, "fp8_mx") > api.dit_block_workspace_size(ok, 1024, "fp8")
+
+
+def test_noalloc_size_limit_is_checked_on_the_host():
+    """hyb_attn_forward_noalloc rejects a layout whose workspace exceeds its
+    built-in scratch before any HIP call (so no GPU is needed here); the
+    header's limit and the binding's agree."""
+    text = open(HEADER).read()
+    m = re.search(r"#define HYB_NOALLOC_SCRATCH_BYTES \((\d+)u \* (\d+)u \* (\d+)u\)", text)
+    assert m and int(m.group(1)) * int(m.group(2)) * int(m.group(3)) == api.NOALLOC_SCRATCH_BYTES
+    lib = api.load()
+    lay = api.Layout(1, 15, 4032, 512, 24, 128).c()
+    t = api._Tensor(16, 0, 0, 0)
+    st = lib.hyb_attn_forward_noalloc(ctypes.byref(lay), 1, 1, 16, t, t, t, t, t, 16, 16, 16, 16, 16,
+                                      0.0, 1e-6, 16, None, None)
+    assert st == api.HYB_ERR_WORKSPACE_TOO_SMALL
+    assert b"built-in scratch" in lib.hyb_last_error()
+    small = api.Layout(1, 0, 64, 0, 1, 64).c()   # invalid layout: reported first
+    assert lib.hyb_attn_forward_noalloc(ctypes.byref(small), 1, 1, 16, t, t, t, t, t, 16, 16, 16, 16, 16,
+                                        0.0, 1e-6, 16, None, None) == api.HYB_ERR_INVALID_ARGUMENT
