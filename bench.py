@@ -253,12 +253,15 @@ def oracle_full(w):
                 value=w.batch * w.n_video / wall / 1e6, unit="Mtokens/s")
 
 
-def cpu_baseline(w, inp, budget_s=20.0):
-    """Time the fp64 oracle on the host on a bounded token sample and scale
-    to Mtokens/s: full-state build (all tokens) + per-token work measured on
-    the sample, extrapolated linearly in tokens."""
+def cpu_baseline(w, inp):
+    """Time the fp64 oracle on the host on a bounded sample and scale to
+    Mtokens/s: the full-state build over all tokens, then the softmax
+    branch, readout and epilogue over every token of one query frame per
+    distinct key-set size (the work of a frame depends only on that size),
+    each scaled by the number of frames of its size.  Timing whole frames
+    keeps the oracle's per-frame set-up in the sample at its real share."""
     import oracle
-    from oracle.layout import Layout as OLayout
+    from oracle.layout import Layout as OLayout, frame_sets
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
@@ -267,30 +270,41 @@ def cpu_baseline(w, inp, budget_s=20.0):
     ctx = threadpool_limits(limits=cores) if threadpool_limits else None
     lay = OLayout(w.batch, w.frames, w.tokens_per_frame, w.text_tokens, w.heads, w.head_dim,
                   w.chunk_frames, w.chunk_radius, w.anchor_first, w.anchor_last)
+    sets = frame_sets(w.frames, w.chunk_frames, w.chunk_radius, w.anchor_first, w.anchor_last)
+    classes = {}
+    for f in range(w.frames):
+        classes.setdefault(len(sets[f][0]), []).append(f)
+    n = w.tokens_per_frame
+    timed = []
     try:
         t0 = time.perf_counter()
         st = oracle.linear_states(inp["k"], inp["v"], inp["text_k"], inp["text_v"], lay)
         t_states = time.perf_counter() - t0
-        per = 256
-        tok = sample_tokens(w, per_frame=per)
-        t0 = time.perf_counter()
-        o_s = oracle.softmax_branch(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], lay, tokens=tok)
-        o_l = oracle.linear_branch(inp["q"], st, lay, tokens=tok)
-        oracle.epilogue(inp["x"][:, tok], o_s, o_l, inp["w_gs"], inp["w_gl"], inp["w_os"], inp["w_ol"],
-                        inp["rms_w"])
-        t_rows = time.perf_counter() - t0
+        t_frames = 0.0
+        for size, frames in sorted(classes.items(), reverse=True):
+            f = frames[len(frames) // 2]
+            tok = np.arange(f * n, (f + 1) * n)
+            t0 = time.perf_counter()
+            o_s = oracle.softmax_branch(inp["q"], inp["k"], inp["v"], inp["text_k"], inp["text_v"], lay, tokens=tok)
+            o_l = oracle.linear_branch(inp["q"], st, lay, tokens=tok)
+            oracle.epilogue(inp["x"][:, tok], o_s, o_l, inp["w_gs"], inp["w_gl"], inp["w_os"], inp["w_ol"],
+                            inp["rms_w"])
+            dt = time.perf_counter() - t0
+            t_frames += dt * len(frames)
+            timed.append((f, size, len(frames), dt))
     finally:
         if ctx is not None:
             ctx.__exit__(None, None, None)
-    n_s = len(tok)
-    full = t_states + t_rows * (w.n_video / n_s)
+    full = t_states + t_frames
     info = host_info()
+    parts = ", ".join("frame %d (%d key frames, stands for %d frames): %.1f s" % t for t in timed)
     return {"value": w.batch * w.n_video / full / 1e6, "unit": "Mtokens/s", "cores": cores, "kind": "oracle",
             "cpu_model": info["cpu_model"], "blas": info["blas"],
-            "sample": ("fp64 NumPy oracle: full per-frame state build over all %d tokens (%.1f s) + softmax, "
-                       "readout and epilogue for %d sampled query tokens (%.1f s), per-token part scaled "
-                       "linearly to all %d tokens" % (w.n_video, t_states, n_s, t_rows, w.n_video)),
-            "wall_s": round(t_states + t_rows, 2)}
+            "sample": ("fp64 NumPy oracle: state build over all %d tokens (%.1f s), then softmax branch, readout "
+                       "and epilogue over every token of one frame per key-set size (%s), each scaled by the "
+                       "number of frames of that size: %.0f s for the whole layer"
+                       % (w.n_video, t_states, parts, full)),
+            "wall_s": round(t_states + sum(t[3] for t in timed), 2)}
 
 
 def device_info(torch):
