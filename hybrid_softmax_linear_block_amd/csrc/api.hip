@@ -76,16 +76,29 @@ hyb::Dims make_dims(const hyb_layout* L) {
   return d;
 }
 
-// State-build split: enough workgroups to fill the chip, >= 256 tokens each.
+// State-build split.  Each split of a frame (and of the text) is one
+// workgroup; two run per CU, 512 on the chip at once.  The time is about
+// (rounds of 512 workgroups) x (bytes one workgroup moves: its keys and
+// values read, its partial state written), so take the split that minimises
+// that product (the smaller split on a tie: fewer partials for the scan).
 void state_split(const hyb::Dims& d, int* split, int* ts, int* tsplit) {
   const long long tiles = (d.n + 63) / 64;
-  long long want = (1024 + (long long)d.B * d.H * d.T - 1) / ((long long)d.B * d.H * d.T);
-  long long cap = (d.n + 255) / 256;
-  if (want > cap) want = cap;
-  if (want < 1) want = 1;
-  if (want > tiles) want = tiles;
-  *split = (int)want;
-  *ts = (int)(64 * ((tiles + want - 1) / want));
+  const long long bht = (long long)d.B * d.H * d.T, bh = (long long)d.B * d.H;
+  const long long part_bytes = ((long long)d.D * d.D + d.D) * 4;
+  long long best_cost = -1;
+  int best = 1;
+  for (int sp = 1; sp <= 16 && sp <= tiles; ++sp) {
+    const long long tss = 64 * ((tiles + sp - 1) / sp);
+    const long long tsp = d.L > 0 ? (d.L + tss - 1) / tss : 0;
+    const long long rounds = (bht * sp + bh * tsp + 511) / 512;
+    const long long cost = rounds * (tss * 4 * d.D + part_bytes);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = sp;
+    }
+  }
+  *split = best;
+  *ts = (int)(64 * ((tiles + best - 1) / best));
   *tsplit = d.L > 0 ? (int)((d.L + *ts - 1) / *ts) : 0;
 }
 

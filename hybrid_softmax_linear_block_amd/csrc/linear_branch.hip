@@ -174,11 +174,79 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 // S^T[e][d], element >= D*D is z[d].  F(f) always starts at the first interior
 // frame and B(f) always ends at the last, so the forward sums are exclusive
 // prefixes and the backward sums exclusive suffixes over the interior frames.
-// Pass 1 (frames ascending) writes the prefix part; pass 2 (descending) adds
-// text and suffix and emits comb = hi + lo bf16 pair (transposed [e][d]) and
-// z_comb in fp32.
-template <int D>
+// Pass 1 (frames ascending) keeps each frame's forward part in registers
+// (frame index static, at most TMAX frames); pass 2 (descending) adds the
+// text and the backward part and emits comb = hi + lo bf16 pair (transposed
+// [e][d]) and z_comb in fp32.  The per-frame states are the sums of their
+// split partials, read again in pass 2 (from L2).
+template <int D, int TMAX>
 __global__ __launch_bounds__(256) void k_scan_bf16(Dims d, const float* __restrict__ part, int split, int tsplit,
+                                                   int slots, bf16_t* __restrict__ chi, bf16_t* __restrict__ clo,
+                                                   float* __restrict__ cz) {
+  constexpr int E = D * D + D;
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long long)d.B * d.H * E) return;
+  const int el = (int)(gid % E);
+  const long long bh = gid / E;
+  const float* pp = part + bh * slots * (long long)E + el;
+  auto frame_state = [&](int g) {
+    float s = 0.f;
+    for (int p = 0; p < split; ++p) s += pp[(long long)(g * split + p) * E];
+    return s;
+  };
+  float text = 0.f;
+  for (int p = 0; p < tsplit; ++p) text += pp[(long long)(d.T * split + p) * E];
+
+  const int i0 = interior_begin(d.g), i1 = interior_end(d.g);
+  float fw[TMAX];
+  {
+    float P = 0.f;
+    int gp = i0;
+#pragma unroll
+    for (int f = 0; f < TMAX; ++f) {
+      fw[f] = 0.f;
+      if (f < d.T) {
+        int flo, fhi, blo, bhi;
+        linear_ranges(d.g, f, &flo, &fhi, &blo, &bhi);
+        if (fhi > flo) {
+          while (gp < fhi) { P += frame_state(gp); ++gp; }
+          fw[f] = P;
+        }
+      }
+    }
+  }
+  {
+    float Q = 0.f;
+    int gp = i1;
+#pragma unroll
+    for (int f = TMAX - 1; f >= 0; --f) {
+      if (f < d.T) {
+        int flo, fhi, blo, bhi;
+        linear_ranges(d.g, f, &flo, &fhi, &blo, &bhi);
+        float val = text + fw[f];
+        if (bhi > blo) {
+          while (gp > blo) { --gp; Q += frame_state(gp); }
+          val += Q;
+        }
+        const long long fo = bh * d.T + f;
+        if (el < D * D) {
+          const bf16_t hi = f32_to_bf16(val);
+          const float rem = val - bf16_to_f32(hi);
+          chi[fo * D * D + el] = hi;
+          clo[fo * D * D + el] = f32_to_bf16(rem);
+        } else {
+          cz[fo * D + (el - D * D)] = val;
+        }
+      }
+    }
+  }
+}
+
+// The same scan for layouts with more frames than the register form covers:
+// pass 1 writes the forward part of every frame to the workspace (pre),
+// pass 2 reads it back.
+template <int D>
+__global__ __launch_bounds__(256) void k_scan_pre_bf16(Dims d, const float* __restrict__ part, int split, int tsplit,
                                                    int slots, float* __restrict__ pre, bf16_t* __restrict__ chi,
                                                    bf16_t* __restrict__ clo, float* __restrict__ cz) {
   constexpr int E = D * D + D;
@@ -243,7 +311,8 @@ __global__ __launch_bounds__(256) void k_scan_bf16(Dims d, const float* __restri
 // hi + lo in registers; three MFMAs per step (hi*hi, hi*lo, lo*hi) keep the
 // product near fp32 accuracy.  Lane = one token; the normaliser
 // phi(q).z + eps is a per-lane dot product.  Also emits sum_e O_l^2 per
-// (token, head) for the RMSNorm.
+// (token, head) for the RMSNorm.  Work items are 512-token tiles of one
+// (b, h, frame).
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2))) void k_readout_bf16(Dims d, Tensor4 q, const bf16_t* __restrict__ chi,
                                                       const bf16_t* __restrict__ clo, const float* __restrict__ cz,
@@ -258,7 +327,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
   const int tiles = (d.n + tt - 1) / tt;
-  int w = blockIdx.x;
+  // XCD-aware order: each XCD runs a contiguous range of (b, h, frame, tile)
+  // items, so the tiles of one frame share one fetch of its state in that
+  // XCD's L2
+  int w = (int)xcd_remap(blockIdx.x, gridDim.x);
   const int tile = w % tiles; w /= tiles;
   const int f = w % d.T; w /= d.T;
   const int h = w % d.H;
@@ -274,16 +346,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   __syncthreads();
 
   const int p_end = min(d.n, (tile + 1) * tt);
+  // q rows of the next 32 tokens are loaded while the current ones are
+  // multiplied (the loop is bound by load latency otherwise)
+  auto load_q = [&](int pb, uint4 (&u)[KS]) {
+    const int pq = min(pb + l32, p_end - 1);
+    const bf16_t* qp = (const bf16_t*)q.p + tok_off(q, b, (long long)f * d.n + pq, h) + 8 * half;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) u[s] = ldg16(qp + 16 * s);
+  };
+  uint4 qr[KS];
+  if (tile * tt + wave * 32 < p_end) load_q(tile * tt + wave * 32, qr);
   for (int p0 = tile * tt + wave * 32; p0 < p_end; p0 += 4 * 32) {
     const int p = p0 + l32;
     const bool ok = p < p_end;
     const long long tok = (long long)f * d.n + (ok ? p : p0);
-    const bf16_t* qp = (const bf16_t*)q.p + tok_off(q, b, tok, h) + 8 * half;
     bf16x8 ph[KS], pl[KS];
     float den = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const uint4 u = ldg16(qp + 16 * s);
+      const uint4 u = qr[s];
       const uint32_t* uu = (const uint32_t*)&u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -299,6 +380,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
         pl[s][2 * i + 1] = static_cast<__bf16>(a1 - static_cast<float>(h1));
       }
     }
+    if (p0 + 4 * 32 < p_end) load_q(p0 + 4 * 32, qr);
     den += __shfl_xor(den, 32);
     const float inv = 1.f / (den + eps);
     float sq = 0.f;
@@ -343,16 +425,30 @@ hipError_t launch_states_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, int TMAX>
+static void launch_scan_t(const Dims& d, const Bf16Args& a, unsigned grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_scan_bf16<D, TMAX>), dim3(grid), dim3(256), 0, s, d, a.part, a.state_split, a.text_split,
+                     a.state_slots, a.comb_hi, a.comb_lo, a.comb_z);
+}
+
 hipError_t launch_scan_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
   const long long E = (long long)d.D * d.D + d.D;
   const long long n = (long long)d.B * d.H * E;
   const unsigned grid = (unsigned)((n + 255) / 256);
-  if (d.D == 128)
-    hipLaunchKernelGGL(k_scan_bf16<128>, dim3(grid), dim3(256), 0, s, d, a.part, a.state_split, a.text_split,
+  // the frame count bounds the unrolled per-frame registers of pass 1
+  if (d.T <= 16) {
+    if (d.D == 128) launch_scan_t<128, 16>(d, a, grid, s); else launch_scan_t<64, 16>(d, a, grid, s);
+  } else if (d.T <= 32) {
+    if (d.D == 128) launch_scan_t<128, 32>(d, a, grid, s); else launch_scan_t<64, 32>(d, a, grid, s);
+  } else if (d.T <= 64) {
+    if (d.D == 128) launch_scan_t<128, 64>(d, a, grid, s); else launch_scan_t<64, 64>(d, a, grid, s);
+  } else if (d.D == 128) {
+    hipLaunchKernelGGL(k_scan_pre_bf16<128>, dim3(grid), dim3(256), 0, s, d, a.part, a.state_split, a.text_split,
                        a.state_slots, a.pre, a.comb_hi, a.comb_lo, a.comb_z);
-  else
-    hipLaunchKernelGGL(k_scan_bf16<64>, dim3(grid), dim3(256), 0, s, d, a.part, a.state_split, a.text_split,
+  } else {
+    hipLaunchKernelGGL(k_scan_pre_bf16<64>, dim3(grid), dim3(256), 0, s, d, a.part, a.state_split, a.text_split,
                        a.state_slots, a.pre, a.comb_hi, a.comb_lo, a.comb_z);
+  }
   return hipGetLastError();
 }
 

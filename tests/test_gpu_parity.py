@@ -79,6 +79,10 @@ EDGE = [
     Workload("two-frames", 1, 2, 64, 3, 1, 64, seed=36),
     Workload("ragged-f32", 1, 5, 50, 7, 2, 64, act="f32", soft="f32", seed=37),
     Workload("f32-d128", 1, 4, 33, 9, 1, 128, act="f32", soft="f32", chunk_frames=2, seed=38),
+    # frame counts past the scan's 16- and 32-frame register forms, and past
+    # 64 (the scan's workspace-prefix form)
+    Workload("frames-40-chunk3", 1, 40, 32, 16, 2, 64, chunk_frames=3, seed=39),
+    Workload("frames-70", 1, 70, 16, 8, 2, 128, seed=40),
 ]
 
 
