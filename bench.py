@@ -307,6 +307,32 @@ def cpu_baseline(w, inp):
             "wall_s": round(t_states + sum(t[3] for t in timed), 2)}
 
 
+def library_gemms(w, torch, reps=10):
+    """torch.matmul (hipBLASLt) on the gate GEMM's shape (x [M, hid] @ [hid, 2 hid], bf16) and the output
+    GEMM's ([M, 2 hid] @ [2 hid, hid], fp16), random normal operands, no epilogue: the library reference for
+    the two epilogue GEMMs, timed with events on torch's stream."""
+    M, hid = w.batch * w.n_video, w.heads * w.head_dim
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    res = {}
+    for name, (k, n, dt) in {"gate": (hid, 2 * hid, torch.bfloat16), "out": (2 * hid, hid, torch.float16)}.items():
+        a = torch.randn(M, k, device="cuda", generator=g).to(dt)
+        b = (torch.randn(k, n, device="cuda", generator=g) * 0.02).to(dt).contiguous()
+        for _ in range(3):
+            torch.matmul(a, b)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) / reps, 4)
+        del a, b
+    res["note"] = "torch.matmul (hipBLASLt), same shapes and dtypes, no epilogue, %d launches" % reps
+    return res
+
+
 def device_info(torch):
     """Name, CU count and peak shader clock of device 0 (the peaks above are
     MI355X's published figures: 256 CUs at 2.4 GHz)."""
@@ -433,6 +459,9 @@ def main():
                     help="only time the fp64 oracle over every token of --workload (host only) and print JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--library-gemms", action="store_true",
+                    help="also time torch.matmul (hipBLASLt) on the gate and output GEMM shapes, without "
+                         "epilogues, in the same process (reported as library_gemm_ms)")
     ap.add_argument("--write-traffic", metavar="PMC_DIR",
                     help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE passes under PMC_DIR (subdirectories fetch, "
                          "write, cfetch, cwrite) into profiles/traffic_<kernel>_<workload>.json and exit")
@@ -562,6 +591,8 @@ def main():
                      "frac": round(soft_tflops / peak, 4), "traffic": traffic_for(soft_key, w.name),
                      "flop_per_launch": wc["softmax_flop"]},
     }
+    if args.library_gemms and w.act != "f32":
+        out["library_gemm_ms"] = library_gemms(w, torch)
     if not args.no_cpu_baseline and w.act != "f32":
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inp)

@@ -43,7 +43,11 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  // one packed round-to-nearest-even conversion
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 template <typename T> struct Elem;
@@ -60,6 +64,10 @@ template <> struct Elem<bf16_t> {
 __device__ __forceinline__ float phi_f(float u) { return u > 0.f ? u + 1.f : __expf(u); }
 
 __device__ __forceinline__ float sigmoid_f(float u) { return 1.f / (1.f + __expf(-u)); }
+// The same with the hardware reciprocal (v_rcp_f32, within 1 ulp) in place of
+// the IEEE division: 4 vector instructions instead of about 14.  Exact at
+// u = 0 (1/2), 0 for u -> -inf, 1 for u -> +inf.
+__device__ __forceinline__ float sigmoid_rcp(float u) { return __builtin_amdgcn_rcpf(1.f + __expf(-u)); }
 
 __device__ __forceinline__ long long tok_off(const Tensor4& t, int b, long long tok, int h) {
   return (long long)b * t.sb + tok * t.st + (long long)h * t.sh;

@@ -71,6 +71,267 @@ __device__ __forceinline__ float gelu_tanh_f(float u) {
   return 0.5f * u * (1.f + t);
 }
 
+// Row-layout epilogue of the gate GEMM (EPI_GATE, bf16 operands) and of the
+// output / residual GEMMs (EPI_OUT, EPI_RES).  In the MFMA layout a lane owns
+// one token and 16 features in four 16-byte pieces, so every global access
+// of the epilogue would touch 32 rows (32 cache lines, 16 bytes of each).
+// Instead each wave passes its accumulators (gates for EPI_GATE) through a
+// private LDS region, one group of 32 tokens at a time, and reads them back
+// so that 32 lanes cover one token's 128 features: every global load and
+// store then covers two whole rows of 256 bytes.  All loads of a group are
+// issued before its stores.  Region: 32 rows of 128
+// floats plus 4 of padding (conflict-free writes of 16 lanes at one column
+// and reads of 16 lanes along one row).  The operand stages are free here:
+// the main loop ended on a barrier after every wave's last LDS read.
+constexpr int EPI_ROW = 132;                       // floats per LDS row
+constexpr int EPI_WAVE_BYTES = 32 * EPI_ROW * 4;  // LDS bytes per wave
+
+template <int WTM, int WFN, int EPI>
+__device__ __forceinline__ void epilogue_rows(const GemmArgs& g, floatx16 (&acc)[WFN][WTM], long long mw, int nwave,
+                                              int lane, float* ldsw) {
+  static_assert(WFN == 4, "row epilogue: 128 features per wave");
+  const int l32 = lane & 31, half = lane >> 5;
+  const int lc = l32, lr = half;  // row layout: features 4 lc .. 4 lc + 3 of row 2 k + lr
+  const bool lin = EPI == EPI_GATE && nwave >= g.hid;  // a wave's features are all in one half (hid % BN == 0)
+  // Source rows (branch output or residual) and destination rows: a
+  // wave-uniform row base (mw + 2 k + 32 i) plus a fixed 32-bit lane offset
+  const uint16_t* src;
+  long long lds_, ldd;  // row strides of source and destination (elements)
+  int scol;             // this lane's first source column
+  if constexpr (EPI == EPI_GATE) {
+    src = lin ? g.ol : g.os;
+    lds_ = g.hid;
+    ldd = 2LL * g.hid;
+    scol = (lin ? nwave - g.hid : nwave) + 4 * lc;
+  } else {
+    src = (const uint16_t*)g.x;
+    lds_ = ldd = g.N;
+    scol = nwave + 4 * lc;
+  }
+  const int dcol = nwave + 4 * lc;
+  const unsigned soff = (unsigned)((lr * lds_ + scol) * 2), doff = (unsigned)((lr * ldd + dcol) * 2);
+  float4 wf = make_float4(0.f, 0.f, 0.f, 0.f);
+  float rv = 0.f;
+  if (lin) {
+    const uint2 w = *(const uint2*)(g.rmsw + scol);
+    wf = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                     __uint_as_float(w.y & 0xffff0000u));
+    rv = g.rinv[min(mw + lane, g.M - 1)];  // token mw + lane; row r's factor sits in lane r
+  }
+  // FULL: every row of the wave is below M (all tiles but the last row of
+  // tiles); otherwise rows past M load row M - 1 and are not stored.
+  auto run = [&](auto full_c, auto extra_c) {
+    constexpr bool FULL = decltype(full_c)::value, EXTRA = decltype(extra_c)::value;
+    auto saddr = [&](int i, int k) -> const char* {
+      if constexpr (FULL) return (const char*)src + (mw + 32 * i + 2 * k) * lds_ * 2 + soff;
+      else return (const char*)src + (min(mw + 32 * i + 2 * k + lr, g.M - 1) * lds_ + scol) * 2;
+    };
+    uint2 in[WTM][16];
+    auto load_in = [&](int i) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) in[i][k] = *(const uint2*)saddr(i, k);
+    };
+    load_in(0);
+#pragma unroll
+    for (int i = 0; i < WTM; ++i) {
+      // MFMA layout -> LDS: token l32, features 32 f + 8 jg + 4 half
+#pragma unroll
+      for (int f = 0; f < WFN; ++f)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          float4 v = make_float4(acc[f][i][4 * jg], acc[f][i][4 * jg + 1], acc[f][i][4 * jg + 2], acc[f][i][4 * jg + 3]);
+          if constexpr (EPI == EPI_GATE) v = make_float4(sigmoid_rcp(v.x), sigmoid_rcp(v.y), sigmoid_rcp(v.z), sigmoid_rcp(v.w));
+          *(float4*)&ldsw[l32 * EPI_ROW + 32 * f + 8 * jg + 4 * half] = v;
+        }
+      if (i + 1 < WTM) load_in(i + 1);
+      // LDS -> row layout.  A wave's LDS operations execute in issue order, so
+      // these reads see the writes above and the next group's writes follow
+      // them; the empty asm keeps the compiler from reordering across lanes.
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int r = 2 * k + lr;
+        const float4 a = *(const float4*)&ldsw[r * EPI_ROW + 4 * lc];
+        float rk = 0.f;
+        if (lin) rk = __shfl(rv, 32 * i + r);
+        const long long m = mw + 32 * i + r;
+        if constexpr (!FULL) {
+          if (m >= g.M) continue;
+        }
+        char* drow = nullptr;
+        if constexpr (EPI == EPI_GATE) drow = (char*)g.ap;
+        else drow = (char*)g.y;
+        drow += (mw + 32 * i + 2 * k) * ldd * 2 + doff;
+        if constexpr (EPI == EPI_GATE) {
+          // fp16 operands enter the products directly (fma with a zero addend:
+          // one rounding, as product of the widened value)
+          typedef __attribute__((ext_vector_type(2))) _Float16 h2_t;
+          const h2_t o01 = __builtin_bit_cast(h2_t, in[i][k].x), o23 = __builtin_bit_cast(h2_t, in[i][k].y);
+          if (lin) {  // A'_l = G_l RMSNorm(O_l), RMSNorm(O_l) = O_l w / rms; saturated to fp16
+            const float v0 = __builtin_fmaf((float)o01[0], wf.x, 0.f) * rk, v1 = __builtin_fmaf((float)o01[1], wf.y, 0.f) * rk;
+            const float v2 = __builtin_fmaf((float)o23[0], wf.z, 0.f) * rk, v3 = __builtin_fmaf((float)o23[1], wf.w, 0.f) * rk;
+            *(uint2*)drow = make_uint2(pack_f16x2(a.x * v0, a.y * v1), pack_f16x2(a.z * v2, a.w * v3));
+          } else {  // A'_s = G_s O_s: |G_s O_s| <= |O_s|, inside fp16's range
+            *(uint2*)drow = make_uint2(pack_f16x2_unsat(__builtin_fmaf((float)o01[0], a.x, 0.f), __builtin_fmaf((float)o01[1], a.y, 0.f)),
+                                       pack_f16x2_unsat(__builtin_fmaf((float)o23[0], a.z, 0.f), __builtin_fmaf((float)o23[1], a.w, 0.f)));
+          }
+          if constexpr (EXTRA) {
+            const long long n = m * ldd + dcol;
+            if (g.gates_dbg) *(float4*)(g.gates_dbg + n) = a;
+            if (g.gates16) store_f16x4(g.gates16 + n, a.x, a.y, a.z, a.w);
+          }
+        } else {
+          const uint2 x = in[i][k];
+          *(uint2*)drow = make_uint2(pack_bf16x2(__uint_as_float(x.x << 16) + a.x, __uint_as_float(x.x & 0xffff0000u) + a.y),
+                                     pack_bf16x2(__uint_as_float(x.y << 16) + a.z, __uint_as_float(x.y & 0xffff0000u) + a.w));
+          if constexpr (EXTRA) *(float4*)(g.delta_dbg + m * ldd + dcol) = a;
+        }
+      }
+      asm volatile("" ::: "memory");
+    }
+  };
+  const bool full = mw + 32 * WTM <= g.M;
+  const bool extra = EPI == EPI_GATE ? (g.gates_dbg || g.gates16) : g.delta_dbg != nullptr;
+  if (full && !extra) run(std::true_type{}, std::false_type{});
+  else if (full) run(std::true_type{}, std::true_type{});
+  else if (!extra) run(std::false_type{}, std::false_type{});
+  else run(std::false_type{}, std::true_type{});
+}
+
+// Epilogue of the gate GEMM (EPI_GATE) and of the output / residual GEMMs
+// (EPI_OUT, EPI_RES).  Lane owns tokens mb + 32 i (i < WTM) and features
+// nw + 32 f + 8 jg + 0..3 (f < WFN, jg < 4); nwave is the wave's first
+// feature (wave-uniform).  Every global load of the tile (branch outputs or
+// residual rows, RMS weights and factors) is issued before the first store,
+// so the epilogue costs one memory round trip (the MX gate, short of
+// registers, does so per token group i); rows past M load the last row and
+// are not stored.
+template <int WTM, int WFN, int EPI, bool MX>
+__device__ __forceinline__ void epilogue_gate_out(const GemmArgs& g, floatx16 (&acc)[WFN][WTM], long long mb, int nwave,
+                                                  int half) {
+  const int nw = nwave + 4 * half;
+  long long mc[WTM];
+#pragma unroll
+  for (int i = 0; i < WTM; ++i) mc[i] = min(mb + 32 * i, g.M - 1);
+  if constexpr (EPI == EPI_GATE) {
+    const bool lin = nwave >= g.hid;  // a wave's features are all in one half (hid % BN == 0)
+    const uint16_t* src = lin ? g.ol : g.os;
+    const int cw = (lin ? nwave - g.hid : nwave) + 4 * half;  // this lane's first column in [0, hid)
+    uint2 ov[WTM][WFN][4];  // fp16 branch outputs
+    uint2 wv[WFN][4];       // bf16 RMS weights (linear half)
+    float rinv[WTM];
+    auto load_w = [&]() {
+#pragma unroll
+      for (int f = 0; f < WFN; ++f)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) wv[f][jg] = *(const uint2*)(g.rmsw + cw + 32 * f + 8 * jg);
+    };
+    auto load_i = [&](int i) {
+#pragma unroll
+      for (int f = 0; f < WFN; ++f)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) ov[i][f][jg] = *(const uint2*)(src + mc[i] * g.hid + cw + 32 * f + 8 * jg);
+      if (lin) {
+        rinv[i] = g.rinv[mc[i]];
+        if constexpr (MX) load_w();
+      }
+    };
+    if constexpr (!MX) {
+      if (lin) load_w();
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) load_i(i);
+    }
+    // the debug / saved-gate stores only in a separate copy of the loop (the
+    // MX gate keeps one copy: two spill its registers)
+    auto gate_out = [&](auto extra_c) {
+      constexpr bool EXTRA = decltype(extra_c)::value;
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) {
+        if constexpr (MX) load_i(i);
+        const long long m = mb + 32 * i;
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int f = 0; f < WFN; ++f) {
+          float4 av[4];
+          float amax = 0.f;
+#pragma unroll
+          for (int jg = 0; jg < 4; ++jg) {
+            const int n = nw + 32 * f + 8 * jg;
+            float4 o = unpack_f16x4(ov[i][f][jg]);
+            if (lin) {  // RMSNorm(O_l) = O_l w / rms
+              const uint2 w = wv[f][jg];
+              o.x = o.x * __uint_as_float(w.x << 16) * rinv[i];
+              o.y = o.y * __uint_as_float(w.x & 0xffff0000u) * rinv[i];
+              o.z = o.z * __uint_as_float(w.y << 16) * rinv[i];
+              o.w = o.w * __uint_as_float(w.y & 0xffff0000u) * rinv[i];
+            }
+            const float g0 = sigmoid_rcp(acc[f][i][4 * jg]), g1 = sigmoid_rcp(acc[f][i][4 * jg + 1]);
+            const float g2 = sigmoid_rcp(acc[f][i][4 * jg + 2]), g3 = sigmoid_rcp(acc[f][i][4 * jg + 3]);
+            av[jg] = make_float4(g0 * o.x, g1 * o.y, g2 * o.z, g3 * o.w);
+            if constexpr (MX) {
+              amax = fmaxf(amax, fmaxf(fmaxf(fabsf(av[jg].x), fabsf(av[jg].y)), fmaxf(fabsf(av[jg].z), fabsf(av[jg].w))));
+            } else {
+              *(uint2*)(g.ap + m * (2LL * g.hid) + n) = make_uint2(pack_f16x2(av[jg].x, av[jg].y),
+                                                                   pack_f16x2(av[jg].z, av[jg].w));
+            }
+            if constexpr (EXTRA) {
+              if (g.gates_dbg) *(float4*)(g.gates_dbg + m * (2LL * g.hid) + n) = make_float4(g0, g1, g2, g3);
+              if (g.gates16) store_f16x4(g.gates16 + m * (2LL * g.hid) + n, g0, g1, g2, g3);
+            }
+          }
+          if constexpr (MX) {
+            // A' as MX e4m3: the 32 features of block f of this token sit in
+            // lanes l and l ^ 32 (4 groups of 4 each)
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            const int se = mx_exponent(amax);
+            const float inv = mx_inverse_scale(se);
+            const int nb = nwave + 32 * f;  // first feature of the block
+            uint8_t* cp = g.ap8 + m * (2LL * g.hid) + nw + 32 * f;
+#pragma unroll
+            for (int jg = 0; jg < 4; ++jg)
+              *(uint32_t*)(cp + 8 * jg) = e4m3x4(av[jg].x * inv, av[jg].y * inv, av[jg].z * inv, av[jg].w * inv);
+            if (half == 0) g.aps[((long long)(nb >> 7) * g.mpad + m) * 4 + ((nb >> 5) & 3)] = (uint8_t)(se + 127);
+          }
+        }
+      }
+    };
+    if (MX || g.gates_dbg || g.gates16) gate_out(std::true_type{});
+    else if constexpr (!MX) gate_out(std::false_type{});
+  } else {
+    // y = x + acc (bf16), x the residual rows
+    uint2 xv[WTM][WFN][4];
+#pragma unroll
+    for (int i = 0; i < WTM; ++i)
+#pragma unroll
+      for (int f = 0; f < WFN; ++f)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) xv[i][f][jg] = *(const uint2*)(g.x + mc[i] * g.N + nw + 32 * f + 8 * jg);
+    auto out = [&](auto dbg_c) {
+      constexpr bool DBG = decltype(dbg_c)::value;
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) {
+        const long long m = mb + 32 * i;
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int f = 0; f < WFN; ++f)
+#pragma unroll
+          for (int jg = 0; jg < 4; ++jg) {
+            const int n = nw + 32 * f + 8 * jg;
+            const float c0 = acc[f][i][4 * jg], c1 = acc[f][i][4 * jg + 1];
+            const float c2 = acc[f][i][4 * jg + 2], c3 = acc[f][i][4 * jg + 3];
+            const uint2 x = xv[i][f][jg];
+            *(uint2*)(g.y + m * g.N + n) =
+                make_uint2(pack_bf16x2(__uint_as_float(x.x << 16) + c0, __uint_as_float(x.x & 0xffff0000u) + c1),
+                           pack_bf16x2(__uint_as_float(x.y << 16) + c2, __uint_as_float(x.y & 0xffff0000u) + c3));
+            if constexpr (DBG) *(float4*)(g.delta_dbg + m * g.N + n) = make_float4(c0, c1, c2, c3);
+          }
+      }
+    };
+    if (g.delta_dbg) out(std::true_type{});
+    else out(std::false_type{});
+  }
+}
+
 // WG = WM x WN waves; each wave computes WTM x WFN blocks of 32 x 32 (tokens x
 // features).  BK-deep k-tiles live in an ST-stage LDS ring filled by
 // wave-wide direct-to-LDS loads (1 KB per wave instruction, 16-byte granules
@@ -103,7 +364,11 @@ void k_gemm_bf16(GemmArgs g) {
   constexpr int XBYTES = MX ? (BM + BN) * 4 : 0;            // block exponents of the k-tile's rows
   constexpr int SBYTES = ABYTES + BBYTES + XBYTES;
   using SW = Swz<BK>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[ST * SBYTES / 2];
+  // the row epilogue reuses the operand stages as 8 wave regions
+  constexpr bool ROWEPI = (EPI == EPI_GATE && !MX) || EPI == EPI_OUT || EPI == EPI_RES;
+  constexpr bool USE_ROWEPI = ROWEPI && NWV == 8 && WTM == 2 && WFN == 4;
+  constexpr int LDSB = USE_ROWEPI && 8 * EPI_WAVE_BYTES > ST * SBYTES ? 8 * EPI_WAVE_BYTES : ST * SBYTES;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDSB / 2];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -173,7 +438,7 @@ void k_gemm_bf16(GemmArgs g) {
       if (lane < 16) dma16(xbase + (long long)(kz * (g.K / KT) + kt) * xstride, lane * 16, lb + BBYTES + wave * 256);
     }
   };
-  // one k-tile: all operand reads first, then the MFMAs
+  // MX: one k-tile, all operand reads first, then the MFMAs
   auto mma = [&](auto stc) {
     constexpr int STG = decltype(stc)::value;
     const uint16_t* at = lds + STG * SBYTES / 2;
@@ -218,41 +483,80 @@ void k_gemm_bf16(GemmArgs g) {
                                      (int)(ea[i] >> (16 * ks)));
       return;
     }
-    uint4 ta[BK / 16][WTM], tb[BK / 16][WFN];
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-#pragma unroll
-      for (int i = 0; i < WTM; ++i)
-        ta[ks][i] = *(const uint4*)&at[SW::off(wm * WTM * 32 + i * 32 + l32, 16 * ks + 8 * half)];
-#pragma unroll
-      for (int f = 0; f < WFN; ++f)
-        tb[ks][f] = *(const uint4*)&bt_[SW::off(wn * WFN * 32 + f * 32 + l32, 16 * ks + 8 * half)];
-    }
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks)
-#pragma unroll
-      for (int f = 0; f < WFN; ++f)
-#pragma unroll
-        for (int i = 0; i < WTM; ++i) {
-          if constexpr (EPI == EPI_OUT)  // fp16 operands (A' and W_o)
-            acc[f][i] = mfma32_f16(__builtin_bit_cast(halfx8, tb[ks][f]), __builtin_bit_cast(halfx8, ta[ks][i]),
-                                   acc[f][i]);
-          else
-            acc[f][i] = mfma32(__builtin_bit_cast(bf16x8, tb[ks][f]), __builtin_bit_cast(bf16x8, ta[ks][i]), acc[f][i]);
-        }
   };
 
   const int nk = g.K / KT;
+  // bf16 / fp16 operands: the k-steps of a k-tile read their operands into
+  // registers that persist across k-tiles, so that the last k-step's MFMAs
+  // run after the barrier, while the first k-step of the next k-tile is read.
+  // Each k-step's WTM x WFN MFMAs are interleaved with the memory operations
+  // (one DMA chunk and one operand read after each MFMA, round robin): the
+  // matrix pipe keeps busy while they issue.
+  constexpr int KS = BK / 16, NSL = WTM * WFN, NR = WTM + WFN;
+  uint4 ra[KS][WTM], rb[KS][WFN];
+  auto rd1 = [&](int stage, auto ksc, int j) {  // operand row block j (A: j < WTM, B: j >= WTM)
+    constexpr int ks = decltype(ksc)::value;
+    const uint16_t* at = lds + stage * (SBYTES / 2);
+    if (j < WTM) ra[ks][j] = *(const uint4*)&at[SW::off(wm * WTM * 32 + j * 32 + l32, 16 * ks + 8 * half)];
+    else rb[ks][j - WTM] = *(const uint4*)&at[ABYTES / 2 + SW::off(wn * WFN * 32 + (j - WTM) * 32 + l32, 16 * ks + 8 * half)];
+  };
+  auto dma1 = [&](int kt2, int stage, int j) {  // 1 KB chunk j of k-tile kt2 (A: j < CA, B: j >= CA)
+    const unsigned la = lds0 + stage * SBYTES;
+    if (j < CA) dma16(abase + (long long)kt2 * BK * 2, aoff[j], la + (wave * CA + j) * 1024);
+    else dma16(bbase + (long long)kt2 * BK * 2, boff[j - CA], la + ABYTES + (wave * CB + j - CA) * 1024);
+  };
+  // k-step ks: MFMA s (s = f * WTM + i) is followed by ops(s)
+  auto phase = [&](auto ksc, auto&& ops) {
+    constexpr int ks = decltype(ksc)::value;
+#pragma unroll
+    for (int f = 0; f < WFN; ++f)
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) {
+        if constexpr (EPI == EPI_OUT)  // fp16 operands (A' and W_o)
+          acc[f][i] = mfma32_f16(__builtin_bit_cast(halfx8, rb[ks][f]), __builtin_bit_cast(halfx8, ra[ks][i]), acc[f][i]);
+        else
+          acc[f][i] = mfma32(__builtin_bit_cast(bf16x8, rb[ks][f]), __builtin_bit_cast(bf16x8, ra[ks][i]), acc[f][i]);
+        __builtin_amdgcn_sched_barrier(0);
+        ops(f * WTM + i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
   // k-tile kt in stage STG: issue k-tile kt + ST - 1 into the stage read at
   // kt - 1 (free after the previous barrier), multiply, wait for kt + 1.
   auto step = [&](int kt, auto stc) {
     constexpr int STG = decltype(stc)::value;
     const bool more = kt + ST - 1 < nk;
-    if (more) issue(kt + ST - 1, (STG + ST - 1) % ST);
-    mma(stc);
+    if constexpr (MX) {
+      if (more) issue(kt + ST - 1, (STG + ST - 1) % ST);
+      mma(stc);
+    } else {
+      // k-steps 0 .. KS-2 before the barrier, reading k-steps 1 .. KS-1
+      // (k-step 0 was read after the previous barrier); the DMA of k-tile
+      // kt + ST - 1 goes with k-step 0
+      static_for<0, KS - 1>([&](auto ksc) {
+        constexpr int ks = decltype(ksc)::value;
+        phase(ksc, [&](int sl) {
+          if constexpr (ks == 0) {
+#pragma unroll
+            for (int j = sl; j < CA + CB; j += NSL)
+              if (more) dma1(kt + ST - 1, (STG + ST - 1) % ST, j);
+          }
+#pragma unroll
+          for (int j = sl; j < NR; j += NSL) rd1(STG, std::integral_constant<int, ks + 1>{}, j);
+        });
+      });
+    }
     if (more) wait_vmcnt<(ST - 2) * LPT>();  // k-tile kt+1 landed; later ones may stay in flight
     else wait_vmcnt<0>();
-    tile_barrier();
+    tile_barrier();  // every wave's reads of this stage are done, k-tile kt+1 is visible
+    if constexpr (!MX) {
+      const bool nxt = kt + 1 < nk;
+      phase(std::integral_constant<int, KS - 1>{}, [&](int sl) {
+#pragma unroll
+        for (int j = sl; j < NR; j += NSL)
+          if (nxt) rd1((STG + 1) % ST, std::integral_constant<int, 0>{}, j);
+      });
+    }
   };
 #pragma unroll
   for (int s0 = 0; s0 < ST - 1; ++s0)
@@ -260,6 +564,10 @@ void k_gemm_bf16(GemmArgs g) {
   if (nk >= ST - 1) wait_vmcnt<(ST - 2) * LPT>();
   else wait_vmcnt<0>();
   tile_barrier();
+  if constexpr (!MX) {
+#pragma unroll
+    for (int j = 0; j < NR; ++j) rd1(0, std::integral_constant<int, 0>{}, j);
+  }
   for (int kt = 0; kt < nk; kt += ST) {
     step(kt, std::integral_constant<int, 0>{});
     if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1 % ST>{});
@@ -428,92 +736,11 @@ void k_gemm_bf16(GemmArgs g) {
     }
     return;
   }
-  // ---- epilogue: lane owns token m, features n0' + 8*jg + 4*half + 0..3.
-  // All loads of one token row are issued before its stores.
-#pragma unroll
-  for (int i = 0; i < WTM; ++i) {
-    const long long m = m0 + wm * WTM * 32 + i * 32 + l32;
-    if (m >= g.M) continue;
-    const int nw = n0 + wn * WFN * 32 + 4 * half;  // + 32 f + 8 jg
-    if constexpr (EPI == EPI_GATE) {
-      float4 val[WFN][4];
-      const bool lin = nw >= g.hid;  // a wave's features are all in one half (hid % BN == 0)
-      if (!lin) {
-#pragma unroll
-        for (int f = 0; f < WFN; ++f)
-#pragma unroll
-          for (int jg = 0; jg < 4; ++jg) val[f][jg] = load_f16x4(g.os + m * g.hid + nw + 32 * f + 8 * jg);
-      } else {
-        const float rinv = g.rinv[m];
-#pragma unroll
-        for (int f = 0; f < WFN; ++f)
-#pragma unroll
-          for (int jg = 0; jg < 4; ++jg) {
-            const int c = nw - g.hid + 32 * f + 8 * jg;
-            const float4 o = load_f16x4(g.ol + m * g.hid + c);
-            const uint2 wv = *(const uint2*)(g.rmsw + c);
-            val[f][jg].x = o.x * __uint_as_float(wv.x << 16) * rinv;
-            val[f][jg].y = o.y * __uint_as_float(wv.x & 0xffff0000u) * rinv;
-            val[f][jg].z = o.z * __uint_as_float(wv.y << 16) * rinv;
-            val[f][jg].w = o.w * __uint_as_float(wv.y & 0xffff0000u) * rinv;
-          }
-      }
-#pragma unroll
-      for (int f = 0; f < WFN; ++f) {
-        float4 av[4];
-        float amax = 0.f;
-#pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          const int n = nw + 32 * f + 8 * jg;
-          const float g0 = sigmoid_f(acc[f][i][4 * jg]), g1 = sigmoid_f(acc[f][i][4 * jg + 1]);
-          const float g2 = sigmoid_f(acc[f][i][4 * jg + 2]), g3 = sigmoid_f(acc[f][i][4 * jg + 3]);
-          av[jg] = make_float4(g0 * val[f][jg].x, g1 * val[f][jg].y, g2 * val[f][jg].z, g3 * val[f][jg].w);
-          if constexpr (MX) {
-            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(av[jg].x), fabsf(av[jg].y)), fmaxf(fabsf(av[jg].z), fabsf(av[jg].w))));
-          } else {
-            uint2 st;
-            st.x = pack_f16x2(av[jg].x, av[jg].y);
-            st.y = pack_f16x2(av[jg].z, av[jg].w);
-            *(uint2*)(g.ap + m * (2LL * g.hid) + n) = st;
-          }
-          if (g.gates_dbg) *(float4*)(g.gates_dbg + m * (2LL * g.hid) + n) = make_float4(g0, g1, g2, g3);
-          if (g.gates16) store_f16x4(g.gates16 + m * (2LL * g.hid) + n, g0, g1, g2, g3);
-        }
-        if constexpr (MX) {
-          // A' as MX e4m3: the 32 features of block f of this token sit in
-          // lanes l and l ^ 32 (4 groups of 4 each)
-          amax = fmaxf(amax, __shfl_xor(amax, 32));
-          const int se = mx_exponent(amax);
-          const float inv = mx_inverse_scale(se);
-          const int nb = nw - 4 * half + 32 * f;  // first feature of the block
-          uint8_t* cp = g.ap8 + m * (2LL * g.hid) + nw + 32 * f;
-#pragma unroll
-          for (int jg = 0; jg < 4; ++jg)
-            *(uint32_t*)(cp + 8 * jg) = e4m3x4(av[jg].x * inv, av[jg].y * inv, av[jg].z * inv, av[jg].w * inv);
-          if (half == 0) g.aps[((long long)(nb >> 7) * g.mpad + m) * 4 + ((nb >> 5) & 3)] = (uint8_t)(se + 127);
-        }
-      }
-    } else {
-      uint2 xv[WFN][4];
-#pragma unroll
-      for (int f = 0; f < WFN; ++f)
-#pragma unroll
-        for (int jg = 0; jg < 4; ++jg) xv[f][jg] = *(const uint2*)(g.x + m * g.N + nw + 32 * f + 8 * jg);
-#pragma unroll
-      for (int f = 0; f < WFN; ++f)
-#pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          const int n = nw + 32 * f + 8 * jg;
-          const float c0 = acc[f][i][4 * jg], c1 = acc[f][i][4 * jg + 1];
-          const float c2 = acc[f][i][4 * jg + 2], c3 = acc[f][i][4 * jg + 3];
-          uint2 st;
-          st.x = pack_bf16x2(__uint_as_float(xv[f][jg].x << 16) + c0, __uint_as_float(xv[f][jg].x & 0xffff0000u) + c1);
-          st.y = pack_bf16x2(__uint_as_float(xv[f][jg].y << 16) + c2, __uint_as_float(xv[f][jg].y & 0xffff0000u) + c3);
-          *(uint2*)(g.y + m * g.N + n) = st;
-          if (g.delta_dbg) *(float4*)(g.delta_dbg + m * g.N + n) = make_float4(c0, c1, c2, c3);
-        }
-    }
-  }
+  if constexpr (USE_ROWEPI)
+    epilogue_rows<WTM, WFN, EPI>(g, acc, m0 + wm * WTM * 32, n0 + wn * WFN * 32, lane,
+                                 (float*)lds + wave * (EPI_WAVE_BYTES / 4));
+  else
+    epilogue_gate_out<WTM, WFN, EPI, MX>(g, acc, m0 + wm * WTM * 32 + l32, n0 + wn * WFN * 32, half);
 }
 
 // Weight transposes into the GEMMs' [N][K] operand layout.

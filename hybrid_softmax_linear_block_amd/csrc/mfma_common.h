@@ -11,6 +11,7 @@
 // and B agree, the kernels pick the key/token order inside each 16-wide k-step
 // to match the register layout the previous MFMA produced.
 #pragma once
+#include <type_traits>
 #include "common.h"
 
 namespace hyb {
@@ -33,19 +34,31 @@ __device__ __forceinline__ uint16_t f32_to_f16_sat(float f) {
 }
 
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  return (uint32_t)f32_to_f16_sat(lo) | ((uint32_t)f32_to_f16_sat(hi) << 16);
+  // clamp to +-65504, then one packed round-to-nearest-even conversion
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+  const f32x2_t v = {fminf(fmaxf(lo, -65504.f), 65504.f), fminf(fmaxf(hi, -65504.f), 65504.f)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
+// The same without the clamp, for values known to lie inside fp16's range.
+__device__ __forceinline__ uint32_t pack_f16x2_unsat(float lo, float hi) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
 
 // Four floats -> four saturated fp16 in one 8-byte store, and back.
 __device__ __forceinline__ void store_f16x4(uint16_t* p, float a, float b, float c, float d) {
   *(uint2*)p = make_uint2(pack_f16x2(a, b), pack_f16x2(c, d));
 }
-__device__ __forceinline__ float4 load_f16x4(const uint16_t* p) {
+__device__ __forceinline__ float4 unpack_f16x4(uint2 u) {
   typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
-  const uint2 u = *(const uint2*)p;
   const half2_t lo = __builtin_bit_cast(half2_t, u.x), hi = __builtin_bit_cast(half2_t, u.y);
   return make_float4((float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]);
 }
+__device__ __forceinline__ float4 load_f16x4(const uint16_t* p) { return unpack_f16x4(*(const uint2*)p); }
 
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 
@@ -76,6 +89,15 @@ struct Swz {
     return row * COLS + ((((col >> 3) ^ key(row))) << 3) + (col & 7);
   }
 };
+
+// Compile-time loop: f(std::integral_constant<int, I>{}) for I = B .. E-1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 __device__ __forceinline__ floatx16 zero16() {
   floatx16 z;
