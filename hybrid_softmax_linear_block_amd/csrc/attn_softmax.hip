@@ -177,6 +177,9 @@ void k_attn_bf16_sp(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4
 
   const int prow = it.qt * BM + wave * 32 + l32;
   const bool row_ok = prow < d.n;
+  // a wave whose 32 rows all lie past the frame's end (the second half of a
+  // frame's last tile when n % BM == 64) only loads tiles and joins barriers
+  const bool idle = it.qt * BM + wave * 32 >= d.n;
   const long long qtok = (long long)it.f * d.n + (row_ok ? prow : 0);
   bf16x8 qf[KS];
   {
@@ -194,8 +197,11 @@ void k_attn_bf16_sp(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4
   wait_vmcnt<0>();
   tile_barrier();
   floatx16 s[KB];
-  qk_tile<D, KB>(s, Ks[0], qf, l32, half);
-  float mx = tile_max<KB>(s, sl2);
+  float mx = 0.f;
+  if (!idle) {
+    qk_tile<D, KB>(s, Ks[0], qf, l32, half);
+    mx = tile_max<KB>(s, sl2);
+  }
   int vcur = valid0;
   tile_barrier();  // K buffer 0 is refilled below
 
@@ -211,6 +217,13 @@ void k_attn_bf16_sp(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4
     }
     ldr.load_v(kwv.vp, kwv.valid(), wave, vs_lds + (BUF ^ 1) * kTileBytes);
     if (kwv.advance()) ldr.set_v(kwv.vs);
+    if (idle) {
+      vcur = vnext;
+      vnext = vk;
+      wait_vmcnt<0>();
+      tile_barrier();
+      return true;
+    }
 
     rescale<DB>(mx, m_run, l_run, oacc);
     if (vcur < BN) mask_tile<KB>(s, vcur, half);
@@ -252,6 +265,7 @@ void k_attn_bf16_sp(Dims d, Tensor4 q, Tensor4 k, Tensor4 v, Tensor4 tk, Tensor4
       break;
     }
   }
+  if (idle) return;
   rescale<DB>(mx, m_run, l_run, oacc);
   if (vcur < BN) mask_tile<KB>(s, vcur, half);
   bf16x8 pf[2 * KB];
