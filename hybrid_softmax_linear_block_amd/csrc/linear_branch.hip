@@ -170,79 +170,108 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 }
 
 // ---------------------------------------------------------------------------
-// Scan across frames.  One thread per (b, h, element); element < D*D is
-// S^T[e][d], element >= D*D is z[d].  F(f) always starts at the first interior
-// frame and B(f) always ends at the last, so the forward sums are exclusive
-// prefixes and the backward sums exclusive suffixes over the interior frames.
-// Pass 1 (frames ascending) keeps each frame's forward part in registers
-// (frame index static, at most TMAX frames); pass 2 (descending) adds the
-// text and the backward part and emits comb = hi + lo bf16 pair (transposed
-// [e][d]) and z_comb in fp32.  The per-frame states are the sums of their
-// split partials, read again in pass 2 (from L2).
-template <int D, int TMAX>
-__global__ __launch_bounds__(256) void k_scan_bf16(Dims d, const float* __restrict__ part, int split, int tsplit,
-                                                   int slots, bf16_t* __restrict__ chi, bf16_t* __restrict__ clo,
-                                                   float* __restrict__ cz) {
-  constexpr int E = D * D + D;
-  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (long long)d.B * d.H * E) return;
-  const int el = (int)(gid % E);
-  const long long bh = gid / E;
-  const float* pp = part + bh * slots * (long long)E + el;
-  auto frame_state = [&](int g) {
-    float s = 0.f;
-    for (int p = 0; p < split; ++p) s += pp[(long long)(g * split + p) * E];
-    return s;
-  };
-  float text = 0.f;
-  for (int p = 0; p < tsplit; ++p) text += pp[(long long)(d.T * split + p) * E];
+// Scan across frames.  F(f) always starts at the first interior frame and
+// B(f) always ends at the last, so with s_g the state of interior frame g
+// (zero outside [i0, i1)):
+//   comb(f) = text + P(fhi(f) - 1) + Q(blo(f)),
+//   P(g) = sum_{j <= g} s_j (inclusive prefix),  Q(g) = sum_{j >= g} s_j (inclusive suffix),
+// each term present only when F(f), B(f) are non-empty.
+//
+// One wave per 64 consecutive state elements of one (b, h) (element < D*D is
+// S^T[e][d], element >= D*D is z[d]).  The frame states (sums of their split
+// partials) are loaded coalesced, lane = element, into a wave-private LDS
+// tile [frame][element]; the scans then run across lanes, lane = frame, as
+// DPP prefix sums over groups of W lanes (W >= T; 64 / W elements per
+// instruction), forward for P and over the reversed frame order for Q; the
+// results go back through LDS so that each output frame is stored lane =
+// element again: comb = hi + lo bf16 pair (transposed [e][d]) and z_comb in
+// fp32.
 
-  const int i0 = interior_begin(d.g), i1 = interior_end(d.g);
-  float fw[TMAX];
-  {
-    float P = 0.f;
-    int gp = i0;
+// Inclusive prefix sum over each group of W consecutive lanes (W = 16, 32,
+// 64): four row shifts inside each 16-lane row, then the row broadcasts of
+// lanes 15 and 31 into the following rows.
+template <int W>
+__device__ __forceinline__ float group_prefix(float x) {
+  static_assert(W == 16 || W == 32 || W == 64, "scan width");
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));  // row_shr:1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));  // row_shr:2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));  // row_shr:4
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));  // row_shr:8
+  if constexpr (W >= 32)  // lane 15 of rows 0 / 2 into rows 1 / 3
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xa, 0xf, false));
+  if constexpr (W == 64)  // lane 31 into rows 2 and 3
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xc, 0xf, false));
+  return x;
+}
+
+template <int D, int W>
+__global__ __launch_bounds__(64) void k_scan_bf16(Dims d, const float* __restrict__ part, int split, int tsplit,
+                                                  int slots, bf16_t* __restrict__ chi, bf16_t* __restrict__ clo,
+                                                  float* __restrict__ cz) {
+  // one wave per workgroup: W x 130 floats of LDS (8.3 KB at W = 16), small
+  // enough to run beside the softmax kernel's workgroups
+  constexpr int E = D * D + D, NCH = E / 64, RS = 65;  // chunks per (b, h); LDS row stride (floats)
+  static_assert(E % 64 == 0 && (D * D) % 64 == 0, "a chunk is all S or all z");
+  __shared__ float lds_[2][W * RS];
+  const int lane = threadIdx.x;
+  const long long gw = blockIdx.x;
+  const long long bh = gw / NCH;
+  const int e0 = (int)(gw % NCH) * 64, el = e0 + lane;
+  float* A = lds_[0];   // frame states, then P in place
+  float* Qt = lds_[1];  // Q
+  const float* pp = part + bh * slots * (long long)E + el;
+  const int T = d.T, i0 = interior_begin(d.g), i1 = interior_end(d.g);
+
+  // frame states, lane = element (all frames' loads of one split in flight together)
+  float text = 0.f;
+  for (int p = 0; p < tsplit; ++p) text += pp[(long long)(T * split + p) * E];
+  float sg[W];
 #pragma unroll
-    for (int f = 0; f < TMAX; ++f) {
-      fw[f] = 0.f;
-      if (f < d.T) {
-        int flo, fhi, blo, bhi;
-        linear_ranges(d.g, f, &flo, &fhi, &blo, &bhi);
-        if (fhi > flo) {
-          while (gp < fhi) { P += frame_state(gp); ++gp; }
-          fw[f] = P;
-        }
-      }
-    }
+  for (int g = 0; g < W; ++g) sg[g] = 0.f;
+  for (int p = 0; p < split; ++p) {
+#pragma unroll
+    for (int g = 0; g < W; ++g)
+      if (g >= i0 && g < i1) sg[g] += pp[(long long)(g * split + p) * E];
   }
-  {
-    float Q = 0.f;
-    int gp = i1;
 #pragma unroll
-    for (int f = TMAX - 1; f >= 0; --f) {
-      if (f < d.T) {
-        int flo, fhi, blo, bhi;
-        linear_ranges(d.g, f, &flo, &fhi, &blo, &bhi);
-        float val = text + fw[f];
-        if (bhi > blo) {
-          while (gp > blo) { --gp; Q += frame_state(gp); }
-          val += Q;
-        }
-        const long long fo = bh * d.T + f;
-        if (el < D * D) {
-          const bf16_t hi = f32_to_bf16(val);
-          const float rem = val - bf16_to_f32(hi);
-          chi[fo * D * D + el] = hi;
-          clo[fo * D * D + el] = f32_to_bf16(rem);
-        } else {
-          cz[fo * D + (el - D * D)] = val;
-        }
-      }
+  for (int g = 0; g < W; ++g) A[g * RS + lane] = sg[g];
+  asm volatile("" ::: "memory");  // a wave's LDS operations run in order; keep the compiler from reordering
+
+  // scans, lane = frame g of element column j
+  constexpr int NG = 64 / W;  // element columns per instruction
+  const int g = lane % W, r = lane / W;
+#pragma unroll 4
+  for (int jb = 0; jb < W; ++jb) {
+    const int j = jb * NG + r;
+    const float a = A[g * RS + j];
+    const float ar = g < T ? A[(T - 1 - g) * RS + j] : 0.f;
+    const float P = group_prefix<W>(a), R = group_prefix<W>(ar);
+    asm volatile("" ::: "memory");
+    A[g * RS + j] = P;
+    if (g < T) Qt[(T - 1 - g) * RS + j] = R;
+  }
+  asm volatile("" ::: "memory");
+
+  // combined states, lane = element
+  for (int f = 0; f < T; ++f) {
+    int flo, fhi, blo, bhi;
+    linear_ranges(d.g, f, &flo, &fhi, &blo, &bhi);
+    float val = text;
+    if (fhi > flo) val += A[(fhi - 1) * RS + lane];
+    if (bhi > blo) val += Qt[blo * RS + lane];
+    const long long fo = bh * T + f;
+    if (e0 < D * D) {
+      const bf16_t hi = f32_to_bf16(val);
+      chi[fo * D * D + el] = hi;
+      clo[fo * D * D + el] = f32_to_bf16(val - bf16_to_f32(hi));
+    } else {
+      cz[fo * D + (el - D * D)] = val;
     }
   }
 }
 
-// The same scan for layouts with more frames than the register form covers:
+// The scan for layouts with more frames than one wave covers (T > 64), one
+// thread per (b, h, element):
 // pass 1 writes the forward part of every frame to the workspace (pre),
 // pass 2 reads it back.
 template <int D>
@@ -425,23 +454,24 @@ hipError_t launch_states_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, int TMAX>
-static void launch_scan_t(const Dims& d, const Bf16Args& a, unsigned grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_scan_bf16<D, TMAX>), dim3(grid), dim3(256), 0, s, d, a.part, a.state_split, a.text_split,
-                     a.state_slots, a.comb_hi, a.comb_lo, a.comb_z);
+template <int D, int W>
+static void launch_scan_t(const Dims& d, const Bf16Args& a, hipStream_t s) {
+  const long long waves = (long long)d.B * d.H * ((D * D + D) / 64);
+  hipLaunchKernelGGL((k_scan_bf16<D, W>), dim3((unsigned)waves), dim3(64), 0, s, d, a.part, a.state_split,
+                     a.text_split, a.state_slots, a.comb_hi, a.comb_lo, a.comb_z);
 }
 
 hipError_t launch_scan_bf16(const Dims& d, const Bf16Args& a, hipStream_t s) {
   const long long E = (long long)d.D * d.D + d.D;
   const long long n = (long long)d.B * d.H * E;
   const unsigned grid = (unsigned)((n + 255) / 256);
-  // the frame count bounds the unrolled per-frame registers of pass 1
+  // the scan width (lanes per frame group) covers the frame count
   if (d.T <= 16) {
-    if (d.D == 128) launch_scan_t<128, 16>(d, a, grid, s); else launch_scan_t<64, 16>(d, a, grid, s);
+    if (d.D == 128) launch_scan_t<128, 16>(d, a, s); else launch_scan_t<64, 16>(d, a, s);
   } else if (d.T <= 32) {
-    if (d.D == 128) launch_scan_t<128, 32>(d, a, grid, s); else launch_scan_t<64, 32>(d, a, grid, s);
+    if (d.D == 128) launch_scan_t<128, 32>(d, a, s); else launch_scan_t<64, 32>(d, a, s);
   } else if (d.T <= 64) {
-    if (d.D == 128) launch_scan_t<128, 64>(d, a, grid, s); else launch_scan_t<64, 64>(d, a, grid, s);
+    if (d.D == 128) launch_scan_t<128, 64>(d, a, s); else launch_scan_t<64, 64>(d, a, s);
   } else if (d.D == 128) {
     hipLaunchKernelGGL(k_scan_pre_bf16<128>, dim3(grid), dim3(256), 0, s, d, a.part, a.state_split, a.text_split,
                        a.state_slots, a.pre, a.comb_hi, a.comb_lo, a.comb_z);
