@@ -307,29 +307,71 @@ def cpu_baseline(w, inp):
             "wall_s": round(t_states + sum(t[3] for t in timed), 2)}
 
 
-def library_gemms(w, torch, reps=10):
-    """torch.matmul (hipBLASLt) on the gate GEMM's shape (x [M, hid] @ [hid, 2 hid], bf16) and the output
-    GEMM's ([M, 2 hid] @ [2 hid, hid], fp16), random normal operands, no epilogue: the library reference for
-    the two epilogue GEMMs, timed with events on torch's stream."""
+def library_gemms(w, torch, step, api, rounds=6, reps=4):
+    """torch (hipBLASLt) on the shapes of the gate GEMM (x [M, hid] @ [hid, 2 hid], bf16) and the output
+    GEMM ([M, 2 hid] @ [2 hid, hid], fp16), random normal operands: the plain products (gate, out), and
+    each with its epilogue as a library-based layer would run it (gate_epi: sigmoid of the bf16 product
+    times a bf16 copy of the branch outputs, to fp16 -- the RMS factors left out; out_epi: addmm with the
+    residual as C in fp16, one hipBLASLt call).  Each round enqueues one timed forward of the layer (its
+    gate / out stage times, ours_*) and, right behind it on the same stream, one launch of each library
+    form, so that both run at the clocks the softmax kernel leaves; alone_* are the plain products, reps
+    launches back to back after an idle synchronisation.  Medians over the rounds."""
     M, hid = w.batch * w.n_video, w.heads * w.head_dim
     g = torch.Generator(device="cuda")
     g.manual_seed(7)
-    res = {}
+    ops = {}
     for name, (k, n, dt) in {"gate": (hid, 2 * hid, torch.bfloat16), "out": (2 * hid, hid, torch.float16)}.items():
         a = torch.randn(M, k, device="cuda", generator=g).to(dt)
         b = (torch.randn(k, n, device="cuda", generator=g) * 0.02).to(dt).contiguous()
-        for _ in range(3):
-            torch.matmul(a, b)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ops[name] = (a, b)
+    o = torch.randn(M, 2 * hid, device="cuda", generator=g).to(torch.bfloat16)  # branch outputs [O_s | O_l]
+    res16 = torch.randn(M, hid, device="cuda", generator=g).to(torch.float16)  # residual rows
+    forms = {
+        "gate": lambda: torch.matmul(*ops["gate"]),
+        "out": lambda: torch.matmul(*ops["out"]),
+        "gate_epi": lambda: (torch.sigmoid(torch.matmul(*ops["gate"])) * o).to(torch.float16),
+        "out_epi": lambda: torch.addmm(res16, *ops["out"]),
+    }
+    for f in forms.values():
+        f()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    lib = {k: [] for k in forms}
+    alone, ours = {"gate": [], "out": []}, {"gate": [], "out": []}
+    for _ in range(rounds):
         torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            torch.matmul(a, b)
-        e1.record()
+        t = api.StageTimer(last="out")
+        step(t)
+        e = [ev() for _ in range(len(forms) + 1)]
+        e[0].record()
+        for i, f in enumerate(forms.values()):
+            f()
+            e[i + 1].record()
         torch.cuda.synchronize()
-        res[name] = round(e0.elapsed_time(e1) / reps, 4)
-        del a, b
-    res["note"] = "torch.matmul (hipBLASLt), same shapes and dtypes, no epilogue, %d launches" % reps
+        el = t.elapsed_ms()
+        t.close()
+        for name in ("gate", "out"):
+            ours[name].append(el[name])
+        for i, name in enumerate(forms):
+            lib[name].append(e[i].elapsed_time(e[i + 1]))
+        for name in ("gate", "out"):
+            torch.cuda.synchronize()
+            e0, e1 = ev(), ev()
+            e0.record()
+            for _ in range(reps):
+                forms[name]()
+            e1.record()
+            torch.cuda.synchronize()
+            alone[name].append(e0.elapsed_time(e1) / reps)
+    med = lambda v: round(float(np.median(v)), 4)  # noqa: E731
+    res = {name: med(v) for name, v in lib.items()}
+    for name in ("gate", "out"):
+        res["ours_" + name] = med(ours[name])
+        res["alone_" + name] = med(alone[name])
+    res["note"] = ("torch (hipBLASLt) on the same shapes and dtypes: gate / out plain products, gate_epi / out_epi "
+                   "with their epilogues as separate library calls, launched right behind a forward of the layer on "
+                   "its stream; alone_* the plain products, %d launches back to back after an idle sync; ours_* "
+                   "are this layer's fused GEMMs with their epilogues in that forward; medians of %d rounds"
+                   % (reps, rounds))
     return res
 
 
@@ -591,8 +633,8 @@ def main():
                      "frac": round(soft_tflops / peak, 4), "traffic": traffic_for(soft_key, w.name),
                      "flop_per_launch": wc["softmax_flop"]},
     }
-    if args.library_gemms and w.act != "f32":
-        out["library_gemm_ms"] = library_gemms(w, torch)
+    if args.library_gemms and w.act != "f32" and not (args.block or args.dit):
+        out["library_gemm_ms"] = library_gemms(w, torch, step, api)
     if not args.no_cpu_baseline and w.act != "f32":
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inp)

@@ -84,12 +84,17 @@ __device__ __forceinline__ float gelu_tanh_f(float u) {
 // and reads of 16 lanes along one row).  The operand stages are free here:
 // the main loop ended on a barrier after every wave's last LDS read.
 constexpr int EPI_ROW = 132;                       // floats per LDS row
-constexpr int EPI_WAVE_BYTES = 32 * EPI_ROW * 4;  // LDS bytes per wave
+constexpr int EPI_WAVE_BYTES = 32 * EPI_ROW * 4;  // LDS bytes per wave (32-row groups)
 
-template <int WTM, int WFN, int EPI>
+// RG: rows per pass through the LDS region (32, or 16 in half the LDS: each
+// 32-token block then takes two passes, lanes 0-15 / 16-31 of a half-wave
+// writing their tokens in turn).
+template <int WTM, int WFN, int EPI, int RG = 32>
 __device__ __forceinline__ void epilogue_rows(const GemmArgs& g, floatx16 (&acc)[WFN][WTM], long long mw, int nwave,
                                               int lane, float* ldsw) {
   static_assert(WFN == 4, "row epilogue: 128 features per wave");
+  static_assert(RG == 16 || RG == 32, "rows per pass");
+  constexpr int NP = 32 / RG, KR = RG / 2;  // passes per 32-token block, row pairs per pass
   const int l32 = lane & 31, half = lane >> 5;
   const int lc = l32, lr = half;  // row layout: features 4 lc .. 4 lc + 3 of row 2 k + lr
   const bool lin = EPI == EPI_GATE && nwave >= g.hid;  // a wave's features are all in one half (hid % BN == 0)
@@ -133,25 +138,29 @@ __device__ __forceinline__ void epilogue_rows(const GemmArgs& g, floatx16 (&acc)
     };
     load_in(0);
 #pragma unroll
-    for (int i = 0; i < WTM; ++i) {
-      // MFMA layout -> LDS: token l32, features 32 f + 8 jg + 4 half
+    for (int ip = 0; ip < WTM * NP; ++ip) {
+      const int i = ip / NP, pp = ip % NP;  // token block, pass
+      // MFMA layout -> LDS: token l32 (those of this pass), features 32 f + 8 jg + 4 half
+      if (NP == 1 || l32 / RG == pp) {
 #pragma unroll
-      for (int f = 0; f < WFN; ++f)
+        for (int f = 0; f < WFN; ++f)
 #pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          float4 v = make_float4(acc[f][i][4 * jg], acc[f][i][4 * jg + 1], acc[f][i][4 * jg + 2], acc[f][i][4 * jg + 3]);
-          if constexpr (EPI == EPI_GATE) v = make_float4(sigmoid_rcp(v.x), sigmoid_rcp(v.y), sigmoid_rcp(v.z), sigmoid_rcp(v.w));
-          *(float4*)&ldsw[l32 * EPI_ROW + 32 * f + 8 * jg + 4 * half] = v;
-        }
-      if (i + 1 < WTM) load_in(i + 1);
+          for (int jg = 0; jg < 4; ++jg) {
+            float4 v = make_float4(acc[f][i][4 * jg], acc[f][i][4 * jg + 1], acc[f][i][4 * jg + 2], acc[f][i][4 * jg + 3]);
+            if constexpr (EPI == EPI_GATE) v = make_float4(sigmoid_rcp(v.x), sigmoid_rcp(v.y), sigmoid_rcp(v.z), sigmoid_rcp(v.w));
+            *(float4*)&ldsw[(l32 % RG) * EPI_ROW + 32 * f + 8 * jg + 4 * half] = v;
+          }
+      }
+      if (pp == 0 && i + 1 < WTM) load_in(i + 1);
       // LDS -> row layout.  A wave's LDS operations execute in issue order, so
-      // these reads see the writes above and the next group's writes follow
+      // these reads see the writes above and the next pass's writes follow
       // them; the empty asm keeps the compiler from reordering across lanes.
       asm volatile("" ::: "memory");
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
+      for (int kr = 0; kr < KR; ++kr) {
+        const int k = pp * KR + kr;  // row pair inside the block: rows 2 k + lr
         const int r = 2 * k + lr;
-        const float4 a = *(const float4*)&ldsw[r * EPI_ROW + 4 * lc];
+        const float4 a = *(const float4*)&ldsw[(2 * kr + lr) * EPI_ROW + 4 * lc];
         float rk = 0.f;
         if (lin) rk = __shfl(rv, 32 * i + r);
         const long long m = mw + 32 * i + r;
