@@ -79,10 +79,14 @@ EDGE = [
     Workload("two-frames", 1, 2, 64, 3, 1, 64, seed=36),
     Workload("ragged-f32", 1, 5, 50, 7, 2, 64, act="f32", soft="f32", seed=37),
     Workload("f32-d128", 1, 4, 33, 9, 1, 128, act="f32", soft="f32", chunk_frames=2, seed=38),
-    # frame counts past the scan's 16- and 32-frame register forms, and past
-    # 64 (the scan's workspace-prefix form)
+    # frame counts past the scan's 16- and 32-lane forms, and past 64 (the
+    # per-thread form)
     Workload("frames-40-chunk3", 1, 40, 32, 16, 2, 64, chunk_frames=3, seed=39),
     Workload("frames-70", 1, 70, 16, 8, 2, 128, seed=40),
+    # hidden 256 (the 256 x 256 GEMM tiles and their row epilogue) with one
+    # token, and with one token past a whole tile
+    Workload("one-token-d128", 1, 1, 1, 3, 2, 128, seed=42),
+    Workload("tile-plus-one", 1, 1, 257, 5, 2, 128, seed=43),
 ]
 
 
