@@ -217,3 +217,87 @@ def test_backward_stays_inside_its_buffers(w):
         got = g.t.float().cpu().numpy()
         assert np.all(np.isfinite(got)), name
         assert np.array_equal(got, base[name]), name
+
+
+BLOCKS = [
+    (Workload("guard-block-ragged-b2", 2, 3, 100, 16, 2, 64, seed=121), None),
+    (Workload("guard-block-d128-fp8", 1, 4, 70, 24, 2, 128, seed=122), "fp8"),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("w,soft", BLOCKS, ids=[w.name for w, _ in BLOCKS])
+def test_projection_block_and_dit_block_stay_inside_their_buffers(w, soft):
+    """hyb_qkv_project, hyb_block_forward and hyb_dit_block_forward (the
+    projection GEMM, its absmax epilogue and the feed-forward GEMMs) with
+    guarded inputs, outputs and workspaces."""
+    import torch
+    from hybrid_softmax_linear_block_amd.inputs import make_ffn_weights, make_projection_weights
+    print("case", w.name, soft, flush=True)
+    inp, pw, fw = make_inputs(w), make_projection_weights(w), make_ffn_weights(w)
+    lay = gu.api_layout(w)
+    bf = torch.bfloat16
+    dev = {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda").to(bf) for k, v in {**inp, **pw, **fw}.items()}
+    B, N, H, D, hid = w.batch, w.n_video, w.heads, w.head_dim, w.hidden
+    args = ("w_gs", "w_gl", "w_os", "w_ol", "rms_w")
+    base_q = [t.float().cpu().numpy() for t in api.qkv_project(lay, dev["x"], dev["w_q"], dev["w_k"], dev["w_v"])]
+    base_y = api.block_forward(lay, dev["x"], dev["w_q"], dev["w_k"], dev["w_v"], dev["text_k"], dev["text_v"],
+                               *[dev[a] for a in args], soft=soft).float().cpu().numpy()
+    base_z = api.dit_block_forward(lay, dev["x"], dev["w_q"], dev["w_k"], dev["w_v"], dev["text_k"], dev["text_v"],
+                                   *[dev[a] for a in args], dev["w_n"], dev["w_1"], dev["w_2"],
+                                   soft=soft).float().cpu().numpy()
+    torch.cuda.synchronize()
+
+    gin = _guard_inputs(w, {**inp, **pw, **fw})
+    t = {k: v.t for k, v in gin.items()}
+    sentinel = 1234.0
+    gq = [Guarded((B, N, H, D), bf, sentinel) for _ in range(3)]
+    gam = Guarded((3 * B * H,), torch.int32, 0x5A5A5A5A)
+    ws = Guarded((api.qkv_workspace_size(lay),), torch.uint8, 0xA5)
+    api.qkv_project(lay, t["x"], t["w_q"], t["w_k"], t["w_v"], q=gq[0].t, k=gq[1].t, v=gq[2].t, absmax=gam.t,
+                    workspace=ws.t)
+    gy = Guarded((B, N, hid), bf, sentinel)
+    wsb = Guarded((api.block_workspace_size(lay, soft),), torch.uint8, 0xA5)
+    api.block_forward(lay, t["x"], t["w_q"], t["w_k"], t["w_v"], t["text_k"], t["text_v"], *[t[a] for a in args],
+                      soft=soft, y=gy.t, workspace=wsb.t)
+    gz = Guarded((B, N, hid), bf, sentinel)
+    F = fw["w_1"].shape[1]
+    wsd = Guarded((api.dit_block_workspace_size(lay, F, soft),), torch.uint8, 0xA5)
+    api.dit_block_forward(lay, t["x"], t["w_q"], t["w_k"], t["w_v"], t["text_k"], t["text_v"],
+                          *[t[a] for a in args], t["w_n"], t["w_1"], t["w_2"], soft=soft, z=gz.t, workspace=wsd.t)
+    torch.cuda.synchronize()
+
+    for name, g in gin.items():
+        assert g.unchanged(), "input %s or its margins were written" % name
+    for name, g in [("q", gq[0]), ("k", gq[1]), ("v", gq[2]), ("absmax", gam), ("qkv workspace", ws), ("y", gy),
+                    ("block workspace", wsb), ("z", gz), ("dit workspace", wsd)]:
+        assert g.margins_intact(), "write outside %s" % name
+    for i in range(3):
+        assert np.array_equal(gq[i].t.float().cpu().numpy(), base_q[i]), "qkv"[i]
+    for name, g, ref in (("y", gy, base_y), ("z", gz, base_z)):
+        got = g.t.float().cpu().numpy()
+        assert np.all(np.isfinite(got)), name
+        assert np.array_equal(got, ref), name
+
+
+@pytest.mark.gpu
+def test_noalloc_entry_point_stays_inside_its_buffers():
+    """hyb_attn_forward_noalloc (the library's own scratch) with guarded
+    inputs and outputs."""
+    import torch
+    w = WORKLOADS[2].with_(name="guard-noalloc", frames=4, tokens_per_frame=200, text_tokens=30, seed=131)
+    print("case", w.name, flush=True)
+    inp = make_inputs(w)
+    base = gu.run_gpu(w, inp, debug=False)
+    gin = _guard_inputs(w, inp)
+    y = Guarded((w.batch, w.n_video, w.hidden), torch.bfloat16, 1234.0)
+    api.forward_noalloc(gu.api_layout(w), gin["x"].t, gin["q"].t, gin["k"].t, gin["v"].t, gin["text_k"].t,
+                        gin["text_v"].t, gin["w_gs"].t, gin["w_gl"].t, gin["w_os"].t, gin["w_ol"].t, gin["rms_w"].t,
+                        y.t)
+    torch.cuda.synchronize()
+    for name, g in gin.items():
+        assert g.unchanged(), "input %s or its margins were written" % name
+    assert y.margins_intact(), "write outside y"
+    got = y.t.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    assert np.array_equal(got, base["y"])
