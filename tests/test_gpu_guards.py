@@ -301,3 +301,65 @@ def test_noalloc_entry_point_stays_inside_its_buffers():
     got = y.t.float().cpu().numpy().astype(np.float64)
     assert np.all(np.isfinite(got))
     assert np.array_equal(got, base["y"])
+
+
+@pytest.mark.gpu
+def test_training_forward_saved_backward_and_block_backward_stay_inside_their_buffers():
+    """hyb_attn_forward_train writing its saved buffer, hyb_attn_backward
+    reading it, and hyb_block_backward, with guarded inputs, outputs, saved
+    buffer and workspaces."""
+    import torch
+    from hybrid_softmax_linear_block_amd.inputs import make_projection_weights
+    w = Workload("guard-train-ragged-b2", 2, 5, 100, 20, 2, 64, qkv_scale=0.5, seed=141)
+    print("case", w.name, flush=True)
+    inp, pw, dy = make_inputs(w), make_projection_weights(w), make_grad_output(w)
+    lay = gu.api_layout(w)
+    bf = torch.bfloat16
+    dev = {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda").to(bf) for k, v in {**inp, **pw}.items()}
+    dyd = torch.from_numpy(np.ascontiguousarray(dy)).to("cuda").to(bf)
+    layer = lambda t: (t["x"], t["q"], t["k"], t["v"], t["text_k"], t["text_v"], t["w_gs"], t["w_gl"], t["w_os"],
+                       t["w_ol"], t["rms_w"])
+    block = lambda t: (t["x"], t["w_q"], t["w_k"], t["w_v"], t["text_k"], t["text_v"], t["w_gs"], t["w_gl"],
+                       t["w_os"], t["w_ol"], t["rms_w"])
+    y0, saved0 = api.forward_train(lay, *layer(dev))
+    g0 = api.backward(lay, *layer(dev), dyd, saved=saved0)
+    b0 = api.block_backward(lay, *block(dev), dyd)
+    torch.cuda.synchronize()
+    g0 = {k: v.float().cpu().numpy() for k, v in g0.items()}
+    b0 = {k: v.float().cpu().numpy() for k, v in b0.items()}
+
+    gin = _guard_inputs(w, {**inp, **pw})
+    gdy = Guarded(dy.shape, bf, float("nan"), host=dy)
+    t = {k: v.t for k, v in gin.items()}
+    B, N, L, H, D, hid = w.batch, w.n_video, w.text_tokens, w.heads, w.head_dim, w.hidden
+    sentinel = -77.0
+    gy = Guarded((B, N, hid), bf, sentinel)
+    gsaved = Guarded((api.saved_size(lay),), torch.uint8, 0x3C)
+    wsf = Guarded((api.workspace_size(lay, "bf16"),), torch.uint8, 0xA5)
+    api.forward_train(lay, *layer(t), y=gy.t, saved=gsaved.t, workspace=wsf.t)
+    shapes = {"dx": ((B, N, hid), bf), "dq": ((B, N, H, D), bf), "dk": ((B, N, H, D), bf),
+              "dv": ((B, N, H, D), bf), "dtext_k": ((B, L, H, D), bf), "dtext_v": ((B, L, H, D), bf),
+              "dw_gate_soft": ((hid, hid), torch.float32), "dw_gate_lin": ((hid, hid), torch.float32),
+              "dw_out_soft": ((hid, hid), torch.float32), "dw_out_lin": ((hid, hid), torch.float32),
+              "drms_weight": ((hid,), torch.float32)}
+    gout = {k: Guarded(s, dt, sentinel) for k, (s, dt) in shapes.items()}
+    wsb = Guarded((api.backward_workspace_size(lay),), torch.uint8, 0x5A)
+    api.backward(lay, *layer(t), gdy.t, saved=gsaved.t, grads={k: v.t for k, v in gout.items()}, workspace=wsb.t)
+    wsk = Guarded((api.block_backward_workspace_size(lay),), torch.uint8, 0x5A)
+    b1 = api.block_backward(lay, *block(t), gdy.t, workspace=wsk.t)
+    torch.cuda.synchronize()
+
+    for name, g in list(gin.items()) + [("dy", gdy)]:
+        assert g.unchanged(), "input %s or its margins were written" % name
+    for name, g in [("y", gy), ("saved", gsaved), ("forward workspace", wsf), ("backward workspace", wsb),
+                    ("block backward workspace", wsk)] + list(gout.items()):
+        assert g.margins_intact(), "write outside %s" % name
+    assert np.array_equal(gy.t.float().cpu().numpy(), y0.float().cpu().numpy()), "y"
+    for name, g in gout.items():
+        got = g.t.float().cpu().numpy()
+        assert np.all(np.isfinite(got)), name
+        assert np.array_equal(got, g0[name]), name
+    for name, v in b1.items():
+        got = v.float().cpu().numpy()
+        assert np.all(np.isfinite(got)), name
+        assert np.array_equal(got, b0[name]), name
