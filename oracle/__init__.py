@@ -58,8 +58,11 @@ Parity status per function (what pins it, in ``tests/test_oracle_*.py``):
                                       round trips, block extent and axis, the
                                       format's error bound, exact products of
                                       representable operands, W_o = 0.
-  Anchor frames as queries (they attend to every frame): parity unpinned --
-  the article says only that anchors interact with the other frames.
+  Anchor frames as queries (they attend to every frame, their linear rows
+  hold text only) are a reading the article cannot confirm: it says only
+  that the anchors interact with the other frames.  The oracle's form of
+  that reading is pinned like every other frame's (hand-written frame sets,
+  the per-frame closed form, dense-mask brute force, text-only linear rows).
 """
 from .layout import Layout, frame_sets, tables  # noqa: F401
 from .hybrid import (phi, softmax_branch, linear_states, linear_branch,  # noqa: F401
