@@ -1,6 +1,6 @@
 // fp8 (OCP e4m3) softmax branch.
 //
-// The VDN-H3 article's performance section measures an "FP8 version" of the
+// The VDN-H3 article's performance section measures an fp8 version of the
 // model without saying which operations run in fp8; here the softmax
 // branch's Q, K, V (video and text) are quantised per (tensor, batch, head)
 // with scale = absmax / 448 and both Q K^T and P V run on the gfx950

@@ -1,6 +1,6 @@
 // MX (microscaling) e4m3 quantisers for the fp8 GEMMs.
 //
-// The VDN-H3 article's performance section reports an "FP8 version" of the
+// The VDN-H3 article's performance section reports an fp8 version of the
 // model without saying which products run in fp8.  With the fp8 GEMM option
 // the Q/K/V projection, the gate GEMM, the output GEMM and the DiT block's
 // feed-forward GEMMs take e4m3 operands with one power-of-two (E8M0) scale

@@ -72,7 +72,7 @@ typedef enum {
  * products accumulated in fp32.  Activations (x, A') are blocked along the
  * feature axis of each token, weights along the input axis of each output
  * column; A' is quantised in the gate GEMM's epilogue.  The article's
- * performance section names an "FP8 version" without saying which products
+ * performance section names an fp8 version without saying which products
  * it quantises; this is the library's reading.  Needs hid % 256 == 0. */
 typedef enum { HYB_F32 = 0, HYB_BF16 = 1, HYB_FP8_E4M3 = 2, HYB_FP8_MX = 3 } hyb_dtype;
 
@@ -204,7 +204,7 @@ hyb_status hyb_attn_forward_noalloc(const hyb_layout* layout, hyb_dtype act, hyb
  * Q/K/V input projection -- the step before the layer.  Article section
  * "分阶段适配预训练模型" (staged adaptation): both attention branches read one
  * set of Q/K/V projections of the block input (stages A2 and B).  The
- * performance section's "FP8 version" quantises the softmax branch's Q/K/V;
+ * performance section's fp8 version quantises the softmax branch's Q/K/V;
  * the per-(tensor, batch, head) absmax that sets those scales is taken here,
  * in the projection GEMM's epilogue, instead of by a separate pass.
  *

@@ -1,7 +1,7 @@
 """fp8 (OCP e4m3) emulation of the softmax branch (oracle, test
 infrastructure only).
 
-The VDN-H3 article's performance section reports an "FP8 version" without
+The VDN-H3 article's performance section reports an fp8 version without
 saying which operations are fp8.  The library's reading, which this module
 writes out:
 

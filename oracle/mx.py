@@ -2,7 +2,7 @@
 infrastructure only).
 
 Source: VDN-H3 article (tahou.com, article 216474224916730885), section
-"性能实测表现" (measured performance): the "FP8 version" of the model is the
+"性能实测表现" (measured performance): the fp8 version of the model is the
 one timed against the dense baseline; the article does not say which
 products it quantises.  The library's reading of the whole fp8 version: the
 softmax branch as in oracle/fp8.py, and the Q/K/V projection, the gate GEMM

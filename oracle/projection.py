@@ -5,7 +5,7 @@ Source: VDN-H3 article (tahou.com, article 216474224916730885), section
 "分阶段适配预训练模型" (staged adaptation): stages A2 and B keep one set of
 Q/K/V projections shared by both attention branches (frozen in A1/A2, LoRA
 in B), so the layer's q, k and v come from a single projection of the block
-input.  The performance section's "FP8 version" (section "性能实测表现")
+input.  The performance section's fp8 version (section "性能实测表现")
 quantises the softmax branch's inputs; the library's reading of that
 quantisation (per (tensor, batch, head) absmax / 448) is in oracle/fp8.py.
 
